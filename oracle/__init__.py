@@ -1,0 +1,17 @@
+"""CPU oracle for the HCA layer forward: test infrastructure only.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The product path (the HIP library and its Python
+binding) never does.
+"""
+from .hca_oracle import (  # noqa: F401
+    BLOCK,
+    attend_decode,
+    attend_prefill,
+    blocks_per_sequence,
+    cache_entries,
+    compress,
+    cu_blocks_from_cu_seqlens,
+    pooling_weights,
+    visible_sets,
+)

@@ -1,0 +1,23 @@
+"""HCA (Heavily Compressed Attention) layer forward for AMD MI355X.
+
+The computation lives in libhca.so (hand-written HIP kernels for gfx950 behind
+the C ABI of include/hca.h); this package is its Python binding.  Build the
+library with `python -m compressed_kv_sparse_amd.build`.
+"""
+from .hca import (  # noqa: F401
+    EXPORTS,
+    HCA_BF16,
+    HCA_F32,
+    HcaError,
+    HcaLibraryMissing,
+    HcaParams,
+    hca_attend_decode,
+    hca_attend_prefill,
+    hca_compress,
+    hca_decode_workspace_bytes,
+    hca_status_string,
+    hca_version,
+    library,
+    make_params,
+    new_decode_workspace,
+)

@@ -1,0 +1,540 @@
+// bf16 HCA attention for 512-dim heads and 64 query heads per KV head, on
+// CDNA4 matrix cores (v_mfma_f32_32x32x16_bf16, fp32 accumulation).
+//
+// What is computed (release blog "ERNIE 5.5 Flash Base", section 2.1, HCA
+// paragraph; Zhidx article, section "1. Latent-Gated Sparse Attention"): each
+// query attends, under one softmax scaled by 1/sqrt(d), to the complete
+// compressed entries of its sequence (block j visible once 128(j+1) <= t+1)
+// followed by the raw window max(0, t-W+1) .. t.  The model card gives the
+// 512-dim heads; the Zhidx article the 64 query heads.
+//
+// Design (gfx950):
+//  * Head packing.  All 64 query heads of one KV head read the same keys, so
+//    a wavefront owns 32 query rows = 32 heads of ONE position: every row of
+//    the wave has the same key set and the key tile is shared by 32 rows in
+//    registers.  A prefill workgroup = 4 wavefronts = 64 heads x 2 adjacent
+//    positions (their key sets differ in at most two keys, masked per row).
+//  * Transposed products keep every per-row quantity inside one lane:
+//      S^T[key, row] = K[key, :] . Q^T[:, row]      (A = K from LDS, B = Q in VGPRs)
+//      O^T[col, row] += V^T[col, key] . P^T[key, row] (A = V^T via transposed LDS
+//                                                      reads, B = P from VGPRs)
+//    With the 32x32 MFMA output layout, lane l holds row l%32 of S^T and of
+//    O^T, so the softmax row max/sum never leave the lane pair (l, l^32) and
+//    P goes from the S accumulators straight into the B operand without LDS.
+//  * Keys stream in tiles of 32 through LDS with direct global->LDS 16-byte
+//    loads (one 1 KiB row per wave instruction, fully coalesced), double
+//    buffered so the next tile is in flight during the current one's math.
+//    K rows are padded to 1040 bytes and V rows to 1088 bytes so the 16-byte
+//    K fragment reads and the transposed 8-byte V reads hit distinct banks.
+//  * Softmax in base 2 (log2 e folded into the scale) without accumulator
+//    rescaling: a row fixes its reference max m at the first tile where it
+//    sees a key and uses exp2(s - m) from then on.  Weights stay <= 2^32 as
+//    long as no later score exceeds m by more than 32 (in log2 units); if one
+//    does, the whole workgroup restarts in an exact two-pass schedule (pass 1:
+//    row max over all keys; pass 2: weights exp2(s - max) <= 1).  The 256 fp32
+//    accumulators per lane therefore live in AGPRs and are only ever touched
+//    by the matrix cores; softmax(x) = exp(x - c)/sum exp(x - c) holds for any
+//    c, so the result is the same up to rounding.
+//  * Decode: one workgroup of 2 wavefronts (64 heads of one query) per
+//    (sequence, KV head, key split); fp32 partials (m, l, unnormalised O) go
+//    to the workspace and the last split to finish (atomic ticket) merges
+//    them in split order, so the result is deterministic.
+#include <algorithm>
+
+#include "hca_internal.h"
+
+#define HCA_GLOBAL __attribute__((address_space(1)))
+
+namespace hca {
+namespace {
+
+constexpr int D = 512;           // head dim of this path
+constexpr int G = 64;            // query heads per KV head
+constexpr int NT = 32;           // keys per tile
+constexpr int KSTR = 1040;       // LDS bytes per K row (1024 + 16 pad)
+constexpr int VSTR = 1088;       // LDS bytes per V row (1024 + 64 pad)
+constexpr int DSTEPS = D / 16;   // k-steps of the score product
+constexpr int CTILES = D / 32;   // 32-column tiles of the output
+constexpr float kHeadroom = 32.f;  // max growth over the reference, log2 units
+
+// Workgroups whose key list is at most this long carry softmax weights as
+// two bf16 terms.
+constexpr int kTwoTermKeys = 64;
+
+// Softmax schedule of one pass over the key tiles.
+enum Mode { kLazy = 0, kMaxOnly = 1, kFixed = 2 };
+
+// Where the keys of one workgroup come from.  Slot kappa < nc is compressed
+// entry kappa of the sequence; slot kappa >= nc is raw position
+// lo + (kappa - nc), stored at row `pos` of raw_k/raw_v, or at row pos % ring
+// when ring > 0 (decode ring buffer).
+struct KeySource {
+  const char* comp_k;
+  const char* comp_v;
+  const char* raw_k;
+  const char* raw_v;
+  size_t rstride;  // bytes between consecutive rows (Hkv * D * 2)
+  int nc, nkeys, lo, ring;
+};
+
+// Which slots a row (one query position t) may see.
+struct RowMask {
+  int nc, nvis_c, nkeys, lo, smin, smax;
+  __device__ __forceinline__ bool valid(int kappa) const {
+    if (kappa >= nkeys) return false;
+    if (kappa < nc) return kappa < nvis_c;
+    const int s = lo + kappa - nc;
+    return s >= smin && s <= smax;
+  }
+};
+
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Issue the direct global->LDS loads of key tile `tile`: NW wavefronts share
+// the 32 K rows and 32 V rows; one instruction moves one 1 KiB row.
+template <int NW>
+__device__ __forceinline__ void issue_tile(const KeySource& ks, int tile, char HCA_LDS* kbuf,
+                                           char HCA_LDS* vbuf, int wave, int lane) {
+  constexpr int RPW = NT / NW;
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int kk = wave * RPW + r;
+    // slots past the end re-read the last key (finite data; masked later)
+    const int kappa = min(tile * NT + kk, ks.nkeys - 1);
+    const char* ksrc;
+    const char* vsrc;
+    if (kappa < ks.nc) {
+      ksrc = ks.comp_k + (size_t)kappa * ks.rstride;
+      vsrc = ks.comp_v + (size_t)kappa * ks.rstride;
+    } else {
+      int pos = ks.lo + (kappa - ks.nc);
+      if (ks.ring) pos %= ks.ring;
+      ksrc = ks.raw_k + (size_t)pos * ks.rstride;
+      vsrc = ks.raw_v + (size_t)pos * ks.rstride;
+    }
+    __builtin_amdgcn_global_load_lds((const void HCA_GLOBAL*)(ksrc + lane * 16),
+                                     (void HCA_LDS*)(kbuf + kk * KSTR), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void HCA_GLOBAL*)(vsrc + lane * 16),
+                                     (void HCA_LDS*)(vbuf + kk * VSTR), 16, 0, 0);
+  }
+}
+
+// Softmax state of the 32 rows a wavefront owns (one row per lane pair
+// l, l^32; both lanes of a pair hold the same m and a partial l).
+struct Acc {
+  f32x16 o[CTILES];  // O^T: lane l holds row l%32, cols 32ct + 8(i/4) + 4(l/32) + i%4
+  float m, l;
+};
+
+__device__ __forceinline__ bf16x8 lds_k_frag(const char HCA_LDS* p) {
+  return *(const bf16x8 HCA_LDS*)p;
+}
+
+// A fragment of V^T for one (32-column tile, 16-key step): two transposed
+// 8-byte reads, keys {16k2 + 4h + j} and {16k2 + 8 + 4h + j}, j < 4.
+__device__ __forceinline__ bf16x8 lds_v_frag(const char HCA_LDS* base) {
+  const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 HCA_LDS*)base);
+  const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 HCA_LDS*)(base + 8 * VSTR));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// One key tile.  kLazy: scores, reference max fixed at the row's first
+// visible key, weights and P.V; returns true (for the whole wave) if a score
+// exceeded the reference by more than kHeadroom.  kMaxOnly: scores and row
+// max only.  kFixed: like kLazy with m already exact.  `masked` (uniform)
+// applies the per-row visibility test to every slot of the tile.  With
+// `two_term` (uniform) the weights enter the P.V product as the sum of two
+// bf16 numbers, P = hi + lo, lo = bf16(P - hi), which carries P to ~2^-16
+// relative instead of 2^-9: rows that see only a few keys have few, large
+// weights whose rounding does not average out.
+__device__ __forceinline__ bool compute_tile(const char HCA_LDS* kbuf, const char HCA_LDS* vbuf,
+                                             const bf16x8 (&qf)[DSTEPS], Acc& st, float sc2,
+                                             int lane, int koff, int voff, const RowMask& rm,
+                                             int tile, bool masked, int mode, bool two_term) {
+  // S^T = K . Q^T over the 512-wide head dim: 32 k-steps of 16, with the K
+  // fragments read PF steps ahead of their MFMA
+  constexpr int PF = 4;
+  f32x16 s = {};
+  bf16x8 kf[PF];
+#pragma unroll
+  for (int k = 0; k < PF; ++k) kf[k] = lds_k_frag(kbuf + koff + k * 32);
+#pragma unroll
+  for (int k = 0; k < DSTEPS; ++k) {
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[k % PF], qf[k], s, 0, 0, 0);
+    if (k + PF < DSTEPS) kf[k % PF] = lds_k_frag(kbuf + koff + (k + PF) * 32);
+  }
+  // scale into log2 units, mask, row max over the lane pair
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = s[i] * sc2;
+  if (masked) {
+    const int kk0 = tile * NT + 4 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)  // accumulator i holds key slot 8(i/4) + 4(l/32) + i%4
+      if (!rm.valid(kk0 + 8 * (i >> 2) + (i & 3))) x[i] = -INFINITY;
+  }
+  float mx = x[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  if (mode == kMaxOnly) {
+    st.m = fmaxf(st.m, mx);
+    return false;
+  }
+  bool over = false;
+  if (mode == kLazy) {
+    if (st.m == -INFINITY) st.m = mx;  // first visible keys of the row
+    over = mx > st.m + kHeadroom;
+  }
+  const float m_use = st.m == -INFINITY ? 0.f : st.m;  // row with no visible key yet
+  float pv[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(x[i] - m_use);
+  bf16x8 pa, pb, qa = {}, qb = {};
+  float ls = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    pa[j] = (bf16)pv[j];
+    pb[j] = (bf16)pv[8 + j];
+  }
+  if (two_term) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      qa[j] = (bf16)(pv[j] - (float)pa[j]);
+      qb[j] = (bf16)(pv[8 + j] - (float)pb[j]);
+      ls += (float)qa[j] + (float)qb[j];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ls += (float)pa[j] + (float)pb[j];  // sum of the weights used
+  st.l += ls;
+  // O^T += V^T . P^T over 16 column tiles x 2 key steps, V fragments read
+  // PF steps ahead; a second pass adds the low parts of two-term weights
+  const int parts = two_term ? 2 : 1;
+  for (int part = 0; part < parts; ++part) {
+    const bf16x8 ba = part ? qa : pa;
+    const bf16x8 bb = part ? qb : pb;
+    bf16x8 vf[PF];
+#pragma unroll
+    for (int u = 0; u < PF; ++u) vf[u] = lds_v_frag(vbuf + voff + (u & 1) * 16 * VSTR + (u >> 1) * 64);
+#pragma unroll
+    for (int u = 0; u < 2 * CTILES; ++u) {
+      const int ct = u >> 1, k2 = u & 1;
+      st.o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[u % PF], k2 ? bb : ba, st.o[ct], 0, 0, 0);
+      const int un = u + PF;
+      if (un < 2 * CTILES) vf[u % PF] = lds_v_frag(vbuf + voff + (un & 1) * 16 * VSTR + (un >> 1) * 64);
+    }
+  }
+  return mode == kLazy && __any(over);
+}
+
+__device__ __forceinline__ bool tile_needs_mask(int tile, int nc, int nkeys) {
+  // slots that can be invisible to a row: entry nc-1 (row t0 when the second
+  // position completes a block), raw slot nc (oldest window key of the later
+  // row), the last slot (newest key, invisible to the earlier row) and the tail
+  const int a = tile * NT, b = a + NT;
+  return (a <= nc && b > nc - 1) || b >= nkeys;
+}
+
+__device__ __forceinline__ void zero_acc(Acc& st) {
+#pragma unroll
+  for (int ct = 0; ct < CTILES; ++ct) st.o[ct] = f32x16{};
+  st.m = -INFINITY;
+  st.l = 0.f;
+}
+
+// All tiles of [t_begin, t_end): the single-pass schedule, and the exact
+// two-pass schedule if a row's scores grow past the headroom.  Tiles stream
+// through a double-buffered LDS area `kv` (buffer i: K rows at i*KV_BYTES,
+// V rows after them).  The headroom test crosses waves through flag[2]: tile
+// i writes flag[i & 1] before the barrier that ends it and every wave reads
+// that slot right after the barrier; a wave can only write the other slot
+// before the next barrier, so no wave sees a flag set for a later tile.
+template <int NW>
+__device__ __forceinline__ void attend_tiles(const KeySource& ks, int t_begin, int t_end,
+                                             const bf16x8 (&qf)[DSTEPS], Acc& st, float sc2,
+                                             const RowMask& rm, int wave, int lane,
+                                             char HCA_LDS* kv, int* flag) {
+  constexpr int KV_BYTES = NT * KSTR + NT * VSTR;
+  const int koff = (lane & 31) * KSTR + (lane >> 5) * 16;
+  const int voff = NT * KSTR + (4 * (lane >> 5) + ((lane & 15) >> 2)) * VSTR +
+                   (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+  zero_acc(st);
+  // few keys: few, large weights, carried as two bf16 terms (see compute_tile)
+  const bool two_term = rm.nkeys <= kTwoTermKeys;
+  int mode = kLazy;
+  for (;;) {
+    if (threadIdx.x == 0) flag[0] = flag[1] = 0;
+    issue_tile<NW>(ks, t_begin, kv, kv + NT * KSTR, wave, lane);
+    wait_vm_all();
+    __syncthreads();
+    bool restart = false;
+    for (int tile = t_begin; tile < t_end; ++tile) {
+      char HCA_LDS* cur = kv + ((tile - t_begin) & 1) * KV_BYTES;
+      char HCA_LDS* nxt = kv + (((tile - t_begin) & 1) ^ 1) * KV_BYTES;
+      if (tile + 1 < t_end) issue_tile<NW>(ks, tile + 1, nxt, nxt + NT * KSTR, wave, lane);
+      const bool over = compute_tile(cur, cur, qf, st, sc2, lane, koff, voff, rm, tile,
+                                     tile_needs_mask(tile, rm.nc, rm.nkeys), mode, two_term);
+      if (over && lane == 0) flag[(tile - t_begin) & 1] = 1;
+      wait_vm_all();
+      __syncthreads();
+      if (mode == kLazy && flag[(tile - t_begin) & 1]) {
+        restart = true;
+        break;
+      }
+    }
+    if (mode == kLazy && !restart) return;
+    if (mode == kFixed) return;
+    __syncthreads();  // every wave has read the flags before they are cleared
+    if (mode == kLazy) {
+      zero_acc(st);
+      mode = kMaxOnly;
+    } else {
+      st.l = 0.f;
+      mode = kFixed;
+    }
+  }
+}
+
+// Q^T fragments of one wavefront: lane l holds row (l%32), head-dim
+// elements 16k + 8(l/32) .. +7 for k-step k.
+__device__ __forceinline__ void load_q(const bf16* qrow, int lane, bf16x8 (&qf)[DSTEPS]) {
+  const bf16* p = qrow + 8 * (lane >> 5);
+#pragma unroll
+  for (int k = 0; k < DSTEPS; ++k) qf[k] = *(const bf16x8*)(p + 16 * k);
+}
+
+// ---------------------------------------------------------------------------
+// Prefill: grid (ceil(max_seqlen/2), batch, Hkv), 256 threads.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256, 1) void prefill_bf16_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) char kv_s[2 * (NT * KSTR + NT * VSTR)];
+  __shared__ int flag_s[2];
+
+  const int b = blockIdx.y, kvh = blockIdx.z;
+  const int start = a.cu_seqlens[b];
+  const int len = a.cu_seqlens[b + 1] - start;
+  // latest (heaviest) position pairs are dispatched first
+  const int pair = (int)gridDim.x - 1 - (int)blockIdx.x;
+  if (2 * pair >= len) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t0 = 2 * pair;
+  const bool t1_ok = t0 + 1 < len;
+  const int t_last = t1_ok ? t0 + 1 : t0;
+  const int pw = wave >> 1;                 // which of the two positions
+  const bool row_ok = pw == 0 || t1_ok;
+  const int t = row_ok ? t0 + pw : t0;      // an absent second position recomputes t0
+  const int head = kvh * G + (wave & 1) * 32 + (lane & 31);
+
+  const int nc = (t_last + 1) / kBlock;     // entries visible to the later position
+  const int lo = max(0, t0 - a.window + 1);  // oldest raw key of the earlier position
+  const int nkeys = nc + (t_last - lo + 1);
+
+  KeySource ks;
+  ks.rstride = (size_t)a.hkv * D * sizeof(bf16);
+  const size_t head_off = (size_t)kvh * D * sizeof(bf16);
+  ks.comp_k = (const char*)a.kc + (size_t)a.cu_blocks[b] * ks.rstride + head_off;
+  ks.comp_v = (const char*)a.vc + (size_t)a.cu_blocks[b] * ks.rstride + head_off;
+  ks.raw_k = (const char*)a.k + (size_t)start * ks.rstride + head_off;
+  ks.raw_v = (const char*)a.v + (size_t)start * ks.rstride + head_off;
+  ks.nc = nc;
+  ks.nkeys = nkeys;
+  ks.lo = lo;
+  ks.ring = 0;
+
+  RowMask rm;
+  rm.nc = nc;
+  rm.nvis_c = (t + 1) / kBlock;
+  rm.nkeys = nkeys;
+  rm.lo = lo;
+  rm.smin = t - a.window + 1;
+  rm.smax = t;
+
+  bf16x8 qf[DSTEPS];
+  const size_t qoff = ((size_t)(start + t) * a.hq + head) * D;
+  load_q((const bf16*)a.q + qoff, lane, qf);
+  Acc st;
+  const float sc2 = a.scale * kLog2e;
+  attend_tiles<4>(ks, 0, (nkeys + NT - 1) / NT, qf, st, sc2, rm, wave, lane, (char HCA_LDS*)kv_s,
+                  flag_s);
+
+  const float inv = 1.f / (st.l + __shfl_xor(st.l, 32));
+  if (!row_ok) return;
+  bf16* orow = (bf16*)a.o + qoff + 4 * (lane >> 5);
+#pragma unroll
+  for (int ct = 0; ct < CTILES; ++ct) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      bf16x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = (bf16)(st.o[ct][4 * q4 + i] * inv);
+      *(bf16x4*)(orow + 32 * ct + 8 * q4) = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode: grid (max_splits, batch, Hkv), 128 threads (2 wavefronts x 32 heads).
+// Workspace: int32 tickets [B*Hkv] (256-byte padded), then fp32 m and l
+// [B*Hkv][splits][64], then fp32 O [B*Hkv][splits][64][512].
+// ---------------------------------------------------------------------------
+struct WsLayout {
+  int* tickets;
+  float* m;
+  float* l;
+  float* o;
+};
+
+__host__ __device__ inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+__host__ __device__ inline WsLayout ws_layout(void* ws, int batch, int hkv, int splits) {
+  WsLayout w;
+  char* p = (char*)ws;
+  const size_t units = (size_t)batch * hkv;
+  w.tickets = (int*)p;
+  p += round_up(units * sizeof(int), 256);
+  w.m = (float*)p;
+  p += round_up(units * splits * G * sizeof(float), 256);
+  w.l = (float*)p;
+  p += round_up(units * splits * G * sizeof(float), 256);
+  w.o = (float*)p;
+  return w;
+}
+
+__global__ __launch_bounds__(128, 1) void decode_bf16_kernel(DecodeArgs a, int tps, int max_splits) {
+  __shared__ __attribute__((aligned(16))) char kv_s[2 * (NT * KSTR + NT * VSTR)];
+  __shared__ int ticket_s;
+  __shared__ int flag_s[2];
+
+  const int split = blockIdx.x, b = blockIdx.y, kvh = blockIdx.z;
+  const int L = a.seqlens[b];
+  const int t = L - 1;                        // the new token's position
+  const int nc = L / kBlock;                  // complete blocks: 128(j+1) <= t+1
+  const int nraw = min(a.window, L);
+  const int lo = L - nraw;
+  const int nkeys = nc + nraw;
+  const int ntiles = (nkeys + NT - 1) / NT;
+  const int nsplit = (ntiles + tps - 1) / tps;
+  if (split >= nsplit) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = wave * 32 + (lane & 31);    // head within the KV group
+  const int head = kvh * G + row;
+
+  KeySource ks;
+  ks.rstride = (size_t)a.hkv * D * sizeof(bf16);
+  const size_t head_off = (size_t)kvh * D * sizeof(bf16);
+  ks.comp_k = (const char*)a.kc + (size_t)a.cu_blocks[b] * ks.rstride + head_off;
+  ks.comp_v = (const char*)a.vc + (size_t)a.cu_blocks[b] * ks.rstride + head_off;
+  ks.raw_k = (const char*)a.kw + (size_t)b * a.ring * ks.rstride + head_off;
+  ks.raw_v = (const char*)a.vw + (size_t)b * a.ring * ks.rstride + head_off;
+  ks.nc = nc;
+  ks.nkeys = nkeys;
+  ks.lo = lo;
+  ks.ring = a.ring;
+
+  RowMask rm;
+  rm.nc = nc;
+  rm.nvis_c = nc;
+  rm.nkeys = nkeys;
+  rm.lo = lo;
+  rm.smin = lo;
+  rm.smax = t;
+
+  bf16x8 qf[DSTEPS];
+  load_q((const bf16*)a.q + ((size_t)b * a.hq + head) * D, lane, qf);
+  Acc st;
+  const float sc2 = a.scale * kLog2e;
+  const int t_begin = split * tps;
+  const int t_end = min(ntiles, t_begin + tps);
+  attend_tiles<2>(ks, t_begin, t_end, qf, st, sc2, rm, wave, lane, (char HCA_LDS*)kv_s, flag_s);
+
+  // partial results of this split
+  const WsLayout w = ws_layout(a.ws, a.batch, a.hkv, max_splits);
+  const size_t unit = (size_t)b * a.hkv + kvh;
+  const size_t prow = (unit * max_splits + split) * G + row;
+  const float l_tot = st.l + __shfl_xor(st.l, 32);
+  if (lane < 32) {
+    w.m[prow] = st.m;
+    w.l[prow] = l_tot;
+  }
+  float* po = w.o + prow * D + 4 * (lane >> 5);
+#pragma unroll
+  for (int ct = 0; ct < CTILES; ++ct) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      f32x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = st.o[ct][4 * q4 + i];
+      *(f32x4*)(po + 32 * ct + 8 * q4) = v;
+    }
+  }
+  // publish, then take a ticket; the last split of this unit merges
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) ticket_s = atomicAdd(&w.tickets[unit], 1);
+  __syncthreads();
+  if (ticket_s != nsplit - 1) return;
+  __threadfence();
+
+  // merge: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, splits in order
+  const float* mrow = w.m + unit * max_splits * G;
+  const float* lrow = w.l + unit * max_splits * G;
+  const float* obase = w.o + unit * max_splits * G * D;
+  const int c = threadIdx.x * 4;  // 128 threads x 4 columns
+  for (int r = 0; r < G; ++r) {
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, mrow[s * G + r]);
+    float den = 0.f;
+    f32x4 num = {};
+    for (int s = 0; s < nsplit; ++s) {
+      const float wgt = __builtin_amdgcn_exp2f(mrow[s * G + r] - M);
+      den += wgt * lrow[s * G + r];
+      const f32x4 os = *(const f32x4*)(obase + ((size_t)s * G + r) * D + c);
+      num += wgt * os;
+    }
+    const float inv = 1.f / den;
+    bf16x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (bf16)(num[i] * inv);
+    *(bf16x4*)((bf16*)a.o + ((size_t)b * a.hq + kvh * G + r) * D + c) = v;
+  }
+  if (threadIdx.x == 0) w.tickets[unit] = 0;  // ready for the next call
+}
+
+}  // namespace
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
+  dim3 grid((unsigned)((a.max_seqlen + 1) / 2), a.batch, a.hkv);
+  prefill_bf16_kernel<<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+DecodePlan decode_plan(int batch, int hkv, int max_blocks, int window) {
+  // keys of the longest sequence: its entries plus at most min(W, L) raw rows
+  const long raw = std::min<long>(window, (long)kBlock * max_blocks + kBlock - 1);
+  const int ntiles = (int)((max_blocks + raw + NT - 1) / NT);
+  const long units = std::max<long>(1, (long)batch * hkv);
+  // aim for about one workgroup per compute unit
+  int splits = (int)std::min<long>(ntiles, std::max<long>(1, (256 + units - 1) / units));
+  const int tps = (ntiles + splits - 1) / splits;
+  splits = (ntiles + tps - 1) / tps;
+  return DecodePlan{tps, splits};
+}
+
+size_t decode_workspace_bytes_bf16(int batch, int hkv, int max_blocks, int window) {
+  const DecodePlan p = decode_plan(batch, hkv, max_blocks, window);
+  const size_t units = (size_t)batch * hkv;
+  return round_up(units * sizeof(int), 256) + 2 * round_up(units * p.max_splits * G * sizeof(float), 256) +
+         units * p.max_splits * G * D * sizeof(float);
+}
+
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
+  const DecodePlan p = decode_plan(a.batch, a.hkv, a.max_blocks, a.window);
+  dim3 grid(p.max_splits, a.batch, a.hkv);
+  decode_bf16_kernel<<<grid, 128, 0, s>>>(a, p.tiles_per_split, p.max_splits);
+  return hipGetLastError();
+}
+
+}  // namespace hca

@@ -1,0 +1,127 @@
+// Block pooling: every complete 128-token block of K (and V) becomes one
+// cached entry (release blog "ERNIE 5.5 Flash Base", section 2.1, HCA
+// paragraph).  The pooling function is a softmax(w_h)-weighted sum over the
+// block's rows with a learned length-128 logit vector per KV head.
+//
+// HBM-bound (1 flop per byte).  One workgroup of 256 threads pools one
+// (entry, KV head, tensor) over a column slice of CW elements:
+//   - every thread owns 16 contiguous bytes of a row (VEC elements), TPR
+//     threads cover the slice of one row, RPP = 256/TPR rows are read per pass,
+//     so each load instruction reads whole rows of the slice (coalesced) and a
+//     workgroup keeps 128 rows x CW elements in flight over a few passes;
+//   - fp32 partial sums are reduced first across the rows held by one
+//     wavefront (lane shuffles) and then across the 4 wavefronts through LDS.
+#include "hca_internal.h"
+
+namespace hca {
+namespace {
+
+template <typename T, int TPR>
+__global__ __launch_bounds__(256) void compress_kernel(CompressArgs a, int cw) {
+  constexpr int VEC = 16 / sizeof(T);     // elements per 16-byte load
+  constexpr int RPP = 256 / TPR;          // rows per pass
+  constexpr int PASSES = kBlock / RPP;
+  static_assert(kBlock % RPP == 0, "rows per pass must divide the block");
+  __shared__ float p_s[kBlock];
+  __shared__ float red_s[4][TPR * VEC];
+  __shared__ float stat_s[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int entry_head = blockIdx.x;              // entry * hkv + head
+  const int h = entry_head % a.hkv;
+  const int entry = entry_head / a.hkv;
+  const int c0 = blockIdx.y * cw;                 // first column of the slice
+  const int which = blockIdx.z;                   // 0: K -> Kc, 1: V -> Vc
+
+  // pooling weights p = softmax(w_h), max-subtracted, in fp32
+  float wv = tid < kBlock ? a.w[h * kBlock + tid] : -INFINITY;
+  float mx = wv;
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if (lane == 0) stat_s[wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(stat_s[0], stat_s[1]), fmaxf(stat_s[2], stat_s[3]));
+  float e = tid < kBlock ? expf(wv - mx) : 0.f;
+  float sm = e;
+  for (int off = 32; off > 0; off >>= 1) sm += __shfl_xor(sm, off);
+  __syncthreads();
+  if (lane == 0) stat_s[wave] = sm;
+  __syncthreads();
+  sm = stat_s[0] + stat_s[1] + stat_s[2] + stat_s[3];
+  if (tid < kBlock) p_s[tid] = e / sm;
+
+  // which sequence owns this entry: largest b with cu_blocks[b] <= entry
+  int lo = 0, hi = a.batch;  // invariant: cu_blocks[lo] <= entry < cu_blocks[hi]
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (a.cu_blocks[mid] <= entry) lo = mid; else hi = mid;
+  }
+  const int j = entry - a.cu_blocks[lo];
+  const size_t tok0 = (size_t)a.cu_seqlens[lo] + (size_t)kBlock * j;
+  const size_t rstride = (size_t)a.hkv * a.d;     // elements between tokens
+  const T* x = (const T*)a.x[which] + tok0 * rstride + (size_t)h * a.d + c0 +
+               (tid % TPR) * VEC;
+  const int r0 = tid / TPR;
+  __syncthreads();
+
+  float acc[VEC];
+#pragma unroll
+  for (int c = 0; c < VEC; ++c) acc[c] = 0.f;
+#pragma unroll 8
+  for (int ps = 0; ps < PASSES; ++ps) {
+    const int row = ps * RPP + r0;
+    const float pr = p_s[row];
+    typedef T vec_t __attribute__((ext_vector_type(VEC)));
+    vec_t xv = *(const vec_t*)(x + (size_t)row * rstride);
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) acc[c] = fmaf(pr, to_f32(xv[c]), acc[c]);
+  }
+  // reduce over the rows a wavefront holds (lanes that differ in the bits
+  // above log2(TPR)), then over the 4 wavefronts
+#pragma unroll
+  for (int off = 32; off >= TPR; off >>= 1) {
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) acc[c] += __shfl_xor(acc[c], off);
+  }
+  if (lane < TPR) {
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) red_s[wave][lane * VEC + c] = acc[c];
+  }
+  __syncthreads();
+  for (int i = tid; i < TPR * VEC; i += 256) {
+    float s = (red_s[0][i] + red_s[1][i]) + (red_s[2][i] + red_s[3][i]);
+    T* out = (T*)a.xc[which] + ((size_t)entry * a.hkv + h) * a.d + c0;
+    out[i] = from_f32<T>(s);
+  }
+}
+
+template <typename T>
+hipError_t launch_typed(const CompressArgs& a, hipStream_t s) {
+  constexpr int VEC = 16 / sizeof(T);
+  // Largest column slice (at most 64 threads x 16 bytes per row, dividing d)
+  // that still gives at least ~1024 workgroups; never below 64 elements.
+  const long work = (long)a.total_blocks * a.hkv * (a.x[1] ? 2 : 1);
+  int cw = 64;
+  for (int c = 64 * VEC; c >= 64; c >>= 1) {
+    if (a.d % c) continue;
+    cw = c;
+    if (work * (a.d / c) >= 1024) break;
+  }
+  dim3 grid(a.total_blocks * a.hkv, a.d / cw, a.x[1] ? 2 : 1);
+  const int tpr = cw / VEC;
+  switch (tpr) {
+    case 64: compress_kernel<T, 64><<<grid, 256, 0, s>>>(a, cw); break;
+    case 32: compress_kernel<T, 32><<<grid, 256, 0, s>>>(a, cw); break;
+    case 16: compress_kernel<T, 16><<<grid, 256, 0, s>>>(a, cw); break;
+    case 8: compress_kernel<T, 8><<<grid, 256, 0, s>>>(a, cw); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_compress(int dtype, const CompressArgs& a, hipStream_t s) {
+  return dtype == 1 ? launch_typed<bf16>(a, s) : launch_typed<float>(a, s);
+}
+
+}  // namespace hca

@@ -1,0 +1,163 @@
+// Host side of the C ABI declared in include/hca.h: argument validation,
+// dispatch by dtype, launch-error mapping.  No allocation, no
+// synchronisation, no global mutable state.
+#include <math.h>
+
+#include "../../include/hca.h"
+#include "hca_internal.h"
+
+namespace {
+
+constexpr int32_t kMaxHeadDim = 1024;
+
+hca_status check_params(const hca_params* p) {
+  if (!p) return HCA_ERR_NULL;
+  if (p->num_q_heads < 1 || p->num_kv_heads < 1 || p->head_dim < 1 || p->window < 1)
+    return HCA_ERR_SHAPE;
+  if (p->num_q_heads % p->num_kv_heads) return HCA_ERR_SHAPE;
+  if (p->num_kv_heads > 65535) return HCA_ERR_SHAPE;
+  if (p->dtype != HCA_F32 && p->dtype != HCA_BF16) return HCA_ERR_UNSUPPORTED;
+  if (p->block != hca::kBlock) return HCA_ERR_UNSUPPORTED;
+  if (p->head_dim > kMaxHeadDim) return HCA_ERR_UNSUPPORTED;
+  if (!(p->softmax_scale == p->softmax_scale)) return HCA_ERR_SHAPE;  // NaN
+  return HCA_OK;
+}
+
+float scale_of(const hca_params* p) {
+  return p->softmax_scale > 0.f ? p->softmax_scale : 1.f / sqrtf((float)p->head_dim);
+}
+
+// The matrix-core path: 512-dim heads, 64 query heads per KV head.
+bool mfma_shape(const hca_params* p) {
+  return p->head_dim == 512 && p->num_q_heads / p->num_kv_heads == 64;
+}
+
+hca_status from_hip(hipError_t e) { return e == hipSuccess ? HCA_OK : HCA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* hca_version(void) { return "0.1.0"; }
+
+const char* hca_status_string(hca_status s) {
+  switch (s) {
+    case HCA_OK: return "HCA_OK";
+    case HCA_ERR_NULL: return "HCA_ERR_NULL: a required pointer is NULL";
+    case HCA_ERR_SHAPE: return "HCA_ERR_SHAPE: inconsistent or out-of-range sizes";
+    case HCA_ERR_UNSUPPORTED: return "HCA_ERR_UNSUPPORTED: shape or dtype not handled by this build";
+    case HCA_ERR_WORKSPACE: return "HCA_ERR_WORKSPACE: decode workspace missing or too small";
+    case HCA_ERR_HIP: return "HCA_ERR_HIP: the HIP runtime rejected a launch";
+  }
+  return "HCA_ERR_UNKNOWN";
+}
+
+hca_status hca_compress(const hca_params* params, int32_t batch, int32_t total_blocks,
+                        const int32_t* cu_seqlens, const int32_t* cu_blocks, const void* k,
+                        const void* v, const float* w, void* kc, void* vc, void* stream) {
+  hca_status st = check_params(params);
+  if (st != HCA_OK) return st;
+  if (batch < 0 || total_blocks < 0) return HCA_ERR_SHAPE;
+  if (params->head_dim % 64) return HCA_ERR_UNSUPPORTED;
+  if ((v == nullptr) != (vc == nullptr)) return HCA_ERR_NULL;
+  if ((long)total_blocks * params->num_kv_heads > 0x7fffffffL) return HCA_ERR_SHAPE;
+  if (total_blocks == 0) return HCA_OK;
+  if (batch == 0) return HCA_ERR_SHAPE;  // entries without sequences
+  if (!cu_seqlens || !cu_blocks || !k || !w || !kc) return HCA_ERR_NULL;
+  hca::CompressArgs a;
+  a.batch = batch;
+  a.total_blocks = total_blocks;
+  a.hkv = params->num_kv_heads;
+  a.d = params->head_dim;
+  a.cu_seqlens = cu_seqlens;
+  a.cu_blocks = cu_blocks;
+  a.x[0] = k;
+  a.x[1] = v;
+  a.xc[0] = kc;
+  a.xc[1] = vc;
+  a.w = w;
+  return from_hip(hca::launch_compress(params->dtype, a, (hipStream_t)stream));
+}
+
+hca_status hca_attend_prefill(const hca_params* params, int32_t batch, int32_t max_seqlen,
+                              const int32_t* cu_seqlens, const int32_t* cu_blocks, const void* q,
+                              const void* k, const void* v, const void* kc, const void* vc,
+                              void* o, void* stream) {
+  hca_status st = check_params(params);
+  if (st != HCA_OK) return st;
+  if (batch < 0 || max_seqlen < 0 || batch > 65535) return HCA_ERR_SHAPE;
+  if (params->dtype == HCA_BF16 && !mfma_shape(params)) return HCA_ERR_UNSUPPORTED;
+  if (params->dtype == HCA_F32 && (long)max_seqlen * params->num_q_heads > 0x7fffffffL)
+    return HCA_ERR_SHAPE;
+  if (batch == 0 || max_seqlen == 0) return HCA_OK;
+  if (!cu_seqlens || !cu_blocks || !q || !k || !v || !o) return HCA_ERR_NULL;
+  if (max_seqlen >= hca::kBlock && (!kc || !vc)) return HCA_ERR_NULL;
+  hca::PrefillArgs a;
+  a.batch = batch;
+  a.max_seqlen = max_seqlen;
+  a.hq = params->num_q_heads;
+  a.hkv = params->num_kv_heads;
+  a.d = params->head_dim;
+  a.window = params->window;
+  a.scale = scale_of(params);
+  a.cu_seqlens = cu_seqlens;
+  a.cu_blocks = cu_blocks;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.kc = kc;
+  a.vc = vc;
+  a.o = o;
+  hipStream_t s = (hipStream_t)stream;
+  return from_hip(params->dtype == HCA_BF16 ? hca::launch_prefill_bf16(a, s)
+                                            : hca::launch_prefill_f32(a, s));
+}
+
+size_t hca_decode_workspace_bytes(const hca_params* params, int32_t batch, int32_t max_blocks) {
+  if (check_params(params) != HCA_OK || batch < 0 || max_blocks < 0) return 0;
+  if (params->dtype == HCA_F32) return 0;
+  if (!mfma_shape(params)) return 0;
+  return hca::decode_workspace_bytes_bf16(batch, params->num_kv_heads, max_blocks, params->window);
+}
+
+hca_status hca_attend_decode(const hca_params* params, int32_t batch, int32_t max_blocks,
+                             const int32_t* seqlens, const int32_t* cu_blocks, const void* q,
+                             const void* kc, const void* vc, const void* kw, const void* vw,
+                             int32_t ring_cap, void* o, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  hca_status st = check_params(params);
+  if (st != HCA_OK) return st;
+  if (batch < 0 || max_blocks < 0 || batch > 65535) return HCA_ERR_SHAPE;
+  if (ring_cap < params->window) return HCA_ERR_SHAPE;
+  if (params->dtype == HCA_BF16 && !mfma_shape(params)) return HCA_ERR_UNSUPPORTED;
+  if (batch == 0) return HCA_OK;
+  if (!seqlens || !cu_blocks || !q || !kw || !vw || !o) return HCA_ERR_NULL;
+  if (max_blocks > 0 && (!kc || !vc)) return HCA_ERR_NULL;
+  hca::DecodeArgs a;
+  a.batch = batch;
+  a.max_blocks = max_blocks;
+  a.hq = params->num_q_heads;
+  a.hkv = params->num_kv_heads;
+  a.d = params->head_dim;
+  a.window = params->window;
+  a.ring = ring_cap;
+  a.scale = scale_of(params);
+  a.seqlens = seqlens;
+  a.cu_blocks = cu_blocks;
+  a.q = q;
+  a.kc = kc;
+  a.vc = vc;
+  a.kw = kw;
+  a.vw = vw;
+  a.o = o;
+  a.ws = workspace;
+  hipStream_t s = (hipStream_t)stream;
+  if (params->dtype == HCA_F32) return from_hip(hca::launch_decode_f32(a, s));
+  const size_t need =
+      hca::decode_workspace_bytes_bf16(batch, params->num_kv_heads, max_blocks, params->window);
+  if (!workspace || workspace_bytes < need) return HCA_ERR_WORKSPACE;
+  if (((uintptr_t)workspace) & 255) return HCA_ERR_WORKSPACE;
+  return from_hip(hca::launch_decode_bf16(a, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+// Internal declarations shared by the HIP translation units of libhca.
+// Not part of the public ABI (include/hca.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hca {
+
+// Tokens pooled into one compressed entry (release blog, section 2.1, HCA
+// paragraph: one cached entry per 128 tokens).
+constexpr int kBlock = 128;
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+#define HCA_LDS __attribute__((address_space(3)))
+
+// log2(e): exp(x) == exp2(x * log2(e)); folded into the score scale so the
+// softmax runs on the hardware base-2 exponential.
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+// float -> bf16 conversion rounds to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// Element type for a dtype code.
+template <int DT> struct dtype_of;
+template <> struct dtype_of<0> { typedef float type; };
+template <> struct dtype_of<1> { typedef bf16 type; };
+
+// ---------------------------------------------------------------------------
+// Launchers (defined in the .hip files, called from hca_api.hip after the
+// arguments were validated).  All return the hipError_t of the launch.
+// ---------------------------------------------------------------------------
+struct CompressArgs {
+  int batch, total_blocks, hkv, d;
+  const int* cu_seqlens;
+  const int* cu_blocks;
+  const void* x[2];  // K, V (x[1] may be null)
+  void* xc[2];       // Kc, Vc
+  const float* w;
+};
+hipError_t launch_compress(int dtype, const CompressArgs& a, hipStream_t s);
+
+struct PrefillArgs {
+  int batch, max_seqlen, hq, hkv, d, window;
+  float scale;
+  const int* cu_seqlens;
+  const int* cu_blocks;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* kc;
+  const void* vc;
+  void* o;
+};
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
+
+struct DecodeArgs {
+  int batch, max_blocks, hq, hkv, d, window, ring;
+  float scale;
+  const int* seqlens;
+  const int* cu_blocks;
+  const void* q;
+  const void* kc;
+  const void* vc;
+  const void* kw;
+  const void* vw;
+  void* o;
+  void* ws;
+};
+hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
+
+// Split plan of the bf16 decode kernel: tiles of 32 keys, `tiles_per_split`
+// tiles per workgroup, `max_splits` workgroups per (sequence, KV head).
+struct DecodePlan {
+  int tiles_per_split;
+  int max_splits;
+};
+DecodePlan decode_plan(int batch, int hkv, int max_blocks, int window);
+size_t decode_workspace_bytes_bf16(int batch, int hkv, int max_blocks, int window);
+
+}  // namespace hca

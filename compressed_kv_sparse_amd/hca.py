@@ -1,0 +1,172 @@
+"""ctypes binding of libhca (include/hca.h): argument marshalling only.
+
+Every function has the name of the C entry point it calls.  Tensors must be
+contiguous torch tensors on the current HIP device; outputs that are not
+passed in are allocated with torch (device memory plumbing) before the call.
+All work happens in the library's HIP kernels on torch's current stream.  If
+libhca.so has not been built the first call raises HcaLibraryMissing: there is
+no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libhca.so")
+
+HCA_F32, HCA_BF16 = 0, 1
+_DTYPES = {torch.float32: HCA_F32, torch.bfloat16: HCA_BF16}
+EXPORTS = ("hca_compress", "hca_attend_prefill", "hca_decode_workspace_bytes",
+           "hca_attend_decode", "hca_status_string", "hca_version")
+
+
+class HcaLibraryMissing(ImportError):
+    pass
+
+
+class HcaError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: {hca_status_string(status)} ({status})")
+
+
+class HcaParams(ctypes.Structure):
+    _fields_ = [
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+def make_params(num_q_heads, num_kv_heads, head_dim, window, dtype, block=128,
+                softmax_scale=0.0) -> HcaParams:
+    """dtype: torch.float32 / torch.bfloat16 or the hca_dtype code."""
+    code = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return HcaParams(int(num_q_heads), int(num_kv_heads), int(head_dim), int(block),
+                     int(window), float(softmax_scale), code)
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libhca.so once; raises HcaLibraryMissing if it was not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise HcaLibraryMissing(
+            f"{LIB_PATH} is missing: build it with `python -m compressed_kv_sparse_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(HcaParams)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.hca_compress.argtypes = [P, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.hca_compress.restype = ctypes.c_int
+    lib.hca_attend_prefill.argtypes = [P, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.hca_attend_prefill.restype = ctypes.c_int
+    lib.hca_decode_workspace_bytes.argtypes = [P, i32, i32]
+    lib.hca_decode_workspace_bytes.restype = sz
+    lib.hca_attend_decode.argtypes = [P, i32, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
+    lib.hca_attend_decode.restype = ctypes.c_int
+    lib.hca_status_string.argtypes = [ctypes.c_int]
+    lib.hca_status_string.restype = ctypes.c_char_p
+    lib.hca_version.argtypes = []
+    lib.hca_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def hca_status_string(status: int) -> str:
+    return library().hca_status_string(int(status)).decode()
+
+
+def hca_version() -> str:
+    return library().hca_version().decode()
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor arguments must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor arguments must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(fn, status):
+    if status != 0:
+        raise HcaError(fn, status)
+
+
+def hca_compress(params: HcaParams, cu_seqlens, cu_blocks, total_blocks: int, k, w, v=None,
+                 kc=None, vc=None, stream=None):
+    """Pool complete 128-token blocks of k (and v).  Returns (kc, vc)."""
+    batch = cu_seqlens.numel() - 1
+    shape = (int(total_blocks), k.shape[1], k.shape[2])
+    if kc is None:
+        kc = torch.empty(shape, dtype=k.dtype, device=k.device)
+    if v is not None and vc is None:
+        vc = torch.empty(shape, dtype=v.dtype, device=v.device)
+    st = library().hca_compress(ctypes.byref(params), batch, int(total_blocks), _ptr(cu_seqlens),
+                                _ptr(cu_blocks), _ptr(k), _ptr(v), _ptr(w), _ptr(kc), _ptr(vc),
+                                _stream(stream))
+    _check("hca_compress", st)
+    return kc, vc
+
+
+def hca_attend_prefill(params: HcaParams, cu_seqlens, cu_blocks, max_seqlen: int, q, k, v, kc, vc,
+                       o=None, stream=None):
+    """Causal HCA attention for a packed batch.  Returns o [N_tok, Hq, d]."""
+    batch = cu_seqlens.numel() - 1
+    if o is None:
+        o = torch.empty_like(q)
+    st = library().hca_attend_prefill(ctypes.byref(params), batch, int(max_seqlen), _ptr(cu_seqlens),
+                                      _ptr(cu_blocks), _ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc),
+                                      _ptr(o), _stream(stream))
+    _check("hca_attend_prefill", st)
+    return o
+
+
+def hca_decode_workspace_bytes(params: HcaParams, batch: int, max_blocks: int) -> int:
+    return int(library().hca_decode_workspace_bytes(ctypes.byref(params), int(batch), int(max_blocks)))
+
+
+def new_decode_workspace(params: HcaParams, batch: int, max_blocks: int, device=None):
+    """Zero-filled workspace of the size hca_attend_decode needs (or None)."""
+    n = hca_decode_workspace_bytes(params, batch, max_blocks)
+    if n == 0:
+        return None
+    return torch.zeros(n, dtype=torch.uint8, device=device or torch.cuda.current_device())
+
+
+def hca_attend_decode(params: HcaParams, seqlens, cu_blocks, max_blocks: int, q, kc, vc, kw, vw,
+                      workspace=None, o=None, stream=None):
+    """One query per sequence against its cache.  Returns o [B, Hq, d]."""
+    batch = seqlens.numel()
+    if o is None:
+        o = torch.empty_like(q)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = library().hca_attend_decode(ctypes.byref(params), batch, int(max_blocks), _ptr(seqlens),
+                                     _ptr(cu_blocks), _ptr(q), _ptr(kc), _ptr(vc), _ptr(kw), _ptr(vw),
+                                     int(kw.shape[1]), _ptr(o), _ptr(workspace), ws_bytes,
+                                     _stream(stream))
+    _check("hca_attend_decode", st)
+    return o
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)

@@ -1,0 +1,167 @@
+/*
+ * hca.h - C ABI of the Heavily Compressed Attention (HCA) layer forward for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (sources: "ERNIE 5.5 Flash Base" release blog, section 2.1,
+ * HCA paragraph; Zhidx article, section "1. Latent-Gated Sparse Attention";
+ * model card at nlp.com.ai, architecture paragraph):
+ *   an HCA layer stores one cached entry per run of 128 tokens and lets every
+ *   query attend to all complete entries together with a short window of the
+ *   most recent raw (uncompressed) tokens.  The pages do not fix the pooling
+ *   function or the window; this library uses
+ *     entry j of KV head h:  Kc[j,h] = sum_{i<128} softmax(w_h)_i * K[128j+i, h]
+ *                            (Vc likewise, with the same w_h),
+ *     keys of query t:       entries j with 128(j+1) <= t+1, then raw
+ *                            positions max(0, t-W+1) .. t (no de-duplication),
+ *     one softmax over all of them with scale 1/sqrt(head_dim),
+ *     query head q reads KV head q / (Hq/Hkv).
+ *
+ * Conventions for every entry point
+ *  - All tensor arguments are DEVICE pointers to caller-owned memory, row
+ *    major with head_dim contiguous.  The library never allocates, frees or
+ *    synchronises; every call is asynchronous on `stream` (a hipStream_t, or
+ *    NULL for the default stream).  It keeps no mutable global state.
+ *  - Host-side argument checks run before anything is enqueued; on failure a
+ *    non-zero hca_status is returned and nothing is launched.  A launch error
+ *    reported by the HIP runtime returns HCA_ERR_HIP.  Faults inside kernels
+ *    surface at the caller's next synchronisation.
+ *  - The contents of device metadata arrays (monotone cu_* prefix sums,
+ *    lengths within the cache capacity) are preconditions, not checked.
+ *  - Outputs must not alias inputs.
+ *  - dtype HCA_BF16: Q, K, V, Kc, Vc, rings and O are bfloat16; arithmetic is
+ *    fp32 accumulation (scores, softmax, pooling) with bf16 MFMA products;
+ *    outputs are rounded to nearest even.  dtype HCA_F32: everything fp32.
+ *  - Supported shapes: block == 128; window >= 1; num_q_heads a multiple of
+ *    num_kv_heads.  HCA_BF16 attention requires head_dim == 512 and
+ *    num_q_heads / num_kv_heads == 64 (the shape of the pages' model: 64 query
+ *    heads sharing KV, 512-dim heads); HCA_F32 accepts head_dim 1..1024 and any
+ *    group size.  hca_compress accepts any head_dim that is a multiple of 64,
+ *    up to 1024, in either dtype.
+ */
+#ifndef HCA_H
+#define HCA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define HCA_API __attribute__((visibility("default")))
+#else
+#define HCA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum hca_status {
+  HCA_OK = 0,
+  HCA_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  HCA_ERR_SHAPE = 2,       /* inconsistent or out-of-range sizes               */
+  HCA_ERR_UNSUPPORTED = 3, /* valid, but not a shape/dtype this build handles  */
+  HCA_ERR_WORKSPACE = 4,   /* decode workspace missing or too small            */
+  HCA_ERR_HIP = 5          /* the HIP runtime rejected a launch                */
+} hca_status;
+
+typedef enum hca_dtype { HCA_F32 = 0, HCA_BF16 = 1 } hca_dtype;
+
+typedef struct hca_params {
+  int32_t num_q_heads;  /* Hq                                                 */
+  int32_t num_kv_heads; /* Hkv, Hq % Hkv == 0                                 */
+  int32_t head_dim;     /* d (keys, queries and values share it)              */
+  int32_t block;        /* tokens per compressed entry; must be 128           */
+  int32_t window;       /* W >= 1: raw positions max(0,t-W+1)..t are visible  */
+  float softmax_scale;  /* <= 0 selects 1/sqrt(head_dim)                      */
+  int32_t dtype;        /* hca_dtype of every tensor except w (always fp32)   */
+} hca_params;
+
+/*
+ * hca_compress - pool every complete 128-token block of K (and V) into one
+ * cached entry (release blog, section 2.1, HCA paragraph: one cached entry
+ * per 128 tokens).
+ *
+ *   batch           number of packed sequences B >= 0
+ *   total_blocks    host copy of cu_blocks[B] (number of entries written)
+ *   cu_seqlens      device int32 [B+1], token offsets of each sequence
+ *   cu_blocks       device int32 [B+1], cu_blocks[b+1]-cu_blocks[b] ==
+ *                   floor((cu_seqlens[b+1]-cu_seqlens[b]) / 128)
+ *   k, v            device [N_tok, Hkv, d] raw keys / values; v may be NULL
+ *   w               device fp32 [Hkv, 128] pooling logits
+ *   kc, vc          device [total_blocks, Hkv, d] outputs; vc NULL iff v NULL
+ *
+ * Entry cu_blocks[b]+j, head h = sum_i softmax(w_h)_i * x[cu_seqlens[b]+128j+i, h]
+ * accumulated in fp32.  A trailing partial block is not pooled.
+ */
+HCA_API hca_status hca_compress(const hca_params* params, int32_t batch, int32_t total_blocks,
+                        const int32_t* cu_seqlens, const int32_t* cu_blocks,
+                        const void* k, const void* v, const float* w,
+                        void* kc, void* vc, void* stream);
+
+/*
+ * hca_attend_prefill - causal HCA attention for every token of a packed
+ * batch (release blog, section 2.1; Zhidx article, section 1: attention over
+ * the compressed entries plus a short raw window).
+ *
+ *   batch, max_seqlen  host: B and max_b (cu_seqlens[b+1]-cu_seqlens[b])
+ *   cu_seqlens, cu_blocks  device int32 [B+1] as for hca_compress
+ *   q               device [N_tok, Hq, d]
+ *   k, v            device [N_tok, Hkv, d] raw keys / values of the batch
+ *   kc, vc          device [cu_blocks[B], Hkv, d] entries (from hca_compress)
+ *   o               device [N_tok, Hq, d] output
+ *
+ * Token t (0-based within its sequence) attends to entries 0 ..
+ * floor((t+1)/128)-1 of its sequence and to raw tokens max(0,t-W+1) .. t.
+ */
+HCA_API hca_status hca_attend_prefill(const hca_params* params, int32_t batch, int32_t max_seqlen,
+                              const int32_t* cu_seqlens, const int32_t* cu_blocks,
+                              const void* q, const void* k, const void* v,
+                              const void* kc, const void* vc, void* o, void* stream);
+
+/*
+ * hca_decode_workspace_bytes - size in bytes of the scratch buffer that
+ * hca_attend_decode needs for `batch` sequences whose longest cache holds
+ * `max_blocks` entries.  Returns 0 for invalid params.
+ */
+HCA_API size_t hca_decode_workspace_bytes(const hca_params* params, int32_t batch, int32_t max_blocks);
+
+/*
+ * hca_attend_decode - one new query per sequence against its HCA cache
+ * (release blog, section 2.1: every query sees all complete entries plus the
+ * recent raw window).
+ *
+ *   batch, max_blocks  host: B and max_b floor(L_b / 128)
+ *   seqlens         device int32 [B], L_b >= 1 counts the new token, whose
+ *                   query sits at position L_b - 1
+ *   cu_blocks       device int32 [B+1]; sequence b owns entries
+ *                   [cu_blocks[b], cu_blocks[b+1]) and at least floor(L_b/128)
+ *   q               device [B, Hq, d]
+ *   kc, vc          device [cu_blocks[B], Hkv, d]
+ *   kw, vw          device [B, ring_cap, Hkv, d] raw rings: position s of
+ *                   sequence b is in slot s % ring_cap; ring_cap >= window
+ *   o               device [B, Hq, d] output
+ *   workspace       device scratch of workspace_bytes >=
+ *                   hca_decode_workspace_bytes(...), 256-byte aligned.  The
+ *                   first 4*batch*num_kv_heads bytes are per-(sequence, KV
+ *                   head) counters that must be ZERO before the first call
+ *                   (allocate the workspace zero-filled); every call that runs
+ *                   to completion leaves them zero again.  Calls that share one
+ *                   workspace must not overlap in time.  HCA_F32 needs no
+ *                   workspace (size 0; NULL is accepted).
+ */
+HCA_API hca_status hca_attend_decode(const hca_params* params, int32_t batch, int32_t max_blocks,
+                             const int32_t* seqlens, const int32_t* cu_blocks,
+                             const void* q, const void* kc, const void* vc,
+                             const void* kw, const void* vw, int32_t ring_cap,
+                             void* o, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+HCA_API const char* hca_status_string(hca_status status);
+
+/* Library version, e.g. "0.1.0" (static storage). */
+HCA_API const char* hca_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HCA_H */

@@ -1,0 +1,143 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry
+point include/hca.h declares, and rejects invalid arguments on the host before
+anything is launched (these calls never reach the HIP runtime)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import compressed_kv_sparse_amd as hca
+from compressed_kv_sparse_amd import hca as binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hca.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(6)
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"HCA_API\s+[\w\s\*]+?\b(hca_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return hca.library()
+
+
+def test_header_declares_the_binding_names():
+    assert declared_symbols() == sorted(hca.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_status_strings(lib):
+    assert hca.hca_version().count(".") == 2
+    for s in range(6):
+        assert hca.hca_status_string(s).startswith("HCA_")
+    assert hca.hca_status_string(99) == "HCA_ERR_UNKNOWN"
+
+
+def _p(**kw):
+    base = dict(num_q_heads=64, num_kv_heads=1, head_dim=512, window=128, dtype=hca.HCA_BF16)
+    base.update(kw)
+    return hca.make_params(**base)
+
+
+NULL = None
+DUMMY = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
+
+
+def _compress(lib, params, batch=1, total_blocks=1, cu=DUMMY, cub=DUMMY, k=DUMMY, v=DUMMY,
+              w=DUMMY, kc=DUMMY, vc=DUMMY):
+    pp = ctypes.byref(params) if params is not None else None
+    return lib.hca_compress(pp, batch, total_blocks, cu, cub, k, v, w, kc, vc, None)
+
+
+def _prefill(lib, params, batch=1, max_seqlen=256, ptrs=None):
+    p = [DUMMY] * 8 if ptrs is None else ptrs
+    pp = ctypes.byref(params) if params is not None else None
+    return lib.hca_attend_prefill(pp, batch, max_seqlen, *p, None)
+
+
+def _decode(lib, params, batch=1, max_blocks=4, ring=128, ws=DUMMY, ws_bytes=1 << 40, ptrs=None):
+    p = [DUMMY] * 7 if ptrs is None else ptrs
+    pp = ctypes.byref(params) if params is not None else None
+    return lib.hca_attend_decode(pp, batch, max_blocks, p[0], p[1], p[2], p[3], p[4], p[5], p[6],
+                                 ring, DUMMY, ws, ws_bytes, None)
+
+
+def test_compress_validation(lib):
+    assert _compress(lib, None) == ERR_NULL
+    assert _compress(lib, _p(block=64)) == ERR_UNSUPPORTED
+    assert _compress(lib, _p(head_dim=500)) == ERR_UNSUPPORTED
+    assert _compress(lib, _p(head_dim=2048)) == ERR_UNSUPPORTED
+    assert _compress(lib, _p(num_q_heads=3, num_kv_heads=2)) == ERR_SHAPE
+    assert _compress(lib, _p(window=0)) == ERR_SHAPE
+    assert _compress(lib, _p(dtype=7)) == ERR_UNSUPPORTED
+    assert _compress(lib, _p(), batch=-1) == ERR_SHAPE
+    assert _compress(lib, _p(), total_blocks=-1) == ERR_SHAPE
+    assert _compress(lib, _p(), v=NULL) == ERR_NULL          # v and vc must both be given or both NULL
+    assert _compress(lib, _p(), k=NULL) == ERR_NULL
+    assert _compress(lib, _p(), w=NULL) == ERR_NULL
+    assert _compress(lib, _p(), batch=0) == ERR_SHAPE        # entries without sequences
+    assert _compress(lib, _p(), total_blocks=0) == OK        # nothing to do: no launch
+
+
+def test_prefill_validation(lib):
+    assert _prefill(lib, None) == ERR_NULL
+    assert _prefill(lib, _p(head_dim=256)) == ERR_UNSUPPORTED   # bf16 path: d == 512 only
+    assert _prefill(lib, _p(num_q_heads=32)) == ERR_UNSUPPORTED  # bf16 path: 64 heads per KV head
+    assert _prefill(lib, _p(), batch=-1) == ERR_SHAPE
+    assert _prefill(lib, _p(), batch=70000) == ERR_SHAPE
+    assert _prefill(lib, _p(), max_seqlen=-5) == ERR_SHAPE
+    assert _prefill(lib, _p(), batch=0) == OK
+    assert _prefill(lib, _p(), max_seqlen=0) == OK
+    ptrs = [DUMMY] * 8
+    ptrs[2] = NULL  # q
+    assert _prefill(lib, _p(), ptrs=ptrs) == ERR_NULL
+    ptrs = [DUMMY] * 8
+    ptrs[5] = NULL  # kc needed once a block can complete
+    assert _prefill(lib, _p(), max_seqlen=128, ptrs=ptrs) == ERR_NULL
+    f32 = _p(dtype=hca.HCA_F32, num_q_heads=4, head_dim=64)
+    assert _prefill(lib, f32, max_seqlen=(1 << 30)) == ERR_SHAPE  # grid would overflow
+
+
+def test_decode_validation(lib):
+    assert _decode(lib, None) == ERR_NULL
+    assert _decode(lib, _p(), ring=64) == ERR_SHAPE              # ring shorter than the window
+    assert _decode(lib, _p(head_dim=128)) == ERR_UNSUPPORTED
+    assert _decode(lib, _p(), batch=-1) == ERR_SHAPE
+    assert _decode(lib, _p(), batch=0) == OK
+    assert _decode(lib, _p(), ws=NULL) == ERR_WORKSPACE
+    assert _decode(lib, _p(), ws_bytes=16) == ERR_WORKSPACE
+    assert _decode(lib, _p(), ws=ctypes.c_void_p(0x1010)) == ERR_WORKSPACE  # not 256-byte aligned
+    ptrs = [DUMMY] * 7
+    ptrs[0] = NULL  # seqlens
+    assert _decode(lib, _p(), ptrs=ptrs) == ERR_NULL
+
+
+def test_workspace_sizes(lib):
+    p = _p()
+    assert hca.hca_decode_workspace_bytes(_p(dtype=hca.HCA_F32, num_q_heads=4, head_dim=64), 8, 10) == 0
+    assert hca.hca_decode_workspace_bytes(_p(head_dim=100), 8, 10) == 0
+    assert hca.hca_decode_workspace_bytes(p, -1, 10) == 0
+    small = hca.hca_decode_workspace_bytes(p, 4, 8)
+    big = hca.hca_decode_workspace_bytes(p, 4, 8192)
+    assert 0 < small <= big
+    # at least one fp32 partial [64, 512] per (sequence, KV head)
+    assert small >= 4 * 64 * 512 * 4
+    # grows with the number of sequences
+    assert hca.hca_decode_workspace_bytes(p, 64, 1024) > hca.hca_decode_workspace_bytes(p, 8, 1024)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "libhca.so"))
+    with pytest.raises(hca.HcaLibraryMissing):
+        binding.library()

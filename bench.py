@@ -1,0 +1,402 @@
+#!/usr/bin/env python3
+"""Benchmark of the HCA layer forward (pooling + attention) on one MI355X.
+
+One step = one pass of the whole path over one batch of the workload:
+  prefill workloads: hca_compress (K and V) then hca_attend_prefill;
+  decode workload:   hca_attend_decode;
+  mixed_1m:          pooling + prefill of the 32768-token chunk, then decode
+                     of the 8 long-context sequences.
+The default workload is prefill_8k (B=1, T=8192, Hq=64, Hkv=1, d=512,
+W=128); `value` is its prefill throughput in tokens/s.  The same run also
+times decode_64x128k (64 queries against 128K-token caches) and reports it
+under "decode" (queries/s, HBM fraction).  Inputs are seeded synthetic
+tensors resident in HBM before the timed region.
+
+Per-kernel durations come from HIP events recorded on the stream the kernels
+run on, around every launch of the timed steps.  The roofline entries use
+algorithmic work: bytes (flops) the method must move (compute), not what the
+implementation adds.  `traffic` is filled from the counter summary in
+profiles/ when it was measured on the current kernel source, else null.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "HCA prefill tokens/s (%MFMA peak) + decode queries/s (%HBM peak), 1 GPU"
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3
+WORKLOADS = ("prefill_8k", "prefill_128k", "decode_64x128k", "mixed_1m", "tiny_f32")
+KERNEL_SOURCES = {
+    "prefill": "compressed_kv_sparse_amd/csrc/attend_bf16.hip",
+    "decode": "compressed_kv_sparse_amd/csrc/attend_bf16.hip",
+    "compress": "compressed_kv_sparse_amd/csrc/compress.hip",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work
+# ---------------------------------------------------------------------------
+def keys_visible(t, window, block=128):
+    return (t + 1) // block + min(window, t + 1)
+
+
+def prefill_work(c, lens, e):
+    """(bytes, flops) of one hca_attend_prefill launch: Q read + O write,
+    raw K+V read once, each compressed entry read once; 4*d*Hq flops per
+    visible (query, key) pair."""
+    ntok = sum(lens)
+    nblk = sum(l // c.block for l in lens)
+    byt = ntok * (2 * c.hq * c.d * e + 2 * c.hkv * c.d * e) + nblk * 2 * c.hkv * c.d * e
+    pairs = 0
+    for L in lens:
+        n = L // c.block
+        # sum over t of floor((t+1)/128): block j is seen by L - (128(j+1) - 1) tokens
+        comp = sum(L - (c.block * (j + 1) - 1) for j in range(n))
+        W = c.window
+        raw = (min(W, L) * (min(W, L) + 1)) // 2 + max(0, L - W) * W
+        pairs += comp + raw
+    return byt, 4 * c.d * c.hq * pairs
+
+
+def compress_work(c, lens, e):
+    nblk = sum(l // c.block for l in lens)
+    return nblk * c.hkv * (2 * c.block * c.d * e + 2 * c.d * e), nblk * c.hkv * 4 * c.block * c.d
+
+
+def decode_work(c, lens, e):
+    byt = 0
+    flops = 0
+    for L in lens:
+        nk = L // c.block + min(c.window, L)
+        byt += 2 * c.hq * c.d * e + 2 * c.hkv * c.d * e * nk
+        flops += 4 * c.d * c.hq * nk
+    return byt, flops
+
+
+# ---------------------------------------------------------------------------
+# timing helpers
+# ---------------------------------------------------------------------------
+class KernelClock:
+    """HIP event pairs around launches on torch's current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def run(self, name, fn):
+        t = self.torch
+        a = t.cuda.Event(enable_timing=True)
+        b = t.cuda.Event(enable_timing=True)
+        a.record()
+        out = fn()
+        b.record()
+        self.pairs.setdefault(name, []).append((a, b))
+        return out
+
+    def mean_ms(self, name):
+        ps = self.pairs.get(name, [])
+        return sum(a.elapsed_time(b) for a, b in ps) / max(1, len(ps))
+
+    def reset(self):
+        self.pairs = {}
+
+
+def source_sha(rel):
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from profiles/traffic_<kernel>_<workload>.txt if
+    the counters were taken on the current kernel source, else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha") != source_sha(KERNEL_SOURCES[kernel]):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def roofline(kernel, workload, byt, flops, ms, bound):
+    if bound == "hbm":
+        ach = byt / (ms * 1e-3) / 1e9
+        peak, unit = PEAK_HBM_GBS, "GB/s"
+    else:
+        ach = flops / (ms * 1e-3) / 1e12
+        peak, unit = PEAK_BF16_TFLOPS, "TFLOP/s"
+    return {"kernel": kernel, "bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
+            "frac": round(ach / peak, 4), "traffic": measured_traffic(kernel, workload),
+            "algorithmic_bytes": int(byt), "algorithmic_flops": int(flops), "avg_ms": round(ms, 5)}
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample
+# ---------------------------------------------------------------------------
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+
+        n = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:  # noqa: BLE001
+        return 1
+
+
+def cpu_baseline_prefill(c, inp, seconds):
+    import numpy as np
+    import torch
+
+    import oracle
+
+    T = inp["lens"][0]
+    cu = inp["cu_seqlens_host"]
+    k, v, w = inp["k"].cpu(), inp["v"].cpu(), inp["w"].cpu()
+    t0 = time.perf_counter()
+    kc = oracle.compress(k, w, cu)
+    vc = oracle.compress(v, w, cu)
+    t_pool = time.perf_counter() - t0
+    order = np.random.default_rng(5).permutation(T)
+    done = 0
+    t_att = 0.0
+    step = 16
+    while t_att < seconds and done < T:
+        rows = sorted(int(x) for x in order[done:done + step])
+        q_rows = inp["q"].index_select(0, torch.tensor(rows, device=inp["q"].device)).cpu()
+        t1 = time.perf_counter()
+        oracle.attend_prefill(q_rows, k, v, kc, vc, cu, c.window, rows=rows, q_holds_rows_only=True)
+        t_att += time.perf_counter() - t1
+        done += len(rows)
+    per_tok = t_att / done + t_pool / T
+    return {"value": round(1.0 / per_tok, 3), "unit": "tokens/s", "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": f"{done} of {T} query rows (seeded random) attended in {t_att:.1f} s plus "
+                      f"pooling of all {len(kc)} blocks in {t_pool:.1f} s, prorated per token"}
+
+
+def cpu_baseline_decode(c, inp, seconds):
+    import oracle
+
+    lens = inp["lens"]
+    done = 0
+    t_all = 0.0
+    while t_all < seconds and done < len(lens):
+        b = done
+        t1 = time.perf_counter()
+        nb = lens[b] // c.block
+        cb = int(inp["cu_blocks_host"][b])
+        oracle.attend_decode(inp["q"][b:b + 1].cpu(), inp["kc"][cb:cb + nb].cpu(),
+                             inp["vc"][cb:cb + nb].cpu(), inp["kw"][b:b + 1].cpu(),
+                             inp["vw"][b:b + 1].cpu(), [lens[b]], [0, nb], c.window)
+        t_all += time.perf_counter() - t1
+        done += 1
+    return {"value": round(done / t_all, 3), "unit": "queries/s", "cores": blas_threads(),
+            "kind": "oracle", "sample": f"{done} of {len(lens)} queries in {t_all:.1f} s"}
+
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+def run_prefill(torch, hca, c, steps, warmup, clock, lens=None):
+    from hca_workloads import prefill_inputs
+
+    inp = prefill_inputs(c, "cuda", lens=lens)
+    dt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
+    p = hca.make_params(c.hq, c.hkv, c.d, c.window, dt)
+    kc = torch.empty((max(1, inp["total_blocks"]), c.hkv, c.d), dtype=dt, device="cuda")
+    vc = torch.empty_like(kc)
+    o = torch.empty_like(inp["q"])
+
+    def step():
+        clock.run("compress", lambda: hca.hca_compress(p, inp["cu_seqlens"], inp["cu_blocks"],
+                                                       inp["total_blocks"], inp["k"], inp["w"],
+                                                       v=inp["v"], kc=kc, vc=vc))
+        clock.run("prefill", lambda: hca.hca_attend_prefill(p, inp["cu_seqlens"], inp["cu_blocks"],
+                                                            inp["max_seqlen"], inp["q"], inp["k"],
+                                                            inp["v"], kc, vc, o=o))
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    clock.reset()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return inp, wall
+
+
+def run_decode(torch, hca, c, steps, warmup, clock, n_sets=4):
+    """Rotates n_sets independent caches so repeats do not hit in the 256 MiB
+    last-level cache."""
+    from hca_workloads import decode_inputs
+
+    sets = [decode_inputs(c, "cuda", seed=c.seed + 17 * i) for i in range(n_sets)]
+    p = hca.make_params(c.hq, c.hkv, c.d, c.window, torch.bfloat16)
+    ws = [hca.new_decode_workspace(p, len(s["lens"]), s["max_blocks"]) for s in sets]
+    outs = [torch.empty_like(s["q"]) for s in sets]
+
+    def step(i):
+        s = sets[i % n_sets]
+        clock.run("decode", lambda: hca.hca_attend_decode(p, s["seqlens"], s["cu_blocks"],
+                                                          s["max_blocks"], s["q"], s["kc"], s["vc"],
+                                                          s["kw"], s["vw"], workspace=ws[i % n_sets],
+                                                          o=outs[i % n_sets]))
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    clock.reset()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return sets[0], wall
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill_8k", choices=WORKLOADS)
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode_64x128k companion")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs the HCA forward on one GPU only; "
+              f"--gpus {args.gpus} (WORLD_SIZE={world}) is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import compressed_kv_sparse_amd as hca
+    from hca_workloads import CONFIGS
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    hca.library()  # fails loudly if libhca.so is missing
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n}))
+        return
+
+    clock = KernelClock(torch)
+    c = CONFIGS[args.workload]
+    e = 2 if c.dtype == "bf16" else 4
+    result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+              "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+              "dtype": c.dtype, "data": "synthetic (seeded random tensors of the workload's shapes)"}
+    kernels = {}
+
+    if c.has_prefill:
+        log(f"[bench] {c.name}: prefill lens={list(c.prefill_lens)} steps={args.steps}")
+        inp, wall = run_prefill(torch, hca, c, args.steps, args.warmup, clock)
+        lens = inp["lens"]
+        pb, pf = prefill_work(c, lens, e)
+        cb, cf = compress_work(c, lens, e)
+        t_pre, t_cmp = clock.mean_ms("prefill"), clock.mean_ms("compress")
+        ms_step = wall * 1e3 / args.steps
+        ntok = sum(lens)
+        bound = "hbm" if pf / pb < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "mfma"
+        kernels["prefill"] = roofline("prefill", c.name, pb, pf, t_pre, bound)
+        kernels["prefill"]["mfma_frac"] = round(pf / (t_pre * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+        kernels["prefill"]["hbm_frac"] = round(pb / (t_pre * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        kernels["compress"] = roofline("compress", c.name, cb, cf, t_cmp, "hbm")
+        result.update({"value": round(ntok / (ms_step * 1e-3), 1), "unit": "tokens/s",
+                       "ms_per_step": round(ms_step, 4)})
+        result["config"] = {"workload": c.name, "batch": len(lens), "seq_len": max(lens),
+                            "q_heads": c.hq, "kv_heads": c.hkv, "head_dim": c.d, "window": c.window,
+                            "block": c.block, "parallelism": "none (1 GPU)"}
+        result["roofline"] = kernels["prefill"]
+        if not args.no_cpu_baseline:
+            log(f"[bench] cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")
+            result["cpu_baseline"] = cpu_baseline_prefill(c, inp, args.cpu_seconds)
+        del inp
+        torch.cuda.empty_cache()
+
+    dcfg = None
+    if c.name == "decode_64x128k":
+        dcfg = c
+    elif c.name == "mixed_1m":
+        dcfg = c
+    elif c.name == "prefill_8k" and not args.no_decode:
+        dcfg = CONFIGS["decode_64x128k"]
+    if dcfg is not None:
+        log(f"[bench] {dcfg.name}: decode steps={args.steps}")
+        clock.reset()
+        dinp, dwall = run_decode(torch, hca, dcfg, args.steps, args.warmup, clock)
+        db, df = decode_work(dcfg, dinp["lens"], 2)
+        t_dec = clock.mean_ms("decode")
+        kernels["decode"] = roofline("decode", dcfg.name, db, df, t_dec, "hbm")
+        dec = {"workload": dcfg.name, "queries_per_s": round(len(dinp["lens"]) / (t_dec * 1e-3), 1),
+               "unit": "queries/s", "ms_per_call": round(t_dec, 5), "batch": len(dinp["lens"]),
+               "context_lens": dinp["lens"] if len(dinp["lens"]) <= 8 else f"{dinp['lens'][0]} each",
+               "roofline": kernels["decode"]}
+        if not args.no_cpu_baseline:
+            dec["cpu_baseline"] = cpu_baseline_decode(dcfg, dinp, min(10.0, args.cpu_seconds))
+        if c.has_prefill:
+            result["decode"] = dec
+            if c.name == "mixed_1m":
+                # one step = chunk prefill (pooling + attention) + the decode batch
+                ms_step = result["ms_per_step"] + t_dec
+                ntok = sum(c.prefill_lens) + len(dinp["lens"])
+                result["value"] = round(ntok / (ms_step * 1e-3), 1)
+                result["ms_per_step"] = round(ms_step, 4)
+                result["unit"] = "tokens/s"
+        else:
+            result.update({"value": dec["queries_per_s"], "unit": "queries/s",
+                           "ms_per_step": round(dwall * 1e3 / args.steps, 4)})
+            result["config"] = {"workload": dcfg.name, "batch": len(dinp["lens"]),
+                                "context": dinp["lens"][0], "q_heads": dcfg.hq, "kv_heads": dcfg.hkv,
+                                "head_dim": dcfg.d, "window": dcfg.window, "block": dcfg.block,
+                                "parallelism": "none (1 GPU)"}
+            result["roofline"] = kernels["decode"]
+            if "cpu_baseline" in dec:
+                result["cpu_baseline"] = dec["cpu_baseline"]
+    result["kernels"] = kernels
+    order = ["metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+             "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"]
+    out = {k: result[k] for k in order if k in result}
+    out.update({k: v for k, v in result.items() if k not in out})
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -35,10 +35,10 @@
 //    accumulators per lane therefore live in AGPRs and are only ever touched
 //    by the matrix cores; softmax(x) = exp(x - c)/sum exp(x - c) holds for any
 //    c, so the result is the same up to rounding.
-//  * Decode: one workgroup of 2 wavefronts (64 heads of one query) per
-//    (sequence, KV head, key split); fp32 partials (m, l, unnormalised O) go
-//    to the workspace and the last split to finish (atomic ticket) merges
-//    them in split order, so the result is deterministic.
+//  * Decode: one workgroup of 4 wavefronts x 16 heads (v_mfma 16x16x32) per
+//    (sequence, KV head, key split); fp32 partials (m, l, O/l) go to the
+//    workspace and the last split to finish (atomic ticket) merges them in
+//    split order, so the result is deterministic.
 #include <algorithm>
 
 #include "hca_internal.h"
@@ -66,15 +66,16 @@ enum Mode { kLazy = 0, kMaxOnly = 1, kFixed = 2 };
 
 // Where the keys of one workgroup come from.  Slot kappa < nc is compressed
 // entry kappa of the sequence; slot kappa >= nc is raw position
-// lo + (kappa - nc), stored at row `pos` of raw_k/raw_v, or at row pos % ring
-// when ring > 0 (decode ring buffer).
+// lo + (kappa - nc), stored at that row of raw_k/raw_v, or at row
+// (lo + kappa - nc) % ring when ring > 0 (decode ring buffer).
 struct KeySource {
   const char* comp_k;
   const char* comp_v;
   const char* raw_k;
   const char* raw_v;
   size_t rstride;  // bytes between consecutive rows (Hkv * D * 2)
-  int nc, nkeys, lo, ring;
+  int nc, nkeys, ring;
+  int raw0;        // row of the oldest raw key: lo, or lo % ring in a ring
 };
 
 // Which slots a row (one query position t) may see.
@@ -107,8 +108,10 @@ __device__ __forceinline__ void issue_tile(const KeySource& ks, int tile, char H
       ksrc = ks.comp_k + (size_t)kappa * ks.rstride;
       vsrc = ks.comp_v + (size_t)kappa * ks.rstride;
     } else {
-      int pos = ks.lo + (kappa - ks.nc);
-      if (ks.ring) pos %= ks.ring;
+      // raw position lo + r; in a ring it sits in slot (lo % R + r) mod R and
+      // r < R, so one wrap-around subtraction replaces the modulo
+      int pos = ks.raw0 + (kappa - ks.nc);
+      if (ks.ring && pos >= ks.ring) pos -= ks.ring;
       ksrc = ks.raw_k + (size_t)pos * ks.rstride;
       vsrc = ks.raw_v + (size_t)pos * ks.rstride;
     }
@@ -138,6 +141,14 @@ __device__ __forceinline__ bf16x8 lds_v_frag(const char HCA_LDS* base) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// A fragment of V^T for one 16-column tile of the 16x16x32 product: keys
+// {4g + j} and {16 + 4g + j}, j < 4, g = l/16.
+__device__ __forceinline__ bf16x8 lds_v_frag16(const char HCA_LDS* base) {
+  const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 HCA_LDS*)base);
+  const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 HCA_LDS*)(base + 16 * VSTR));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // One key tile.  kLazy: scores, reference max fixed at the row's first
 // visible key, weights and P.V; returns true (for the whole wave) if a score
 // exceeded the reference by more than kHeadroom.  kMaxOnly: scores and row
@@ -147,13 +158,12 @@ __device__ __forceinline__ bf16x8 lds_v_frag(const char HCA_LDS* base) {
 // bf16 numbers, P = hi + lo, lo = bf16(P - hi), which carries P to ~2^-16
 // relative instead of 2^-9: rows that see only a few keys have few, large
 // weights whose rounding does not average out.
+template <int MODE>
 __device__ __forceinline__ bool compute_tile(const char HCA_LDS* kbuf, const char HCA_LDS* vbuf,
                                              const bf16x8 (&qf)[DSTEPS], Acc& st, float sc2,
                                              int lane, int koff, int voff, const RowMask& rm,
-                                             int tile, bool masked, int mode, bool two_term) {
-  // S^T = K . Q^T over the 512-wide head dim: 32 k-steps of 16, with the K
-  // fragments read PF steps ahead of their MFMA
-  constexpr int PF = 4;
+                                             int tile, bool masked, bool two_term) {
+  constexpr int PF = 2;  // fragments read ahead of their MFMA
   f32x16 s = {};
   bf16x8 kf[PF];
 #pragma unroll
@@ -163,53 +173,49 @@ __device__ __forceinline__ bool compute_tile(const char HCA_LDS* kbuf, const cha
     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[k % PF], qf[k], s, 0, 0, 0);
     if (k + PF < DSTEPS) kf[k % PF] = lds_k_frag(kbuf + koff + (k + PF) * 32);
   }
-  // scale into log2 units, mask, row max over the lane pair
-  float x[16];
+  // scale into log2 units (in place), mask, row max over the lane pair
 #pragma unroll
-  for (int i = 0; i < 16; ++i) x[i] = s[i] * sc2;
+  for (int i = 0; i < 16; ++i) s[i] *= sc2;
   if (masked) {
     const int kk0 = tile * NT + 4 * (lane >> 5);
 #pragma unroll
     for (int i = 0; i < 16; ++i)  // accumulator i holds key slot 8(i/4) + 4(l/32) + i%4
-      if (!rm.valid(kk0 + 8 * (i >> 2) + (i & 3))) x[i] = -INFINITY;
+      if (!rm.valid(kk0 + 8 * (i >> 2) + (i & 3))) s[i] = -INFINITY;
   }
-  float mx = x[0];
+  float mx = s[0];
 #pragma unroll
-  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
+  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
   mx = fmaxf(mx, __shfl_xor(mx, 32));
-  if (mode == kMaxOnly) {
+  if (MODE == kMaxOnly) {
     st.m = fmaxf(st.m, mx);
     return false;
   }
   bool over = false;
-  if (mode == kLazy) {
+  if (MODE == kLazy) {
     if (st.m == -INFINITY) st.m = mx;  // first visible keys of the row
     over = mx > st.m + kHeadroom;
   }
   const float m_use = st.m == -INFINITY ? 0.f : st.m;  // row with no visible key yet
-  float pv[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(x[i] - m_use);
+  for (int i = 0; i < 16; ++i) s[i] = __builtin_amdgcn_exp2f(s[i] - m_use);
   bf16x8 pa, pb, qa = {}, qb = {};
   float ls = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    pa[j] = (bf16)pv[j];
-    pb[j] = (bf16)pv[8 + j];
+    pa[j] = (bf16)s[j];
+    pb[j] = (bf16)s[8 + j];
   }
   if (two_term) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      qa[j] = (bf16)(pv[j] - (float)pa[j]);
-      qb[j] = (bf16)(pv[8 + j] - (float)pb[j]);
+      qa[j] = (bf16)(s[j] - (float)pa[j]);
+      qb[j] = (bf16)(s[8 + j] - (float)pb[j]);
       ls += (float)qa[j] + (float)qb[j];
     }
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) ls += (float)pa[j] + (float)pb[j];  // sum of the weights used
   st.l += ls;
-  // O^T += V^T . P^T over 16 column tiles x 2 key steps, V fragments read
-  // PF steps ahead; a second pass adds the low parts of two-term weights
   const int parts = two_term ? 2 : 1;
   for (int part = 0; part < parts; ++part) {
     const bf16x8 ba = part ? qa : pa;
@@ -225,7 +231,7 @@ __device__ __forceinline__ bool compute_tile(const char HCA_LDS* kbuf, const cha
       if (un < 2 * CTILES) vf[u % PF] = lds_v_frag(vbuf + voff + (un & 1) * 16 * VSTR + (un >> 1) * 64);
     }
   }
-  return mode == kLazy && __any(over);
+  return MODE == kLazy && __any(over);
 }
 
 __device__ __forceinline__ bool tile_needs_mask(int tile, int nc, int nkeys) {
@@ -243,57 +249,50 @@ __device__ __forceinline__ void zero_acc(Acc& st) {
   st.l = 0.f;
 }
 
-// All tiles of [t_begin, t_end): the single-pass schedule, and the exact
-// two-pass schedule if a row's scores grow past the headroom.  Tiles stream
-// through a double-buffered LDS area `kv` (buffer i: K rows at i*KV_BYTES,
-// V rows after them).  The headroom test crosses waves through flag[2]: tile
-// i writes flag[i & 1] before the barrier that ends it and every wave reads
-// that slot right after the barrier; a wave can only write the other slot
-// before the next barrier, so no wave sees a flag set for a later tile.
+// One pass over tiles [t_begin, t_end) in schedule MODE.  Returns true (for
+// every wave) if a kLazy pass stopped because the headroom was exceeded.
+template <int NW, int MODE>
+__device__ __forceinline__ bool tile_pass(const KeySource& ks, int t_begin, int t_end,
+                                          const bf16x8 (&qf)[DSTEPS], Acc& st, float sc2,
+                                          const RowMask& rm, int wave, int lane, char HCA_LDS* kv,
+                                          int* flag, bool two_term) {
+  constexpr int KV_BYTES = NT * KSTR + NT * VSTR;
+  const int koff = (lane & 31) * KSTR + (lane >> 5) * 16;
+  const int voff = NT * KSTR + (4 * (lane >> 5) + ((lane & 15) >> 2)) * VSTR +
+                   (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+  if (MODE == kLazy && threadIdx.x == 0) flag[0] = flag[1] = 0;
+  issue_tile<NW>(ks, t_begin, kv, kv + NT * KSTR, wave, lane);
+  wait_vm_all();
+  __syncthreads();
+  for (int tile = t_begin; tile < t_end; ++tile) {
+    char HCA_LDS* cur = kv + ((tile - t_begin) & 1) * KV_BYTES;
+    char HCA_LDS* nxt = kv + (((tile - t_begin) & 1) ^ 1) * KV_BYTES;
+    if (tile + 1 < t_end) issue_tile<NW>(ks, tile + 1, nxt, nxt + NT * KSTR, wave, lane);
+    const bool over = compute_tile<MODE>(cur, cur, qf, st, sc2, lane, koff, voff, rm, tile,
+                                         tile_needs_mask(tile, rm.nc, rm.nkeys), two_term);
+    if (MODE == kLazy && over && lane == 0) flag[(tile - t_begin) & 1] = 1;
+    wait_vm_all();
+    __syncthreads();
+    if (MODE == kLazy && flag[(tile - t_begin) & 1]) return true;
+  }
+  return false;
+}
+
+// All tiles of [t_begin, t_end): the single-pass schedule, then, only if a
+// row's scores grew past the headroom, the exact two-pass schedule.
 template <int NW>
 __device__ __forceinline__ void attend_tiles(const KeySource& ks, int t_begin, int t_end,
                                              const bf16x8 (&qf)[DSTEPS], Acc& st, float sc2,
                                              const RowMask& rm, int wave, int lane,
                                              char HCA_LDS* kv, int* flag) {
-  constexpr int KV_BYTES = NT * KSTR + NT * VSTR;
-  const int koff = (lane & 31) * KSTR + (lane >> 5) * 16;
-  const int voff = NT * KSTR + (4 * (lane >> 5) + ((lane & 15) >> 2)) * VSTR +
-                   (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
-  zero_acc(st);
-  // few keys: few, large weights, carried as two bf16 terms (see compute_tile)
   const bool two_term = rm.nkeys <= kTwoTermKeys;
-  int mode = kLazy;
-  for (;;) {
-    if (threadIdx.x == 0) flag[0] = flag[1] = 0;
-    issue_tile<NW>(ks, t_begin, kv, kv + NT * KSTR, wave, lane);
-    wait_vm_all();
-    __syncthreads();
-    bool restart = false;
-    for (int tile = t_begin; tile < t_end; ++tile) {
-      char HCA_LDS* cur = kv + ((tile - t_begin) & 1) * KV_BYTES;
-      char HCA_LDS* nxt = kv + (((tile - t_begin) & 1) ^ 1) * KV_BYTES;
-      if (tile + 1 < t_end) issue_tile<NW>(ks, tile + 1, nxt, nxt + NT * KSTR, wave, lane);
-      const bool over = compute_tile(cur, cur, qf, st, sc2, lane, koff, voff, rm, tile,
-                                     tile_needs_mask(tile, rm.nc, rm.nkeys), mode, two_term);
-      if (over && lane == 0) flag[(tile - t_begin) & 1] = 1;
-      wait_vm_all();
-      __syncthreads();
-      if (mode == kLazy && flag[(tile - t_begin) & 1]) {
-        restart = true;
-        break;
-      }
-    }
-    if (mode == kLazy && !restart) return;
-    if (mode == kFixed) return;
-    __syncthreads();  // every wave has read the flags before they are cleared
-    if (mode == kLazy) {
-      zero_acc(st);
-      mode = kMaxOnly;
-    } else {
-      st.l = 0.f;
-      mode = kFixed;
-    }
-  }
+  zero_acc(st);
+  if (!tile_pass<NW, kLazy>(ks, t_begin, t_end, qf, st, sc2, rm, wave, lane, kv, flag, two_term))
+    return;
+  __syncthreads();
+  zero_acc(st);
+  tile_pass<NW, kMaxOnly>(ks, t_begin, t_end, qf, st, sc2, rm, wave, lane, kv, flag, two_term);
+  tile_pass<NW, kFixed>(ks, t_begin, t_end, qf, st, sc2, rm, wave, lane, kv, flag, two_term);
 }
 
 // Q^T fragments of one wavefront: lane l holds row (l%32), head-dim
@@ -340,7 +339,7 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_kernel(PrefillArgs a) {
   ks.raw_v = (const char*)a.v + (size_t)start * ks.rstride + head_off;
   ks.nc = nc;
   ks.nkeys = nkeys;
-  ks.lo = lo;
+  ks.raw0 = lo;
   ks.ring = 0;
 
   RowMask rm;
@@ -375,9 +374,161 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_kernel(PrefillArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode: grid (max_splits, batch, Hkv), 128 threads (2 wavefronts x 32 heads).
+// Decode tiles: 16 query heads per wavefront on v_mfma_f32_16x16x32_bf16.
+// Decode streams each key once from HBM and does 64 flops per byte, far
+// below the matrix-core ridge, so it uses the narrower product: a wavefront
+// then needs 128 accumulator and 64 query registers instead of 256 and 128.
+// Layouts (16x16x32): A lane l = row l%16, k 8(l/16)..+7; B lane l = col
+// l%16, k 8(l/16)..+7; D lane l = rows 4(l/16)..+3, col l%16.
+// ---------------------------------------------------------------------------
+constexpr int DSTEPS16 = D / 32;  // k-steps of the score product
+constexpr int CTILES16 = D / 16;  // 16-column tiles of the output
+
+struct Acc16 {
+  f32x4 o[CTILES16];  // O^T: lane l holds row l%16, cols 16ct + 4(l/16) + i
+  float m, l;
+};
+
+// Scores of one 32-key tile land as S^T in two 16x16 outputs: lane l holds
+// row l%16 and key slots 4g + i (first output) and 16 + 4g + i (second),
+// g = l/16.  P^T as the B operand of the 16x16x32 product needs for lane l
+// the 8 keys k = 8g + j; taking j < 4 -> 4g + j and j >= 4 -> 16 + 4g + j-4
+// makes P come straight from those accumulators, and the V^T A operand reads
+// the same two 4-key runs with two transposed LDS reads.
+template <int MODE>
+__device__ __forceinline__ bool compute_tile16(const char HCA_LDS* kbuf, const char HCA_LDS* vbuf,
+                                               const bf16x8 (&qf)[DSTEPS16], Acc16& st, float sc2,
+                                               int lane, int koff, int voff, const RowMask& rm,
+                                               int tile, bool masked, bool two_term) {
+  constexpr int PF = 2;
+  f32x4 s0 = {}, s1 = {};
+  bf16x8 kf[2 * PF];
+#pragma unroll
+  for (int k = 0; k < PF; ++k) {
+    kf[2 * k] = lds_k_frag(kbuf + koff + k * 64);
+    kf[2 * k + 1] = lds_k_frag(kbuf + koff + 16 * KSTR + k * 64);
+  }
+#pragma unroll
+  for (int k = 0; k < DSTEPS16; ++k) {
+    const int r = (k % PF) * 2;
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[r], qf[k], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[r + 1], qf[k], s1, 0, 0, 0);
+    if (k + PF < DSTEPS16) {
+      kf[r] = lds_k_frag(kbuf + koff + (k + PF) * 64);
+      kf[r + 1] = lds_k_frag(kbuf + koff + 16 * KSTR + (k + PF) * 64);
+    }
+  }
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = s0[i] * sc2;
+    x[4 + i] = s1[i] * sc2;
+  }
+  if (masked) {
+    const int kk0 = tile * NT + 4 * (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (!rm.valid(kk0 + (i >> 2) * 16 + (i & 3))) x[i] = -INFINITY;
+  }
+  float mx = x[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16));  // lanes l, l^16, l^32, l^48 share row l%16
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  if (MODE == kMaxOnly) {
+    st.m = fmaxf(st.m, mx);
+    return false;
+  }
+  bool over = false;
+  if (MODE == kLazy) {
+    if (st.m == -INFINITY) st.m = mx;
+    over = mx > st.m + kHeadroom;
+  }
+  const float m_use = st.m == -INFINITY ? 0.f : st.m;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = __builtin_amdgcn_exp2f(x[i] - m_use);
+  bf16x8 pa, qa = {};
+  float ls = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) pa[j] = (bf16)x[j];
+  if (two_term) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      qa[j] = (bf16)(x[j] - (float)pa[j]);
+      ls += (float)qa[j];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ls += (float)pa[j];
+  st.l += ls;
+  const int parts = two_term ? 2 : 1;
+  for (int part = 0; part < parts; ++part) {
+    const bf16x8 bp = part ? qa : pa;
+    bf16x8 vf[PF];
+#pragma unroll
+    for (int u = 0; u < PF; ++u) vf[u] = lds_v_frag16(vbuf + voff + u * 32);
+#pragma unroll
+    for (int ct = 0; ct < CTILES16; ++ct) {
+      st.o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[ct % PF], bp, st.o[ct], 0, 0, 0);
+      if (ct + PF < CTILES16) vf[ct % PF] = lds_v_frag16(vbuf + voff + (ct + PF) * 32);
+    }
+  }
+  return MODE == kLazy && __any(over);
+}
+
+__device__ __forceinline__ void zero_acc16(Acc16& st) {
+#pragma unroll
+  for (int ct = 0; ct < CTILES16; ++ct) st.o[ct] = f32x4{};
+  st.m = -INFINITY;
+  st.l = 0.f;
+}
+
+template <int MODE>
+__device__ __forceinline__ bool tile_pass16(const KeySource& ks, int t_begin, int t_end,
+                                            const bf16x8 (&qf)[DSTEPS16], Acc16& st, float sc2,
+                                            const RowMask& rm, int wave, int lane, char HCA_LDS* kv,
+                                            int* flag, bool two_term) {
+  constexpr int KV_BYTES = NT * KSTR + NT * VSTR;
+  const int g = lane >> 4;
+  const int koff = (lane & 15) * KSTR + g * 16;
+  const int voff = NT * KSTR + (4 * g + ((lane & 15) >> 2)) * VSTR + 4 * (lane & 3) * 2;
+  if (MODE == kLazy && threadIdx.x == 0) flag[0] = flag[1] = 0;
+  issue_tile<4>(ks, t_begin, kv, kv + NT * KSTR, wave, lane);
+  wait_vm_all();
+  __syncthreads();
+  for (int tile = t_begin; tile < t_end; ++tile) {
+    char HCA_LDS* cur = kv + ((tile - t_begin) & 1) * KV_BYTES;
+    char HCA_LDS* nxt = kv + (((tile - t_begin) & 1) ^ 1) * KV_BYTES;
+    if (tile + 1 < t_end) issue_tile<4>(ks, tile + 1, nxt, nxt + NT * KSTR, wave, lane);
+    const bool over = compute_tile16<MODE>(cur, cur, qf, st, sc2, lane, koff, voff, rm, tile,
+                                           tile_needs_mask(tile, rm.nc, rm.nkeys), two_term);
+    if (MODE == kLazy && over && lane == 0) flag[(tile - t_begin) & 1] = 1;
+    wait_vm_all();
+    __syncthreads();
+    if (MODE == kLazy && flag[(tile - t_begin) & 1]) return true;
+  }
+  return false;
+}
+
+__device__ __forceinline__ void attend_tiles16(const KeySource& ks, int t_begin, int t_end,
+                                               const bf16x8 (&qf)[DSTEPS16], Acc16& st, float sc2,
+                                               const RowMask& rm, int wave, int lane,
+                                               char HCA_LDS* kv, int* flag) {
+  const bool two_term = rm.nkeys <= kTwoTermKeys;
+  zero_acc16(st);
+  if (!tile_pass16<kLazy>(ks, t_begin, t_end, qf, st, sc2, rm, wave, lane, kv, flag, two_term))
+    return;
+  __syncthreads();
+  zero_acc16(st);
+  tile_pass16<kMaxOnly>(ks, t_begin, t_end, qf, st, sc2, rm, wave, lane, kv, flag, two_term);
+  tile_pass16<kFixed>(ks, t_begin, t_end, qf, st, sc2, rm, wave, lane, kv, flag, two_term);
+}
+
+// ---------------------------------------------------------------------------
+// Decode: grid (max_splits, batch, Hkv), 256 threads (4 wavefronts x 16 heads).
 // Workspace: int32 tickets [B*Hkv] (256-byte padded), then fp32 m and l
-// [B*Hkv][splits][64], then fp32 O [B*Hkv][splits][64][512].
+// [B*Hkv][splits][64], then fp32 O [B*Hkv][splits][64][512] normalised by
+// its own l (a convex combination of value rows).
 // ---------------------------------------------------------------------------
 struct WsLayout {
   int* tickets;
@@ -402,7 +553,7 @@ __host__ __device__ inline WsLayout ws_layout(void* ws, int batch, int hkv, int 
   return w;
 }
 
-__global__ __launch_bounds__(128, 1) void decode_bf16_kernel(DecodeArgs a, int tps, int max_splits) {
+__global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a, int tps, int max_splits) {
   __shared__ __attribute__((aligned(16))) char kv_s[2 * (NT * KSTR + NT * VSTR)];
   __shared__ int ticket_s;
   __shared__ int flag_s[2];
@@ -419,7 +570,7 @@ __global__ __launch_bounds__(128, 1) void decode_bf16_kernel(DecodeArgs a, int t
   if (split >= nsplit) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int row = wave * 32 + (lane & 31);    // head within the KV group
+  const int row = wave * 16 + (lane & 15);    // head within the KV group
   const int head = kvh * G + row;
 
   KeySource ks;
@@ -431,7 +582,7 @@ __global__ __launch_bounds__(128, 1) void decode_bf16_kernel(DecodeArgs a, int t
   ks.raw_v = (const char*)a.vw + (size_t)b * a.ring * ks.rstride + head_off;
   ks.nc = nc;
   ks.nkeys = nkeys;
-  ks.lo = lo;
+  ks.raw0 = lo % a.ring;
   ks.ring = a.ring;
 
   RowMask rm;
@@ -442,34 +593,31 @@ __global__ __launch_bounds__(128, 1) void decode_bf16_kernel(DecodeArgs a, int t
   rm.smin = lo;
   rm.smax = t;
 
-  bf16x8 qf[DSTEPS];
-  load_q((const bf16*)a.q + ((size_t)b * a.hq + head) * D, lane, qf);
-  Acc st;
+  // Q^T fragments: lane l holds head row l%16, elements 32k + 8(l/16) .. +7
+  bf16x8 qf[DSTEPS16];
+  const bf16* qrow = (const bf16*)a.q + ((size_t)b * a.hq + head) * D + 8 * (lane >> 4);
+#pragma unroll
+  for (int k = 0; k < DSTEPS16; ++k) qf[k] = *(const bf16x8*)(qrow + 32 * k);
+  Acc16 st;
   const float sc2 = a.scale * kLog2e;
   const int t_begin = split * tps;
   const int t_end = min(ntiles, t_begin + tps);
-  attend_tiles<2>(ks, t_begin, t_end, qf, st, sc2, rm, wave, lane, (char HCA_LDS*)kv_s, flag_s);
+  attend_tiles16(ks, t_begin, t_end, qf, st, sc2, rm, wave, lane, (char HCA_LDS*)kv_s, flag_s);
 
-  // partial results of this split
+  // this split's partial result: m, l and O / l
   const WsLayout w = ws_layout(a.ws, a.batch, a.hkv, max_splits);
   const size_t unit = (size_t)b * a.hkv + kvh;
   const size_t prow = (unit * max_splits + split) * G + row;
-  const float l_tot = st.l + __shfl_xor(st.l, 32);
-  if (lane < 32) {
+  float l_tot = st.l + __shfl_xor(st.l, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (lane < 16) {
     w.m[prow] = st.m;
     w.l[prow] = l_tot;
   }
-  float* po = w.o + prow * D + 4 * (lane >> 5);
+  const float inv = 1.f / l_tot;
+  float* po = w.o + prow * D + 4 * (lane >> 4);
 #pragma unroll
-  for (int ct = 0; ct < CTILES; ++ct) {
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      f32x4 v;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = st.o[ct][4 * q4 + i];
-      *(f32x4*)(po + 32 * ct + 8 * q4) = v;
-    }
-  }
+  for (int ct = 0; ct < CTILES16; ++ct) *(f32x4*)(po + 16 * ct) = st.o[ct] * inv;
   // publish, then take a ticket; the last split of this unit merges
   __threadfence();
   __syncthreads();
@@ -478,26 +626,25 @@ __global__ __launch_bounds__(128, 1) void decode_bf16_kernel(DecodeArgs a, int t
   if (ticket_s != nsplit - 1) return;
   __threadfence();
 
-  // merge: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, splits in order
+  // merge: O = sum_s 2^(m_s - M) l_s O_s / sum_s 2^(m_s - M) l_s, splits in order
   const float* mrow = w.m + unit * max_splits * G;
   const float* lrow = w.l + unit * max_splits * G;
   const float* obase = w.o + unit * max_splits * G * D;
-  const int c = threadIdx.x * 4;  // 128 threads x 4 columns
-  for (int r = 0; r < G; ++r) {
+  const int c = (threadIdx.x & 127) * 4;  // 128 threads cover 512 columns
+  for (int r = threadIdx.x >> 7; r < G; r += 2) {
     float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, mrow[s * G + r]);
+    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, mrow[sp * G + r]);
     float den = 0.f;
     f32x4 num = {};
-    for (int s = 0; s < nsplit; ++s) {
-      const float wgt = __builtin_amdgcn_exp2f(mrow[s * G + r] - M);
-      den += wgt * lrow[s * G + r];
-      const f32x4 os = *(const f32x4*)(obase + ((size_t)s * G + r) * D + c);
-      num += wgt * os;
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float wgt = __builtin_amdgcn_exp2f(mrow[sp * G + r] - M) * lrow[sp * G + r];
+      den += wgt;
+      num += wgt * *(const f32x4*)(obase + ((size_t)sp * G + r) * D + c);
     }
-    const float inv = 1.f / den;
+    const float rden = 1.f / den;
     bf16x4 v;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = (bf16)(num[i] * inv);
+    for (int i = 0; i < 4; ++i) v[i] = (bf16)(num[i] * rden);
     *(bf16x4*)((bf16*)a.o + ((size_t)b * a.hq + kvh * G + r) * D + c) = v;
   }
   if (threadIdx.x == 0) w.tickets[unit] = 0;  // ready for the next call
@@ -533,7 +680,7 @@ size_t decode_workspace_bytes_bf16(int batch, int hkv, int max_blocks, int windo
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
   const DecodePlan p = decode_plan(a.batch, a.hkv, a.max_blocks, a.window);
   dim3 grid(p.max_splits, a.batch, a.hkv);
-  decode_bf16_kernel<<<grid, 128, 0, s>>>(a, p.tiles_per_split, p.max_splits);
+  decode_bf16_kernel<<<grid, 256, 0, s>>>(a, p.tiles_per_split, p.max_splits);
   return hipGetLastError();
 }
 

@@ -92,34 +92,43 @@ struct RowMask {
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Issue the direct global->LDS loads of key tile `tile`: NW wavefronts share
-// the 32 K rows and 32 V rows; one instruction moves one 1 KiB row.
+// the 32 K rows and 32 V rows; one instruction moves one 1 KiB row.  The row
+// of slot kappa is base + kappa * rstride, where base is chosen among three
+// precomputed pointers (compressed entries, raw rows, raw rows one ring length
+// back), so no branch and no per-row modulo is needed.
 template <int NW>
 __device__ __forceinline__ void issue_tile(const KeySource& ks, int tile, char HCA_LDS* kbuf,
                                            char HCA_LDS* vbuf, int wave, int lane) {
   constexpr int RPW = NT / NW;
+  const ptrdiff_t rs = (ptrdiff_t)ks.rstride;
+  const ptrdiff_t raw_shift = (ptrdiff_t)(ks.raw0 - ks.nc) * rs;  // raw slot kappa -> row raw0 + kappa - nc
+  const ptrdiff_t wrap_shift = raw_shift - (ptrdiff_t)ks.ring * rs;
+  const int wrap_from = ks.ring ? ks.nc - ks.raw0 + ks.ring : 0x7fffffff;  // first slot past the ring end
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
     const int kk = wave * RPW + r;
     // slots past the end re-read the last key (finite data; masked later)
     const int kappa = min(tile * NT + kk, ks.nkeys - 1);
-    const char* ksrc;
-    const char* vsrc;
-    if (kappa < ks.nc) {
-      ksrc = ks.comp_k + (size_t)kappa * ks.rstride;
-      vsrc = ks.comp_v + (size_t)kappa * ks.rstride;
-    } else {
-      // raw position lo + r; in a ring it sits in slot (lo % R + r) mod R and
-      // r < R, so one wrap-around subtraction replaces the modulo
-      int pos = ks.raw0 + (kappa - ks.nc);
-      if (ks.ring && pos >= ks.ring) pos -= ks.ring;
-      ksrc = ks.raw_k + (size_t)pos * ks.rstride;
-      vsrc = ks.raw_v + (size_t)pos * ks.rstride;
-    }
-    __builtin_amdgcn_global_load_lds((const void HCA_GLOBAL*)(ksrc + lane * 16),
-                                     (void HCA_LDS*)(kbuf + kk * KSTR), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void HCA_GLOBAL*)(vsrc + lane * 16),
-                                     (void HCA_LDS*)(vbuf + kk * VSTR), 16, 0, 0);
+    const bool comp = kappa < ks.nc;
+    const ptrdiff_t shift = comp ? 0 : (kappa >= wrap_from ? wrap_shift : raw_shift);
+    const ptrdiff_t off = (ptrdiff_t)kappa * rs + shift + lane * 16;
+    const char* ksrc = (comp ? ks.comp_k : ks.raw_k) + off;
+    const char* vsrc = (comp ? ks.comp_v : ks.raw_v) + off;
+    __builtin_amdgcn_global_load_lds((const void HCA_GLOBAL*)ksrc, (void HCA_LDS*)(kbuf + kk * KSTR),
+                                     16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void HCA_GLOBAL*)vsrc, (void HCA_LDS*)(vbuf + kk * VSTR),
+                                     16, 0, 0);
   }
+}
+
+// Copy `rows` rows of 1 KiB (consecutive in global memory) into LDS rows of
+// KSTR bytes with direct loads, one row per wave instruction, and wait for
+// them.  Used to bring a wavefront's query rows in with whole-row requests.
+__device__ __forceinline__ void stage_rows(const char* src, char HCA_LDS* dst, int rows, int lane) {
+  for (int r = 0; r < rows; ++r)
+    __builtin_amdgcn_global_load_lds((const void HCA_GLOBAL*)(src + (size_t)r * D * sizeof(bf16) + lane * 16),
+                                     (void HCA_LDS*)(dst + r * KSTR), 16, 0, 0);
+  wait_vm_all();
 }
 
 // Softmax state of the 32 rows a wavefront owns (one row per lane pair
@@ -163,16 +172,31 @@ __device__ __forceinline__ bool compute_tile(const char HCA_LDS* kbuf, const cha
                                              const bf16x8 (&qf)[DSTEPS], Acc& st, float sc2,
                                              int lane, int koff, int voff, const RowMask& rm,
                                              int tile, bool masked, bool two_term) {
-  constexpr int PF = 2;  // fragments read ahead of their MFMA
-  f32x16 s = {};
-  bf16x8 kf[PF];
+  // S^T = K . Q^T: 32 k-steps split over two independent accumulator chains
+  // (a single dependent chain runs the matrix core at ~60% with one wave per
+  // SIMD).  The chains are issued as inline MFMAs with VGPR accumulators so
+  // that the 256 AGPRs stay with O; K fragments are read KPF steps ahead.
+  constexpr int KPF = 4;
+  bf16x8 kf[KPF];
 #pragma unroll
-  for (int k = 0; k < PF; ++k) kf[k] = lds_k_frag(kbuf + koff + k * 32);
+  for (int k = 0; k < KPF; ++k) kf[k] = lds_k_frag(kbuf + koff + k * 32);
+  f32x16 s0, s1;
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s0) : "v"(kf[0]), "v"(qf[0]));
+  kf[0] = lds_k_frag(kbuf + koff + KPF * 32);
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s1) : "v"(kf[1]), "v"(qf[1]));
+  kf[1] = lds_k_frag(kbuf + koff + (KPF + 1) * 32);
 #pragma unroll
-  for (int k = 0; k < DSTEPS; ++k) {
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[k % PF], qf[k], s, 0, 0, 0);
-    if (k + PF < DSTEPS) kf[k % PF] = lds_k_frag(kbuf + koff + (k + PF) * 32);
+  for (int k = 2; k < DSTEPS; ++k) {
+    if (k & 1)
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s1) : "v"(kf[k % KPF]), "v"(qf[k]));
+    else
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s0) : "v"(kf[k % KPF]), "v"(qf[k]));
+    if (k + KPF < DSTEPS) kf[k % KPF] = lds_k_frag(kbuf + koff + (k + KPF) * 32);
   }
+  // a VALU read of an MFMA result needs up to 18 wait states; the compiler
+  // does not see inside the inline MFMAs, so they are spent here (24)
+  asm volatile("s_nop 15\n\ts_nop 7" : "+v"(s0), "+v"(s1));
+  f32x16 s = s0 + s1;
   // scale into log2 units (in place), mask, row max over the lane pair
 #pragma unroll
   for (int i = 0; i < 16; ++i) s[i] *= sc2;
@@ -220,15 +244,18 @@ __device__ __forceinline__ bool compute_tile(const char HCA_LDS* kbuf, const cha
   for (int part = 0; part < parts; ++part) {
     const bf16x8 ba = part ? qa : pa;
     const bf16x8 bb = part ? qb : pb;
-    bf16x8 vf[PF];
+    // step u: column tile u % 16 and key step u / 16, so consecutive MFMAs
+    // accumulate into different tiles; V fragments read VPF steps ahead
+    constexpr int VPF = 4;
+    bf16x8 vf[VPF];
 #pragma unroll
-    for (int u = 0; u < PF; ++u) vf[u] = lds_v_frag(vbuf + voff + (u & 1) * 16 * VSTR + (u >> 1) * 64);
+    for (int u = 0; u < VPF; ++u) vf[u] = lds_v_frag(vbuf + voff + (u >> 4) * 16 * VSTR + (u & 15) * 64);
 #pragma unroll
     for (int u = 0; u < 2 * CTILES; ++u) {
-      const int ct = u >> 1, k2 = u & 1;
-      st.o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[u % PF], k2 ? bb : ba, st.o[ct], 0, 0, 0);
-      const int un = u + PF;
-      if (un < 2 * CTILES) vf[u % PF] = lds_v_frag(vbuf + voff + (un & 1) * 16 * VSTR + (un >> 1) * 64);
+      const int ct = u & 15, k2 = u >> 4;
+      st.o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[u % VPF], k2 ? bb : ba, st.o[ct], 0, 0, 0);
+      const int un = u + VPF;
+      if (un < 2 * CTILES) vf[u % VPF] = lds_v_frag(vbuf + voff + (un >> 4) * 16 * VSTR + (un & 15) * 64);
     }
   }
   return MODE == kLazy && __any(over);
@@ -251,29 +278,42 @@ __device__ __forceinline__ void zero_acc(Acc& st) {
 
 // One pass over tiles [t_begin, t_end) in schedule MODE.  Returns true (for
 // every wave) if a kLazy pass stopped because the headroom was exceeded.
+// The two LDS buffers are distinct arrays and the loop is unrolled by two,
+// so which buffer a read touches is known at compile time: the compiler then
+// does not make LDS reads of one buffer wait for the direct loads still in
+// flight into the other.  The headroom test crosses waves through flag[0]
+// (tiles in buffer 0) and flag[1] (buffer 1): a tile sets its slot before the
+// barrier that ends it and every wave reads the slot right after that
+// barrier; the other slot can only be set before the next barrier, so no wave
+// sees a flag raised for a later tile.
 template <int NW, int MODE>
 __device__ __forceinline__ bool tile_pass(const KeySource& ks, int t_begin, int t_end,
                                           const bf16x8 (&qf)[DSTEPS], Acc& st, float sc2,
-                                          const RowMask& rm, int wave, int lane, char HCA_LDS* kv,
-                                          int* flag, bool two_term) {
-  constexpr int KV_BYTES = NT * KSTR + NT * VSTR;
+                                          const RowMask& rm, int wave, int lane, char HCA_LDS* kv0,
+                                          char HCA_LDS* kv1, int* flag, bool two_term) {
   const int koff = (lane & 31) * KSTR + (lane >> 5) * 16;
   const int voff = NT * KSTR + (4 * (lane >> 5) + ((lane & 15) >> 2)) * VSTR +
                    (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
   if (MODE == kLazy && threadIdx.x == 0) flag[0] = flag[1] = 0;
-  issue_tile<NW>(ks, t_begin, kv, kv + NT * KSTR, wave, lane);
+  issue_tile<NW>(ks, t_begin, kv0, kv0 + NT * KSTR, wave, lane);
   wait_vm_all();
   __syncthreads();
-  for (int tile = t_begin; tile < t_end; ++tile) {
-    char HCA_LDS* cur = kv + ((tile - t_begin) & 1) * KV_BYTES;
-    char HCA_LDS* nxt = kv + (((tile - t_begin) & 1) ^ 1) * KV_BYTES;
-    if (tile + 1 < t_end) issue_tile<NW>(ks, tile + 1, nxt, nxt + NT * KSTR, wave, lane);
-    const bool over = compute_tile<MODE>(cur, cur, qf, st, sc2, lane, koff, voff, rm, tile,
-                                         tile_needs_mask(tile, rm.nc, rm.nkeys), two_term);
-    if (MODE == kLazy && over && lane == 0) flag[(tile - t_begin) & 1] = 1;
+  for (int tile = t_begin; tile < t_end; tile += 2) {
+    if (tile + 1 < t_end) issue_tile<NW>(ks, tile + 1, kv1, kv1 + NT * KSTR, wave, lane);
+    bool over = compute_tile<MODE>(kv0, kv0, qf, st, sc2, lane, koff, voff, rm, tile,
+                                   tile_needs_mask(tile, rm.nc, rm.nkeys), two_term);
+    if (MODE == kLazy && over && lane == 0) flag[0] = 1;
     wait_vm_all();
     __syncthreads();
-    if (MODE == kLazy && flag[(tile - t_begin) & 1]) return true;
+    if (MODE == kLazy && flag[0]) return true;
+    if (tile + 1 >= t_end) break;
+    if (tile + 2 < t_end) issue_tile<NW>(ks, tile + 2, kv0, kv0 + NT * KSTR, wave, lane);
+    over = compute_tile<MODE>(kv1, kv1, qf, st, sc2, lane, koff, voff, rm, tile + 1,
+                              tile_needs_mask(tile + 1, rm.nc, rm.nkeys), two_term);
+    if (MODE == kLazy && over && lane == 0) flag[1] = 1;
+    wait_vm_all();
+    __syncthreads();
+    if (MODE == kLazy && flag[1]) return true;
   }
   return false;
 }
@@ -284,30 +324,24 @@ template <int NW>
 __device__ __forceinline__ void attend_tiles(const KeySource& ks, int t_begin, int t_end,
                                              const bf16x8 (&qf)[DSTEPS], Acc& st, float sc2,
                                              const RowMask& rm, int wave, int lane,
-                                             char HCA_LDS* kv, int* flag) {
+                                             char HCA_LDS* kv0, char HCA_LDS* kv1, int* flag) {
   const bool two_term = rm.nkeys <= kTwoTermKeys;
   zero_acc(st);
-  if (!tile_pass<NW, kLazy>(ks, t_begin, t_end, qf, st, sc2, rm, wave, lane, kv, flag, two_term))
+  if (!tile_pass<NW, kLazy>(ks, t_begin, t_end, qf, st, sc2, rm, wave, lane, kv0, kv1, flag,
+                            two_term))
     return;
   __syncthreads();
   zero_acc(st);
-  tile_pass<NW, kMaxOnly>(ks, t_begin, t_end, qf, st, sc2, rm, wave, lane, kv, flag, two_term);
-  tile_pass<NW, kFixed>(ks, t_begin, t_end, qf, st, sc2, rm, wave, lane, kv, flag, two_term);
-}
-
-// Q^T fragments of one wavefront: lane l holds row (l%32), head-dim
-// elements 16k + 8(l/32) .. +7 for k-step k.
-__device__ __forceinline__ void load_q(const bf16* qrow, int lane, bf16x8 (&qf)[DSTEPS]) {
-  const bf16* p = qrow + 8 * (lane >> 5);
-#pragma unroll
-  for (int k = 0; k < DSTEPS; ++k) qf[k] = *(const bf16x8*)(p + 16 * k);
+  tile_pass<NW, kMaxOnly>(ks, t_begin, t_end, qf, st, sc2, rm, wave, lane, kv0, kv1, flag, two_term);
+  tile_pass<NW, kFixed>(ks, t_begin, t_end, qf, st, sc2, rm, wave, lane, kv0, kv1, flag, two_term);
 }
 
 // ---------------------------------------------------------------------------
 // Prefill: grid (ceil(max_seqlen/2), batch, Hkv), 256 threads.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256, 1) void prefill_bf16_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) char kv_s[2 * (NT * KSTR + NT * VSTR)];
+  __shared__ __attribute__((aligned(16))) char kv0_s[NT * KSTR + NT * VSTR];
+  __shared__ __attribute__((aligned(16))) char kv1_s[NT * KSTR + NT * VSTR];
   __shared__ int flag_s[2];
 
   const int b = blockIdx.y, kvh = blockIdx.z;
@@ -350,17 +384,29 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_kernel(PrefillArgs a) {
   rm.smin = t - a.window + 1;
   rm.smax = t;
 
+  // The wave's 32 query rows (heads head0 .. head0+31 of position t) are
+  // contiguous: stage them through LDS with whole-row loads, then read the
+  // Q^T fragments (lane l: row l%32, elements 16k + 8(l/32) .. +7).  The key
+  // buffers are idle before the first tile and after the last one.
+  char HCA_LDS* stage = (char HCA_LDS*)((wave >> 1) ? kv1_s : kv0_s) + (wave & 1) * 32 * KSTR;
+  const int head0 = kvh * G + (wave & 1) * 32;
+  const size_t qrow0 = ((size_t)(start + t) * a.hq + head0) * D;
   bf16x8 qf[DSTEPS];
-  const size_t qoff = ((size_t)(start + t) * a.hq + head) * D;
-  load_q((const bf16*)a.q + qoff, lane, qf);
+  stage_rows((const char*)((const bf16*)a.q + qrow0), stage, 32, lane);
+  const int qoff = (lane & 31) * KSTR + (lane >> 5) * 16;
+#pragma unroll
+  for (int k = 0; k < DSTEPS; ++k) qf[k] = *(const bf16x8 HCA_LDS*)(stage + qoff + k * 32);
+  __syncthreads();  // every wave holds its fragments before tile 0 lands
   Acc st;
   const float sc2 = a.scale * kLog2e;
-  attend_tiles<4>(ks, 0, (nkeys + NT - 1) / NT, qf, st, sc2, rm, wave, lane, (char HCA_LDS*)kv_s,
-                  flag_s);
+  attend_tiles<4>(ks, 0, (nkeys + NT - 1) / NT, qf, st, sc2, rm, wave, lane, (char HCA_LDS*)kv0_s,
+                  (char HCA_LDS*)kv1_s, flag_s);
 
+  // O = acc / l, rounded to bf16, written to LDS in the accumulator layout
+  // (lane l: row l%32, cols 32ct + 8q + 4(l/32) .. +3) and stored row by row
   const float inv = 1.f / (st.l + __shfl_xor(st.l, 32));
   if (!row_ok) return;
-  bf16* orow = (bf16*)a.o + qoff + 4 * (lane >> 5);
+  const int ooff = (lane & 31) * KSTR + (lane >> 5) * 8;
 #pragma unroll
   for (int ct = 0; ct < CTILES; ++ct) {
 #pragma unroll
@@ -368,9 +414,13 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_kernel(PrefillArgs a) {
       bf16x4 v;
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = (bf16)(st.o[ct][4 * q4 + i] * inv);
-      *(bf16x4*)(orow + 32 * ct + 8 * q4) = v;
+      *(bf16x4 HCA_LDS*)(stage + ooff + (32 * ct + 8 * q4) * 2) = v;
     }
   }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's LDS writes are done
+  bf16* orow = (bf16*)a.o + qrow0;
+  for (int r = 0; r < 32; ++r)
+    *(bf16x8*)(orow + (size_t)r * D + lane * 8) = *(const bf16x8 HCA_LDS*)(stage + r * KSTR + lane * 16);
 }
 
 // ---------------------------------------------------------------------------
@@ -486,26 +536,32 @@ __device__ __forceinline__ void zero_acc16(Acc16& st) {
 template <int MODE>
 __device__ __forceinline__ bool tile_pass16(const KeySource& ks, int t_begin, int t_end,
                                             const bf16x8 (&qf)[DSTEPS16], Acc16& st, float sc2,
-                                            const RowMask& rm, int wave, int lane, char HCA_LDS* kv,
-                                            int* flag, bool two_term) {
-  constexpr int KV_BYTES = NT * KSTR + NT * VSTR;
+                                            const RowMask& rm, int wave, int lane,
+                                            char HCA_LDS* kv0, char HCA_LDS* kv1, int* flag,
+                                            bool two_term) {
   const int g = lane >> 4;
   const int koff = (lane & 15) * KSTR + g * 16;
   const int voff = NT * KSTR + (4 * g + ((lane & 15) >> 2)) * VSTR + 4 * (lane & 3) * 2;
   if (MODE == kLazy && threadIdx.x == 0) flag[0] = flag[1] = 0;
-  issue_tile<4>(ks, t_begin, kv, kv + NT * KSTR, wave, lane);
+  issue_tile<4>(ks, t_begin, kv0, kv0 + NT * KSTR, wave, lane);
   wait_vm_all();
   __syncthreads();
-  for (int tile = t_begin; tile < t_end; ++tile) {
-    char HCA_LDS* cur = kv + ((tile - t_begin) & 1) * KV_BYTES;
-    char HCA_LDS* nxt = kv + (((tile - t_begin) & 1) ^ 1) * KV_BYTES;
-    if (tile + 1 < t_end) issue_tile<4>(ks, tile + 1, nxt, nxt + NT * KSTR, wave, lane);
-    const bool over = compute_tile16<MODE>(cur, cur, qf, st, sc2, lane, koff, voff, rm, tile,
-                                           tile_needs_mask(tile, rm.nc, rm.nkeys), two_term);
-    if (MODE == kLazy && over && lane == 0) flag[(tile - t_begin) & 1] = 1;
+  for (int tile = t_begin; tile < t_end; tile += 2) {  // two buffers, unrolled (see tile_pass)
+    if (tile + 1 < t_end) issue_tile<4>(ks, tile + 1, kv1, kv1 + NT * KSTR, wave, lane);
+    bool over = compute_tile16<MODE>(kv0, kv0, qf, st, sc2, lane, koff, voff, rm, tile,
+                                     tile_needs_mask(tile, rm.nc, rm.nkeys), two_term);
+    if (MODE == kLazy && over && lane == 0) flag[0] = 1;
     wait_vm_all();
     __syncthreads();
-    if (MODE == kLazy && flag[(tile - t_begin) & 1]) return true;
+    if (MODE == kLazy && flag[0]) return true;
+    if (tile + 1 >= t_end) break;
+    if (tile + 2 < t_end) issue_tile<4>(ks, tile + 2, kv0, kv0 + NT * KSTR, wave, lane);
+    over = compute_tile16<MODE>(kv1, kv1, qf, st, sc2, lane, koff, voff, rm, tile + 1,
+                                tile_needs_mask(tile + 1, rm.nc, rm.nkeys), two_term);
+    if (MODE == kLazy && over && lane == 0) flag[1] = 1;
+    wait_vm_all();
+    __syncthreads();
+    if (MODE == kLazy && flag[1]) return true;
   }
   return false;
 }
@@ -513,15 +569,16 @@ __device__ __forceinline__ bool tile_pass16(const KeySource& ks, int t_begin, in
 __device__ __forceinline__ void attend_tiles16(const KeySource& ks, int t_begin, int t_end,
                                                const bf16x8 (&qf)[DSTEPS16], Acc16& st, float sc2,
                                                const RowMask& rm, int wave, int lane,
-                                               char HCA_LDS* kv, int* flag) {
+                                               char HCA_LDS* kv0, char HCA_LDS* kv1, int* flag) {
   const bool two_term = rm.nkeys <= kTwoTermKeys;
   zero_acc16(st);
-  if (!tile_pass16<kLazy>(ks, t_begin, t_end, qf, st, sc2, rm, wave, lane, kv, flag, two_term))
+  if (!tile_pass16<kLazy>(ks, t_begin, t_end, qf, st, sc2, rm, wave, lane, kv0, kv1, flag,
+                          two_term))
     return;
   __syncthreads();
   zero_acc16(st);
-  tile_pass16<kMaxOnly>(ks, t_begin, t_end, qf, st, sc2, rm, wave, lane, kv, flag, two_term);
-  tile_pass16<kFixed>(ks, t_begin, t_end, qf, st, sc2, rm, wave, lane, kv, flag, two_term);
+  tile_pass16<kMaxOnly>(ks, t_begin, t_end, qf, st, sc2, rm, wave, lane, kv0, kv1, flag, two_term);
+  tile_pass16<kFixed>(ks, t_begin, t_end, qf, st, sc2, rm, wave, lane, kv0, kv1, flag, two_term);
 }
 
 // ---------------------------------------------------------------------------
@@ -554,7 +611,8 @@ __host__ __device__ inline WsLayout ws_layout(void* ws, int batch, int hkv, int 
 }
 
 __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a, int tps, int max_splits) {
-  __shared__ __attribute__((aligned(16))) char kv_s[2 * (NT * KSTR + NT * VSTR)];
+  __shared__ __attribute__((aligned(16))) char kv0_s[NT * KSTR + NT * VSTR];
+  __shared__ __attribute__((aligned(16))) char kv1_s[NT * KSTR + NT * VSTR];
   __shared__ int ticket_s;
   __shared__ int flag_s[2];
 
@@ -602,7 +660,8 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a, int t
   const float sc2 = a.scale * kLog2e;
   const int t_begin = split * tps;
   const int t_end = min(ntiles, t_begin + tps);
-  attend_tiles16(ks, t_begin, t_end, qf, st, sc2, rm, wave, lane, (char HCA_LDS*)kv_s, flag_s);
+  attend_tiles16(ks, t_begin, t_end, qf, st, sc2, rm, wave, lane, (char HCA_LDS*)kv0_s,
+                 (char HCA_LDS*)kv1_s, flag_s);
 
   // this split's partial result: m, l and O / l
   const WsLayout w = ws_layout(a.ws, a.batch, a.hkv, max_splits);

@@ -36,9 +36,9 @@
 //    by the matrix cores; softmax(x) = exp(x - c)/sum exp(x - c) holds for any
 //    c, so the result is the same up to rounding.
 //  * Decode: one workgroup of 4 wavefronts x 16 heads (v_mfma 16x16x32) per
-//    (sequence, KV head, key split); fp32 partials (m, l, O/l) go to the
-//    workspace and the last split to finish (atomic ticket) merges them in
-//    split order, so the result is deterministic.
+//    (sequence, KV head, key split) writes fp32 partials (m, l, O/l) to the
+//    workspace; a second, fully parallel kernel merges them in split order,
+//    so the result is deterministic.
 #include <algorithm>
 
 #include "hca_internal.h"
@@ -582,13 +582,12 @@ __device__ __forceinline__ void attend_tiles16(const KeySource& ks, int t_begin,
 }
 
 // ---------------------------------------------------------------------------
-// Decode: grid (max_splits, batch, Hkv), 256 threads (4 wavefronts x 16 heads).
-// Workspace: int32 tickets [B*Hkv] (256-byte padded), then fp32 m and l
-// [B*Hkv][splits][64], then fp32 O [B*Hkv][splits][64][512] normalised by
-// its own l (a convex combination of value rows).
+// Decode: split kernel grid (max_splits, batch, Hkv), 256 threads (4
+// wavefronts x 16 heads), then the merge kernel.
+// Workspace: fp32 m and l [B*Hkv][splits][64], then fp32 O [B*Hkv][splits]
+// [64][512] normalised by its own l (a convex combination of value rows).
 // ---------------------------------------------------------------------------
 struct WsLayout {
-  int* tickets;
   float* m;
   float* l;
   float* o;
@@ -600,8 +599,6 @@ __host__ __device__ inline WsLayout ws_layout(void* ws, int batch, int hkv, int 
   WsLayout w;
   char* p = (char*)ws;
   const size_t units = (size_t)batch * hkv;
-  w.tickets = (int*)p;
-  p += round_up(units * sizeof(int), 256);
   w.m = (float*)p;
   p += round_up(units * splits * G * sizeof(float), 256);
   w.l = (float*)p;
@@ -613,7 +610,6 @@ __host__ __device__ inline WsLayout ws_layout(void* ws, int batch, int hkv, int 
 __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a, int tps, int max_splits) {
   __shared__ __attribute__((aligned(16))) char kv0_s[NT * KSTR + NT * VSTR];
   __shared__ __attribute__((aligned(16))) char kv1_s[NT * KSTR + NT * VSTR];
-  __shared__ int ticket_s;
   __shared__ int flag_s[2];
 
   const int split = blockIdx.x, b = blockIdx.y, kvh = blockIdx.z;
@@ -677,36 +673,46 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a, int t
   float* po = w.o + prow * D + 4 * (lane >> 4);
 #pragma unroll
   for (int ct = 0; ct < CTILES16; ++ct) *(f32x4*)(po + 16 * ct) = st.o[ct] * inv;
-  // publish, then take a ticket; the last split of this unit merges
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) ticket_s = atomicAdd(&w.tickets[unit], 1);
-  __syncthreads();
-  if (ticket_s != nsplit - 1) return;
-  __threadfence();
+}
 
-  // merge: O = sum_s 2^(m_s - M) l_s O_s / sum_s 2^(m_s - M) l_s, splits in order
-  const float* mrow = w.m + unit * max_splits * G;
-  const float* lrow = w.l + unit * max_splits * G;
-  const float* obase = w.o + unit * max_splits * G * D;
-  const int c = (threadIdx.x & 127) * 4;  // 128 threads cover 512 columns
-  for (int r = threadIdx.x >> 7; r < G; r += 2) {
-    float M = -INFINITY;
-    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, mrow[sp * G + r]);
-    float den = 0.f;
-    f32x4 num = {};
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float wgt = __builtin_amdgcn_exp2f(mrow[sp * G + r] - M) * lrow[sp * G + r];
-      den += wgt;
-      num += wgt * *(const f32x4*)(obase + ((size_t)sp * G + r) * D + c);
-    }
-    const float rden = 1.f / den;
-    bf16x4 v;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = (bf16)(num[i] * rden);
-    *(bf16x4*)((bf16*)a.o + ((size_t)b * a.hq + kvh * G + r) * D + c) = v;
+// Merge of the split partials: O = sum_s 2^(m_s - M) l_s O_s / sum_s 2^(m_s - M) l_s
+// with M = max_s m_s, splits taken in order (deterministic).  One workgroup
+// of 256 threads merges kMergeRows heads of one (sequence, KV head); each
+// thread owns 8 columns of one head and issues its split loads independently.
+constexpr int kMergeRows = 4;
+
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int tps, int max_splits) {
+  const int unit = blockIdx.y;  // b * Hkv + kvh
+  const int b = unit / a.hkv, kvh = unit % a.hkv;
+  const int r = blockIdx.x * kMergeRows + (threadIdx.x >> 6);  // head within the KV group
+  const int c = (threadIdx.x & 63) * 8;
+  const int L = a.seqlens[b];
+  const int nkeys = L / kBlock + min(a.window, L);
+  const int nsplit = ((nkeys + NT - 1) / NT + tps - 1) / tps;
+  const WsLayout w = ws_layout(a.ws, a.batch, a.hkv, max_splits);
+  const float* mrow = w.m + (size_t)unit * max_splits * G + r;
+  const float* lrow = w.l + (size_t)unit * max_splits * G + r;
+  const float* orow = w.o + ((size_t)unit * max_splits * G + r) * D + c;
+  float M = -INFINITY;
+  for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, mrow[sp * G]);
+  float den = 0.f;
+  f32x4 n0 = {}, n1 = {};
+#pragma unroll 4
+  for (int sp = 0; sp < nsplit; ++sp) {
+    const float wgt = __builtin_amdgcn_exp2f(mrow[sp * G] - M) * lrow[sp * G];
+    den += wgt;
+    const float* op = orow + (size_t)sp * G * D;
+    n0 += wgt * *(const f32x4*)op;
+    n1 += wgt * *(const f32x4*)(op + 4);
   }
-  if (threadIdx.x == 0) w.tickets[unit] = 0;  // ready for the next call
+  const float rden = 1.f / den;
+  bf16x8 v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = (bf16)(n0[i] * rden);
+    v[4 + i] = (bf16)(n1[i] * rden);
+  }
+  *(bf16x8*)((bf16*)a.o + ((size_t)b * a.hq + kvh * G + r) * D + c) = v;
 }
 
 }  // namespace
@@ -732,14 +738,18 @@ DecodePlan decode_plan(int batch, int hkv, int max_blocks, int window) {
 size_t decode_workspace_bytes_bf16(int batch, int hkv, int max_blocks, int window) {
   const DecodePlan p = decode_plan(batch, hkv, max_blocks, window);
   const size_t units = (size_t)batch * hkv;
-  return round_up(units * sizeof(int), 256) + 2 * round_up(units * p.max_splits * G * sizeof(float), 256) +
+  return 2 * round_up(units * p.max_splits * G * sizeof(float), 256) +
          units * p.max_splits * G * D * sizeof(float);
 }
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
   const DecodePlan p = decode_plan(a.batch, a.hkv, a.max_blocks, a.window);
-  dim3 grid(p.max_splits, a.batch, a.hkv);
-  decode_bf16_kernel<<<grid, 256, 0, s>>>(a, p.tiles_per_split, p.max_splits);
+  decode_bf16_kernel<<<dim3(p.max_splits, a.batch, a.hkv), 256, 0, s>>>(a, p.tiles_per_split,
+                                                                      p.max_splits);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  decode_merge_kernel<<<dim3(G / kMergeRows, a.batch * a.hkv), 256, 0, s>>>(a, p.tiles_per_split,
+                                                                          p.max_splits);
   return hipGetLastError();
 }
 

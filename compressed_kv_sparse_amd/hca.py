@@ -146,11 +146,11 @@ def hca_decode_workspace_bytes(params: HcaParams, batch: int, max_blocks: int) -
 
 
 def new_decode_workspace(params: HcaParams, batch: int, max_blocks: int, device=None):
-    """Zero-filled workspace of the size hca_attend_decode needs (or None)."""
+    """Workspace of the size hca_attend_decode needs (or None if it needs none)."""
     n = hca_decode_workspace_bytes(params, batch, max_blocks)
     if n == 0:
         return None
-    return torch.zeros(n, dtype=torch.uint8, device=device or torch.cuda.current_device())
+    return torch.empty(n, dtype=torch.uint8, device=device or torch.cuda.current_device())
 
 
 def hca_attend_decode(params: HcaParams, seqlens, cu_blocks, max_blocks: int, q, kc, vc, kw, vw,

@@ -140,13 +140,11 @@ HCA_API size_t hca_decode_workspace_bytes(const hca_params* params, int32_t batc
  *                   sequence b is in slot s % ring_cap; ring_cap >= window
  *   o               device [B, Hq, d] output
  *   workspace       device scratch of workspace_bytes >=
- *                   hca_decode_workspace_bytes(...), 256-byte aligned.  The
- *                   first 4*batch*num_kv_heads bytes are per-(sequence, KV
- *                   head) counters that must be ZERO before the first call
- *                   (allocate the workspace zero-filled); every call that runs
- *                   to completion leaves them zero again.  Calls that share one
- *                   workspace must not overlap in time.  HCA_F32 needs no
- *                   workspace (size 0; NULL is accepted).
+ *                   hca_decode_workspace_bytes(...), 256-byte aligned, any
+ *                   contents (it holds per-split partial results between the
+ *                   two kernels of one call).  Calls that share one workspace
+ *                   must not overlap in time.  HCA_F32 needs no workspace
+ *                   (size 0; NULL is accepted).
  */
 HCA_API hca_status hca_attend_decode(const hca_params* params, int32_t batch, int32_t max_blocks,
                              const int32_t* seqlens, const int32_t* cu_blocks,

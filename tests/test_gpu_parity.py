@@ -220,17 +220,20 @@ def test_decode_f32(lens, hq, hkv, d, window, ring):
 
 
 def test_decode_workspace_reuse_and_determinism():
-    """Tickets return to zero after each call, so one workspace serves many
-    calls, and the split merge is bitwise repeatable."""
+    """One workspace serves many calls whatever it holds (it is filled with
+    garbage first), and the split merge is bitwise repeatable."""
     c = CONFIGS["decode_64x128k"]
     inp = decode_inputs(c, DEV, lens=[3000, 9000, 20000], seed=101)
     p = params_for(c)
     ws = hca.new_decode_workspace(p, 3, inp["max_blocks"])
+    ws.fill_(0x7f)
     o1 = run_decode(p, inp, ws).clone()
     o2 = run_decode(p, inp, ws).clone()
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
-    assert int(ws[: 4 * 3].view(torch.int32).abs().sum().item()) == 0
+    ref = oracle.attend_decode(inp["q"].cpu(), inp["kc"].cpu(), inp["vc"].cpu(), inp["kw"].cpu(),
+                               inp["vw"].cpu(), inp["lens"], inp["cu_blocks_host"], c.window)
+    assert_close(o1, ref, torch.bfloat16, "decode with a reused, garbage-filled workspace")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])

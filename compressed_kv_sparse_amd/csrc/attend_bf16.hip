@@ -78,24 +78,53 @@ struct KeySource {
   int raw0;        // row of the oldest raw key: lo, or lo % ring in a ring
 };
 
-// Which slots a row (one query position t) may see.
+// Which slots a row (one query position t) may see: compressed slots
+// [0, nvis_c) and raw slots [r0, r1] (its window; r1 <= nkeys - 1).  nc and
+// nkeys describe the workgroup's whole key list.
 struct RowMask {
-  int nc, nvis_c, nkeys, lo, smin, smax;
+  int nc, nkeys, nvis_c, r0, r1;
   __device__ __forceinline__ bool valid(int kappa) const {
-    if (kappa >= nkeys) return false;
-    if (kappa < nc) return kappa < nvis_c;
-    const int s = lo + kappa - nc;
-    return s >= smin && s <= smax;
+    return kappa < nvis_c || (unsigned)(kappa - r0) <= (unsigned)(r1 - r0);
   }
 };
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Two floats to one dword of two bf16 (round to nearest even), first in the
+// low half: one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ unsigned pack2_bf16(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
+}
+__device__ __forceinline__ float bf16_lo(unsigned p) { return __builtin_bit_cast(float, p << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned p) { return __builtin_bit_cast(float, p & 0xffff0000u); }
+// acc + both bf16 halves of p, exactly as the matrix core will see them
+__device__ __forceinline__ float sum2_bf16(unsigned p, float acc) {
+  const bf16x2 one = {(bf16)1.f, (bf16)1.f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p), one, acc, false);
+}
+// max over lanes l and l^32 (v_permlane32_swap: no LDS round trip)
+__device__ __forceinline__ float max_xor32(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+// max over lanes l and l^16
+__device__ __forceinline__ float max_xor16(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
 
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Issue the direct global->LDS loads of key tile `tile`: NW wavefronts share
 // the 32 K rows and 32 V rows; one instruction moves one 1 KiB row.  The row
-// of slot kappa is base + kappa * rstride, where base is chosen among three
-// precomputed pointers (compressed entries, raw rows, raw rows one ring length
-// back), so no branch and no per-row modulo is needed.
+// of slot kappa is base + kappa * rstride, where base is one of three
+// pointers (compressed entries, raw rows, raw rows one ring length back); no
+// per-row modulo is needed.
 template <int NW>
 __device__ __forceinline__ void issue_tile(const KeySource& ks, int tile, char HCA_LDS* kbuf,
                                            char HCA_LDS* vbuf, int wave, int lane) {
@@ -104,11 +133,33 @@ __device__ __forceinline__ void issue_tile(const KeySource& ks, int tile, char H
   const ptrdiff_t raw_shift = (ptrdiff_t)(ks.raw0 - ks.nc) * rs;  // raw slot kappa -> row raw0 + kappa - nc
   const ptrdiff_t wrap_shift = raw_shift - (ptrdiff_t)ks.ring * rs;
   const int wrap_from = ks.ring ? ks.nc - ks.raw0 + ks.ring : 0x7fffffff;  // first slot past the ring end
+  const int a0 = tile * NT;
+  const int kk0 = wave * RPW;
+  // Common case: all 32 slots lie in one region and inside the key list, so
+  // the rows are consecutive from one uniform base and each load only adds
+  // a constant multiple of the row stride.
+  const bool inside = a0 + NT <= ks.nkeys;
+  const bool all_comp = a0 + NT <= ks.nc;
+  const bool all_raw = a0 >= ks.nc && (a0 + NT <= wrap_from || a0 >= wrap_from);
+  if (inside && (all_comp || all_raw)) {
+    const ptrdiff_t shift = all_comp ? 0 : (a0 >= wrap_from ? wrap_shift : raw_shift);
+    const ptrdiff_t first = (ptrdiff_t)(a0 + kk0) * rs + shift;
+    const char* kb = (all_comp ? ks.comp_k : ks.raw_k) + first;
+    const char* vb = (all_comp ? ks.comp_v : ks.raw_v) + first;
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      __builtin_amdgcn_global_load_lds((const void HCA_GLOBAL*)(kb + r * rs + lane * 16),
+                                       (void HCA_LDS*)(kbuf + (kk0 + r) * KSTR), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void HCA_GLOBAL*)(vb + r * rs + lane * 16),
+                                       (void HCA_LDS*)(vbuf + (kk0 + r) * VSTR), 16, 0, 0);
+    }
+    return;
+  }
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
-    const int kk = wave * RPW + r;
+    const int kk = kk0 + r;
     // slots past the end re-read the last key (finite data; masked later)
-    const int kappa = min(tile * NT + kk, ks.nkeys - 1);
+    const int kappa = min(a0 + kk, ks.nkeys - 1);
     const bool comp = kappa < ks.nc;
     const ptrdiff_t shift = comp ? 0 : (kappa >= wrap_from ? wrap_shift : raw_shift);
     const ptrdiff_t off = (ptrdiff_t)kappa * rs + shift + lane * 16;
@@ -197,19 +248,19 @@ __device__ __forceinline__ bool compute_tile(const char HCA_LDS* kbuf, const cha
   // does not see inside the inline MFMAs, so they are spent here (24)
   asm volatile("s_nop 15\n\ts_nop 7" : "+v"(s0), "+v"(s1));
   f32x16 s = s0 + s1;
-  // scale into log2 units (in place), mask, row max over the lane pair
-#pragma unroll
-  for (int i = 0; i < 16; ++i) s[i] *= sc2;
+  // mask, then the row max over the lane pair; scores stay unscaled until
+  // the exponent (sc2 > 0, so max(sc2 * s) == sc2 * max(s) exactly)
   if (masked) {
+    asm volatile("");  // keep this a branch: most tiles need no mask
     const int kk0 = tile * NT + 4 * (lane >> 5);
 #pragma unroll
     for (int i = 0; i < 16; ++i)  // accumulator i holds key slot 8(i/4) + 4(l/32) + i%4
-      if (!rm.valid(kk0 + 8 * (i >> 2) + (i & 3))) s[i] = -INFINITY;
+      s[i] = rm.valid(kk0 + 8 * (i >> 2) + (i & 3)) ? s[i] : -INFINITY;
   }
   float mx = s[0];
 #pragma unroll
   for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = max_xor32(mx) * sc2;
   if (MODE == kMaxOnly) {
     st.m = fmaxf(st.m, mx);
     return false;
@@ -219,27 +270,34 @@ __device__ __forceinline__ bool compute_tile(const char HCA_LDS* kbuf, const cha
     if (st.m == -INFINITY) st.m = mx;  // first visible keys of the row
     over = mx > st.m + kHeadroom;
   }
-  const float m_use = st.m == -INFINITY ? 0.f : st.m;  // row with no visible key yet
+  const float nm = st.m == -INFINITY ? 0.f : -st.m;  // row with no visible key yet
+  float w[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) s[i] = __builtin_amdgcn_exp2f(s[i] - m_use);
-  bf16x8 pa, pb, qa = {}, qb = {};
-  float ls = 0.f;
+  for (int i = 0; i < 16; ++i) w[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sc2, nm));
+  // P as packed bf16 (B operand: weights 0..7 then 8..15); l sums the
+  // rounded weights, i.e. exactly what enters the product
+  u32x4 ua, ub, va = {}, vb = {};
+  float la = 0.f, lb = 0.f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    pa[j] = (bf16)s[j];
-    pb[j] = (bf16)s[8 + j];
+  for (int j = 0; j < 4; ++j) {
+    ua[j] = pack2_bf16(w[2 * j], w[2 * j + 1]);
+    ub[j] = pack2_bf16(w[8 + 2 * j], w[9 + 2 * j]);
+    la = sum2_bf16(ua[j], la);
+    lb = sum2_bf16(ub[j], lb);
   }
   if (two_term) {
+    asm volatile("");  // a branch, not a select: only short key lists take it
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      qa[j] = (bf16)(s[j] - (float)pa[j]);
-      qb[j] = (bf16)(s[8 + j] - (float)pb[j]);
-      ls += (float)qa[j] + (float)qb[j];
+    for (int j = 0; j < 4; ++j) {
+      va[j] = pack2_bf16(w[2 * j] - bf16_lo(ua[j]), w[2 * j + 1] - bf16_hi(ua[j]));
+      vb[j] = pack2_bf16(w[8 + 2 * j] - bf16_lo(ub[j]), w[9 + 2 * j] - bf16_hi(ub[j]));
+      la = sum2_bf16(va[j], la);
+      lb = sum2_bf16(vb[j], lb);
     }
   }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) ls += (float)pa[j] + (float)pb[j];  // sum of the weights used
-  st.l += ls;
+  st.l += la + lb;
+  const bf16x8 pa = __builtin_bit_cast(bf16x8, ua), pb = __builtin_bit_cast(bf16x8, ub);
+  const bf16x8 qa = __builtin_bit_cast(bf16x8, va), qb = __builtin_bit_cast(bf16x8, vb);
   const int parts = two_term ? 2 : 1;
   for (int part = 0; part < parts; ++part) {
     const bf16x8 ba = part ? qa : pa;
@@ -378,11 +436,10 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_kernel(PrefillArgs a) {
 
   RowMask rm;
   rm.nc = nc;
-  rm.nvis_c = (t + 1) / kBlock;
   rm.nkeys = nkeys;
-  rm.lo = lo;
-  rm.smin = t - a.window + 1;
-  rm.smax = t;
+  rm.nvis_c = (t + 1) / kBlock;
+  rm.r0 = nc + max(t - a.window + 1, lo) - lo;
+  rm.r1 = nc + t - lo;
 
   // The wave's 32 query rows (heads head0 .. head0+31 of position t) are
   // contiguous: stage them through LDS with whole-row loads, then read the
@@ -471,20 +528,20 @@ __device__ __forceinline__ bool compute_tile16(const char HCA_LDS* kbuf, const c
   float x[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    x[i] = s0[i] * sc2;
-    x[4 + i] = s1[i] * sc2;
+    x[i] = s0[i];
+    x[4 + i] = s1[i];
   }
   if (masked) {
+    asm volatile("");  // keep this a branch: most tiles need no mask
     const int kk0 = tile * NT + 4 * (lane >> 4);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if (!rm.valid(kk0 + (i >> 2) * 16 + (i & 3))) x[i] = -INFINITY;
+      x[i] = rm.valid(kk0 + (i >> 2) * 16 + (i & 3)) ? x[i] : -INFINITY;
   }
   float mx = x[0];
 #pragma unroll
   for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
-  mx = fmaxf(mx, __shfl_xor(mx, 16));  // lanes l, l^16, l^32, l^48 share row l%16
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = max_xor32(max_xor16(mx)) * sc2;  // lanes l, l^16, l^32, l^48 share row l%16
   if (MODE == kMaxOnly) {
     st.m = fmaxf(st.m, mx);
     return false;
@@ -494,23 +551,26 @@ __device__ __forceinline__ bool compute_tile16(const char HCA_LDS* kbuf, const c
     if (st.m == -INFINITY) st.m = mx;
     over = mx > st.m + kHeadroom;
   }
-  const float m_use = st.m == -INFINITY ? 0.f : st.m;
+  const float nm = st.m == -INFINITY ? 0.f : -st.m;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) x[i] = __builtin_amdgcn_exp2f(x[i] - m_use);
-  bf16x8 pa, qa = {};
+  for (int i = 0; i < 8; ++i) x[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], sc2, nm));
+  u32x4 ua, va = {};
   float ls = 0.f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) pa[j] = (bf16)x[j];
+  for (int j = 0; j < 4; ++j) {
+    ua[j] = pack2_bf16(x[2 * j], x[2 * j + 1]);
+    ls = sum2_bf16(ua[j], ls);
+  }
   if (two_term) {
+    asm volatile("");  // a branch, not a select: only short key lists take it
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      qa[j] = (bf16)(x[j] - (float)pa[j]);
-      ls += (float)qa[j];
+    for (int j = 0; j < 4; ++j) {
+      va[j] = pack2_bf16(x[2 * j] - bf16_lo(ua[j]), x[2 * j + 1] - bf16_hi(ua[j]));
+      ls = sum2_bf16(va[j], ls);
     }
   }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) ls += (float)pa[j];
   st.l += ls;
+  const bf16x8 pa = __builtin_bit_cast(bf16x8, ua), qa = __builtin_bit_cast(bf16x8, va);
   const int parts = two_term ? 2 : 1;
   for (int part = 0; part < parts; ++part) {
     const bf16x8 bp = part ? qa : pa;
@@ -641,11 +701,10 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a, int t
 
   RowMask rm;
   rm.nc = nc;
-  rm.nvis_c = nc;
   rm.nkeys = nkeys;
-  rm.lo = lo;
-  rm.smin = lo;
-  rm.smax = t;
+  rm.nvis_c = nc;
+  rm.r0 = nc;
+  rm.r1 = nkeys - 1;
 
   // Q^T fragments: lane l holds head row l%16, elements 32k + 8(l/16) .. +7
   bf16x8 qf[DSTEPS16];

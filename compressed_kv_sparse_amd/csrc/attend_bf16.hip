@@ -405,8 +405,10 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_kernel(PrefillArgs a) {
   const int b = blockIdx.y, kvh = blockIdx.z;
   const int start = a.cu_seqlens[b];
   const int len = a.cu_seqlens[b + 1] - start;
-  // latest (heaviest) position pairs are dispatched first
-  const int pair = (int)gridDim.x - 1 - (int)blockIdx.x;
+  // pairs in position order: measured 3-10% faster than heaviest-first
+  // (and far faster than orders that group heavy pairs on some XCDs, since
+  // workgroup i runs on XCD i % 8)
+  const int pair = (int)blockIdx.x;
   if (2 * pair >= len) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

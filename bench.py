@@ -38,9 +38,9 @@ PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3
 WORKLOADS = ("prefill_8k", "prefill_128k", "decode_64x128k", "mixed_1m", "tiny_f32")
 KERNEL_SOURCES = {
-    "prefill": "compressed_kv_sparse_amd/csrc/attend_bf16.hip",
-    "decode": "compressed_kv_sparse_amd/csrc/attend_bf16.hip",
-    "compress": "compressed_kv_sparse_amd/csrc/compress.hip",
+    "prefill": ("compressed_kv_sparse_amd/csrc/prefill_bf16.hip", "compressed_kv_sparse_amd/csrc/bf16_tiles.h"),
+    "decode": ("compressed_kv_sparse_amd/csrc/decode_bf16.hip", "compressed_kv_sparse_amd/csrc/bf16_tiles.h"),
+    "compress": ("compressed_kv_sparse_amd/csrc/compress.hip",),
 }
 
 
@@ -116,9 +116,13 @@ class KernelClock:
         self.pairs = {}
 
 
-def source_sha(rel):
-    with open(os.path.join(ROOT, rel), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_sha(rels):
+    """SHA-256 (16 hex digits) over the kernel's source files, in order."""
+    h = hashlib.sha256()
+    for rel in rels:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel, workload):

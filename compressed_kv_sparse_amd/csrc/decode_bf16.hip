@@ -1,0 +1,354 @@
+// bf16 HCA decode attention for 512-dim heads and 64 query heads per KV head
+// on CDNA4 matrix cores (v_mfma_f32_16x16x32_bf16, fp32 accumulation).
+//
+// What is computed (release blog "ERNIE 5.5 Flash Base", section 2.1, HCA
+// paragraph): the new token of each sequence, at position t = L-1, attends
+// under one softmax (scale 1/sqrt(d)) to the sequence's complete compressed
+// entries (floor(L/128) of them) and to its raw window, read from a ring
+// buffer that holds position s in slot s % R.
+//
+// Design (gfx950): one workgroup of 4 wavefronts x 16 heads per (sequence,
+// KV head, key split) streams its key range through LDS (tiles of 32 keys,
+// double buffered) and writes fp32 partials (m, l, O/l) to the workspace; a
+// second, fully parallel kernel merges them in split order, so the result
+// is deterministic.  Scores use the transposed product S^T = K Q^T and the
+// output O^T += V^T P^T as in prefill, with the softmax schedule of
+// bf16_tiles.h (no accumulator rescaling).
+#include <algorithm>
+
+#include "bf16_tiles.h"
+
+namespace hca {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Decode tiles: 16 query heads per wavefront on v_mfma_f32_16x16x32_bf16.
+// Decode streams each key once from HBM and does 64 flops per byte, far
+// below the matrix-core ridge, so it uses the narrower product: a wavefront
+// then needs 128 accumulator and 64 query registers instead of 256 and 128.
+// Layouts (16x16x32): A lane l = row l%16, k 8(l/16)..+7; B lane l = col
+// l%16, k 8(l/16)..+7; D lane l = rows 4(l/16)..+3, col l%16.
+// ---------------------------------------------------------------------------
+constexpr int DSTEPS16 = D / 32;  // k-steps of the score product
+constexpr int CTILES16 = D / 16;  // 16-column tiles of the output
+
+struct Acc16 {
+  f32x4 o[CTILES16];  // O^T: lane l holds row l%16, cols 16ct + 4(l/16) + i
+  float m, l;
+};
+
+// Scores of one 32-key tile land as S^T in two 16x16 outputs: lane l holds
+// row l%16 and key slots 4g + i (first output) and 16 + 4g + i (second),
+// g = l/16.  P^T as the B operand of the 16x16x32 product needs for lane l
+// the 8 keys k = 8g + j; taking j < 4 -> 4g + j and j >= 4 -> 16 + 4g + j-4
+// makes P come straight from those accumulators, and the V^T A operand reads
+// the same two 4-key runs with two transposed LDS reads.
+template <int MODE>
+__device__ __forceinline__ bool compute_tile16(const char HCA_LDS* kbuf, const char HCA_LDS* vbuf,
+                                               const bf16x8 (&qf)[DSTEPS16], Acc16& st, float sc2,
+                                               int lane, int koff, int voff, const RowMask& rm,
+                                               int tile, bool masked, bool two_term) {
+  constexpr int PF = 2;
+  f32x4 s0 = {}, s1 = {};
+  bf16x8 kf[2 * PF];
+#pragma unroll
+  for (int k = 0; k < PF; ++k) {
+    kf[2 * k] = lds_k_frag(kbuf + koff + k * 64);
+    kf[2 * k + 1] = lds_k_frag(kbuf + koff + 16 * KSTR + k * 64);
+  }
+#pragma unroll
+  for (int k = 0; k < DSTEPS16; ++k) {
+    const int r = (k % PF) * 2;
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[r], qf[k], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[r + 1], qf[k], s1, 0, 0, 0);
+    if (k + PF < DSTEPS16) {
+      kf[r] = lds_k_frag(kbuf + koff + (k + PF) * 64);
+      kf[r + 1] = lds_k_frag(kbuf + koff + 16 * KSTR + (k + PF) * 64);
+    }
+  }
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = s0[i];
+    x[4 + i] = s1[i];
+  }
+  if (masked) {
+    asm volatile("");  // keep this a branch: most tiles need no mask
+    const int kk0 = tile * NT + 4 * (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      x[i] = rm.valid(kk0 + (i >> 2) * 16 + (i & 3)) ? x[i] : -INFINITY;
+  }
+  float mx = x[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
+  mx = max_xor32(max_xor16(mx)) * sc2;  // lanes l, l^16, l^32, l^48 share row l%16
+  if (MODE == kMaxOnly) {
+    st.m = fmaxf(st.m, mx);
+    return false;
+  }
+  bool over = false;
+  if (MODE == kLazy) {
+    if (st.m == -INFINITY) st.m = mx;
+    over = mx > st.m + kHeadroom;
+  }
+  const float nm = st.m == -INFINITY ? 0.f : -st.m;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], sc2, nm));
+  u32x4 ua, va = {};
+  float ls = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    ua[j] = pack2_bf16(x[2 * j], x[2 * j + 1]);
+    ls = sum2_bf16(ua[j], ls);
+  }
+  if (two_term) {
+    asm volatile("");  // a branch, not a select: only short key lists take it
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      va[j] = pack2_bf16(x[2 * j] - bf16_lo(ua[j]), x[2 * j + 1] - bf16_hi(ua[j]));
+      ls = sum2_bf16(va[j], ls);
+    }
+  }
+  st.l += ls;
+  const bf16x8 pa = __builtin_bit_cast(bf16x8, ua), qa = __builtin_bit_cast(bf16x8, va);
+  const int parts = two_term ? 2 : 1;
+  for (int part = 0; part < parts; ++part) {
+    const bf16x8 bp = part ? qa : pa;
+    bf16x8 vf[PF];
+#pragma unroll
+    for (int u = 0; u < PF; ++u) vf[u] = lds_v_frag16(vbuf + voff + u * 32);
+#pragma unroll
+    for (int ct = 0; ct < CTILES16; ++ct) {
+      st.o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[ct % PF], bp, st.o[ct], 0, 0, 0);
+      if (ct + PF < CTILES16) vf[ct % PF] = lds_v_frag16(vbuf + voff + (ct + PF) * 32);
+    }
+  }
+  return MODE == kLazy && __any(over);
+}
+
+__device__ __forceinline__ void zero_acc16(Acc16& st) {
+#pragma unroll
+  for (int ct = 0; ct < CTILES16; ++ct) st.o[ct] = f32x4{};
+  st.m = -INFINITY;
+  st.l = 0.f;
+}
+
+template <int MODE>
+__device__ __forceinline__ bool tile_pass16(const KeySource& ks, int t_begin, int t_end,
+                                            const bf16x8 (&qf)[DSTEPS16], Acc16& st, float sc2,
+                                            const RowMask& rm, int wave, int lane,
+                                            char HCA_LDS* kv0, char HCA_LDS* kv1, int* flag,
+                                            bool two_term) {
+  const int g = lane >> 4;
+  const int koff = (lane & 15) * KSTR + g * 16;
+  const int voff = NT * KSTR + (4 * g + ((lane & 15) >> 2)) * VSTR + 4 * (lane & 3) * 2;
+  if (MODE == kLazy && threadIdx.x == 0) flag[0] = flag[1] = 0;
+  issue_tile<4>(ks, t_begin, kv0, kv0 + NT * KSTR, wave, lane);
+  wait_vm_all();
+  __syncthreads();
+  for (int tile = t_begin; tile < t_end; tile += 2) {  // two buffers, unrolled (see tile_pass)
+    if (tile + 1 < t_end) issue_tile<4>(ks, tile + 1, kv1, kv1 + NT * KSTR, wave, lane);
+    bool over = compute_tile16<MODE>(kv0, kv0, qf, st, sc2, lane, koff, voff, rm, tile,
+                                     tile_needs_mask(tile, rm.nc, rm.nkeys), two_term);
+    if (MODE == kLazy && over && lane == 0) flag[0] = 1;
+    wait_vm_all();
+    __syncthreads();
+    if (MODE == kLazy && flag[0]) return true;
+    if (tile + 1 >= t_end) break;
+    if (tile + 2 < t_end) issue_tile<4>(ks, tile + 2, kv0, kv0 + NT * KSTR, wave, lane);
+    over = compute_tile16<MODE>(kv1, kv1, qf, st, sc2, lane, koff, voff, rm, tile + 1,
+                                tile_needs_mask(tile + 1, rm.nc, rm.nkeys), two_term);
+    if (MODE == kLazy && over && lane == 0) flag[1] = 1;
+    wait_vm_all();
+    __syncthreads();
+    if (MODE == kLazy && flag[1]) return true;
+  }
+  return false;
+}
+
+__device__ __forceinline__ void attend_tiles16(const KeySource& ks, int t_begin, int t_end,
+                                               const bf16x8 (&qf)[DSTEPS16], Acc16& st, float sc2,
+                                               const RowMask& rm, int wave, int lane,
+                                               char HCA_LDS* kv0, char HCA_LDS* kv1, int* flag) {
+  const bool two_term = rm.nkeys <= kTwoTermKeys;
+  zero_acc16(st);
+  if (!tile_pass16<kLazy>(ks, t_begin, t_end, qf, st, sc2, rm, wave, lane, kv0, kv1, flag,
+                          two_term))
+    return;
+  __syncthreads();
+  zero_acc16(st);
+  tile_pass16<kMaxOnly>(ks, t_begin, t_end, qf, st, sc2, rm, wave, lane, kv0, kv1, flag, two_term);
+  tile_pass16<kFixed>(ks, t_begin, t_end, qf, st, sc2, rm, wave, lane, kv0, kv1, flag, two_term);
+}
+
+// ---------------------------------------------------------------------------
+// Decode: split kernel grid (max_splits, batch, Hkv), 256 threads (4
+// wavefronts x 16 heads), then the merge kernel.
+// Workspace: fp32 m and l [B*Hkv][splits][64], then fp32 O [B*Hkv][splits]
+// [64][512] normalised by its own l (a convex combination of value rows).
+// ---------------------------------------------------------------------------
+struct WsLayout {
+  float* m;
+  float* l;
+  float* o;
+};
+
+__host__ __device__ inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+__host__ __device__ inline WsLayout ws_layout(void* ws, int batch, int hkv, int splits) {
+  WsLayout w;
+  char* p = (char*)ws;
+  const size_t units = (size_t)batch * hkv;
+  w.m = (float*)p;
+  p += round_up(units * splits * G * sizeof(float), 256);
+  w.l = (float*)p;
+  p += round_up(units * splits * G * sizeof(float), 256);
+  w.o = (float*)p;
+  return w;
+}
+
+__global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a, int tps, int max_splits) {
+  __shared__ __attribute__((aligned(16))) char kv0_s[NT * KSTR + NT * VSTR];
+  __shared__ __attribute__((aligned(16))) char kv1_s[NT * KSTR + NT * VSTR];
+  __shared__ int flag_s[2];
+
+  const int split = blockIdx.x, b = blockIdx.y, kvh = blockIdx.z;
+  const int L = a.seqlens[b];
+  const int t = L - 1;                        // the new token's position
+  const int nc = L / kBlock;                  // complete blocks: 128(j+1) <= t+1
+  const int nraw = min(a.window, L);
+  const int lo = L - nraw;
+  const int nkeys = nc + nraw;
+  const int ntiles = (nkeys + NT - 1) / NT;
+  const int nsplit = (ntiles + tps - 1) / tps;
+  if (split >= nsplit) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = wave * 16 + (lane & 15);    // head within the KV group
+  const int head = kvh * G + row;
+
+  KeySource ks;
+  ks.rstride = a.hkv * D * (int)sizeof(bf16);
+  {
+    const size_t rs = (size_t)ks.rstride;
+    const size_t head_off = (size_t)kvh * D * sizeof(bf16);
+    const int nb = a.cu_blocks[b + 1] - a.cu_blocks[b];
+    ks.comp_k = make_rsrc((const char*)a.kc + (size_t)a.cu_blocks[b] * rs + head_off, (unsigned)(nb * rs));
+    ks.comp_v = make_rsrc((const char*)a.vc + (size_t)a.cu_blocks[b] * rs + head_off, (unsigned)(nb * rs));
+    ks.raw_k = make_rsrc((const char*)a.kw + (size_t)b * a.ring * rs + head_off, (unsigned)(a.ring * rs));
+    ks.raw_v = make_rsrc((const char*)a.vw + (size_t)b * a.ring * rs + head_off, (unsigned)(a.ring * rs));
+  }
+  ks.nc = nc;
+  ks.nkeys = nkeys;
+  ks.raw0 = lo % a.ring;
+  ks.ring = a.ring;
+
+  RowMask rm;
+  rm.nc = nc;
+  rm.nkeys = nkeys;
+  rm.nvis_c = nc;
+  rm.r0 = nc;
+  rm.r1 = nkeys - 1;
+
+  // Q^T fragments: lane l holds head row l%16, elements 32k + 8(l/16) .. +7
+  bf16x8 qf[DSTEPS16];
+  const bf16* qrow = (const bf16*)a.q + ((size_t)b * a.hq + head) * D + 8 * (lane >> 4);
+#pragma unroll
+  for (int k = 0; k < DSTEPS16; ++k) qf[k] = *(const bf16x8*)(qrow + 32 * k);
+  Acc16 st;
+  const float sc2 = a.scale * kLog2e;
+  const int t_begin = split * tps;
+  const int t_end = min(ntiles, t_begin + tps);
+  attend_tiles16(ks, t_begin, t_end, qf, st, sc2, rm, wave, lane, (char HCA_LDS*)kv0_s,
+                 (char HCA_LDS*)kv1_s, flag_s);
+
+  // this split's partial result: m, l and O / l
+  const WsLayout w = ws_layout(a.ws, a.batch, a.hkv, max_splits);
+  const size_t unit = (size_t)b * a.hkv + kvh;
+  const size_t prow = (unit * max_splits + split) * G + row;
+  float l_tot = st.l + __shfl_xor(st.l, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (lane < 16) {
+    w.m[prow] = st.m;
+    w.l[prow] = l_tot;
+  }
+  const float inv = 1.f / l_tot;
+  float* po = w.o + prow * D + 4 * (lane >> 4);
+#pragma unroll
+  for (int ct = 0; ct < CTILES16; ++ct) *(f32x4*)(po + 16 * ct) = st.o[ct] * inv;
+}
+
+// Merge of the split partials: O = sum_s 2^(m_s - M) l_s O_s / sum_s 2^(m_s - M) l_s
+// with M = max_s m_s, splits taken in order (deterministic).  One workgroup
+// of 256 threads merges kMergeRows heads of one (sequence, KV head); each
+// thread owns 8 columns of one head and issues its split loads independently.
+constexpr int kMergeRows = 4;
+
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int tps, int max_splits) {
+  const int unit = blockIdx.y;  // b * Hkv + kvh
+  const int b = unit / a.hkv, kvh = unit % a.hkv;
+  const int r = blockIdx.x * kMergeRows + (threadIdx.x >> 6);  // head within the KV group
+  const int c = (threadIdx.x & 63) * 8;
+  const int L = a.seqlens[b];
+  const int nkeys = L / kBlock + min(a.window, L);
+  const int nsplit = ((nkeys + NT - 1) / NT + tps - 1) / tps;
+  const WsLayout w = ws_layout(a.ws, a.batch, a.hkv, max_splits);
+  const float* mrow = w.m + (size_t)unit * max_splits * G + r;
+  const float* lrow = w.l + (size_t)unit * max_splits * G + r;
+  const float* orow = w.o + ((size_t)unit * max_splits * G + r) * D + c;
+  float M = -INFINITY;
+  for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, mrow[sp * G]);
+  float den = 0.f;
+  f32x4 n0 = {}, n1 = {};
+#pragma unroll 4
+  for (int sp = 0; sp < nsplit; ++sp) {
+    const float wgt = __builtin_amdgcn_exp2f(mrow[sp * G] - M) * lrow[sp * G];
+    den += wgt;
+    const float* op = orow + (size_t)sp * G * D;
+    n0 += wgt * *(const f32x4*)op;
+    n1 += wgt * *(const f32x4*)(op + 4);
+  }
+  const float rden = 1.f / den;
+  bf16x8 v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = (bf16)(n0[i] * rden);
+    v[4 + i] = (bf16)(n1[i] * rden);
+  }
+  *(bf16x8*)((bf16*)a.o + ((size_t)b * a.hq + kvh * G + r) * D + c) = v;
+}
+
+}  // namespace
+
+DecodePlan decode_plan(int batch, int hkv, int max_blocks, int window) {
+  // keys of the longest sequence: its entries plus at most min(W, L) raw rows
+  const long raw = std::min<long>(window, (long)kBlock * max_blocks + kBlock - 1);
+  const int ntiles = (int)((max_blocks + raw + NT - 1) / NT);
+  const long units = std::max<long>(1, (long)batch * hkv);
+  // aim for about one workgroup per compute unit
+  int splits = (int)std::min<long>(ntiles, std::max<long>(1, (256 + units - 1) / units));
+  const int tps = (ntiles + splits - 1) / splits;
+  splits = (ntiles + tps - 1) / tps;
+  return DecodePlan{tps, splits};
+}
+
+size_t decode_workspace_bytes_bf16(int batch, int hkv, int max_blocks, int window) {
+  const DecodePlan p = decode_plan(batch, hkv, max_blocks, window);
+  const size_t units = (size_t)batch * hkv;
+  return 2 * round_up(units * p.max_splits * G * sizeof(float), 256) +
+         units * p.max_splits * G * D * sizeof(float);
+}
+
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
+  const DecodePlan p = decode_plan(a.batch, a.hkv, a.max_blocks, a.window);
+  decode_bf16_kernel<<<dim3(p.max_splits, a.batch, a.hkv), 256, 0, s>>>(a, p.tiles_per_split,
+                                                                      p.max_splits);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  decode_merge_kernel<<<dim3(G / kMergeRows, a.batch * a.hkv), 256, 0, s>>>(a, p.tiles_per_split,
+                                                                          p.max_splits);
+  return hipGetLastError();
+}
+
+}  // namespace hca

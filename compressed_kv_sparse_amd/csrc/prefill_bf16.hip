@@ -1,0 +1,558 @@
+// bf16 HCA prefill attention for 512-dim heads and 64 query heads per KV
+// head on CDNA4 matrix cores (v_mfma_f32_32x32x16_bf16, fp32 accumulation).
+//
+// What is computed: release blog "ERNIE 5.5 Flash Base", section 2.1, HCA
+// paragraph, and Zhidx article, section "1. Latent-Gated Sparse Attention":
+// query t attends under one softmax (scale 1/sqrt(d)) to the complete
+// compressed entries j with 128(j+1) <= t+1, then to the raw window
+// max(0, t-W+1) .. t.
+//
+// Design (gfx950):
+//  * Head packing.  The 64 query heads of a KV head read the same keys, so a
+//    workgroup of 4 wavefronts owns 64 heads x 2 adjacent positions.  Wave
+//    w = 2 pw + hg holds the 32 score rows "heads 32hg .. +31 of position
+//    t0 + pw": every row of a wave has the same key set.
+//  * Transposed products keep every per-row quantity in one lane:
+//      S^T[key, row] = K[key, :] . Q^T[:, row]        (A = K from LDS, B = Q^T
+//                                                        resident in 128 VGPRs)
+//      O^T[col, row] += V^T[col, key] . P^T[key, row]  (A = V^T by transposed LDS
+//                                                        reads, B = P)
+//    With the 32x32 output layout lane l holds row l%32, so the row max and
+//    sum stay in the lane pair (l, l^32) and P is formed in the registers
+//    that received S.
+//  * Output split.  A wave accumulates O^T for all 64 heads of its position
+//    over one column half (256 AGPRs): every V^T fragment read from LDS
+//    feeds two MFMAs, one per head group.  The two waves of a position swap
+//    their bf16 weights through LDS.
+//  * Software pipeline.  Stage s issues, interleaved one by one, the score
+//    MFMAs of tile s+1 and the output MFMAs of tile s-1, and spreads the
+//    softmax of tile s (VALU) between them: the three are independent, so
+//    the matrix cores never wait for the exponentials.  Meanwhile K(s+2) and
+//    V(s) stream into LDS.  K, V and weight buffers alternate with the
+//    stage's parity; the stage loop is unrolled by two so that every LDS
+//    access names its buffer at compile time (the compiler then never makes
+//    an LDS read wait for direct loads into another buffer).
+//  * Softmax without rescaling (Mode in bf16_tiles.h): the 256 fp32
+//    accumulators per lane stay in AGPRs and are only touched by the matrix
+//    cores.  A pass whose scores climb more than 32 (log2 units) above a
+//    row's first maximum restarts the workgroup in the exact two-pass
+//    schedule.
+//  * Short key lists (<= 64 keys) carry the weights as two bf16 terms
+//    P = hi + lo, lo = bf16(P - hi) (~2^-16 relative instead of 2^-9): rows
+//    that see only a few keys have few large weights whose rounding does not
+//    average out.  They take a plain per-tile loop (at most two tiles).
+#include "bf16_tiles.h"
+
+namespace hca {
+namespace {
+
+constexpr int DSTEPS = D / 16;  // k-steps of the score product (32)
+constexpr int HCT = 8;          // 32-column output tiles per wave (256 columns)
+constexpr int WSLOT = 2048;     // LDS bytes of one wave's bf16 weights of one tile (64 lanes x 32 B)
+constexpr int OSTR = 528;       // LDS bytes per staged output half-row (512 + 16 pad)
+
+// bf16 weights of one tile in B-operand order: hi[k2] feeds key step k2.
+struct Wts {
+  bf16x8 hi[2];
+};
+
+// Output accumulators and softmax state of one wave.
+struct PState {
+  f32x16 o[2][HCT];  // O^T [0] = own head group, [1] = the partner's: lane l
+                     // holds head 32g + l%32 of the wave's position and
+                     // columns 256hg + 32ct + 8(r/4) + 4(l/32) + r%4
+  float m, l;        // state of the wave's own score rows (lane pair l, l^32;
+                     // both lanes hold m, each a partial l)
+};
+
+// Everything a stage needs besides the registers it updates.  The LDS
+// pointers are the addresses of distinct __shared__ arrays.
+struct Ctx {
+  KeySource ks;
+  RowMask rm;
+  char HCA_LDS* kb[2];
+  char HCA_LDS* vb[2];
+  char HCA_LDS* ws[2];  // weight slots [parity]: 4 waves x WSLOT
+  int* flag;
+  int lane, wave, n;
+  int koff;   // this lane's K fragment offset in a K tile
+  int voff;   // this lane's V^T fragment offset in a V tile (column half included)
+  int wown;   // this wave's slot offset (+ lane * 16)
+  int wpar;   // the partner's slot offset (+ lane * 16)
+  float sc2;  // softmax scale * log2(e)
+};
+
+__device__ __forceinline__ void zero_state(PState& st) {
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int ct = 0; ct < HCT; ++ct) st.o[g][ct] = f32x16{};
+  st.m = -INFINITY;
+  st.l = 0.f;
+}
+
+// Visibility mask of one tile's scores (uniform branch at the caller: only
+// tiles that contain an invisible slot pay for it).  Accumulator r of lane
+// l holds key slot 8(r/4) + 4(l/32) + r%4 of the tile.
+__device__ __forceinline__ void mask_scores(f32x16& s, const RowMask& rm, int tile, int lane) {
+  const int kk0 = tile * NT + 4 * (lane >> 5);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = rm.valid(kk0 + 8 * (r >> 2) + (r & 3)) ? s[r] : -INFINITY;
+}
+
+// Softmax work of one tile while it is spread over a stage's steps (see
+// stage()): partial maxima, the lane-pair max and reference update, 16
+// exponentials, then packing to bf16 and the row sum of exactly the rounded
+// weights.
+struct SmWork {
+  float x[16];  // partial maxima, then weights
+  float mx;     // row max, then the exponent offset
+  u32x4 ua, ub;
+  float la, lb;
+  bool over;
+};
+
+// Score MFMA k of the chain in `acc` (inline, so that the accumulator stays
+// in VGPRs while the 256 AGPRs hold O).
+__device__ __forceinline__ void s_mfma(int k, f32x16& acc, const bf16x8& kf, const bf16x8& qf) {
+  if (k == 0)
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(kf), "v"(qf));
+  else
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(kf), "v"(qf));
+}
+
+// V^T fragment f of the wave's column half: column tile f & 7, key step f >> 3.
+__device__ __forceinline__ int vfrag_off(int f) { return (f >> 3) * 16 * VSTR + (f & 7) * 64; }
+
+// One pipeline stage s with parity P = s & 1 (see the file comment): the
+// score product of tile s+1 (K in kb[1-P]) into `sacc`, the softmax of tile
+// s from `sprev` (weights into `own` and the wave's slot ws[P]) and the
+// output product of tile s-1 (V in vb[1-P]; weights in `own` and the
+// partner's from ws[1-P]).  Every stage runs all three parts, so the hot
+// loop is straight-line code and the accumulators never change registers;
+// a part whose tile lies outside [0, n) computes on stale (finite) buffer
+// contents and contributes nothing: the softmax of a missing tile writes
+// zero weights, and an output product with zero weights adds zero.  Loads
+// K(s+2) into kb[P] and V(s) into vb[P], and ends with the workgroup
+// barrier.  A kLazy softmax that exceeds the headroom raises flag[0] for the
+// rest of the pass.
+template <int P, int MODE>
+__device__ __forceinline__ void stage(const Ctx& c, int s, const bf16x8 (&qf)[DSTEPS], f32x16& sacc,
+                                      f32x16& sprev, Wts& own, PState& st) {
+  const bool hm = s >= 0 && s < c.n;  // tile s exists
+  const unsigned keep = hm ? ~0u : 0u;  // weights of a missing tile are zeroed (no branch)
+  if (s + 2 < c.n) issue_tile<4, true, false>(c.ks, s + 2, c.kb[P], nullptr, c.wave, c.lane);
+  if (hm) issue_tile<4, false, true>(c.ks, s, nullptr, c.vb[P], c.wave, c.lane);
+  if (hm && tile_needs_mask(s, c.rm.nc, c.rm.nkeys)) {
+    asm volatile("");  // a branch: most tiles need no mask
+    mask_scores(sprev, c.rm, s, c.lane);
+  }
+  Wts par;
+  {
+    const char HCA_LDS* pin = c.ws[1 - P] + c.wpar;
+    par.hi[0] = *(const bf16x8 HCA_LDS*)pin;
+    par.hi[1] = *(const bf16x8 HCA_LDS*)(pin + 1024);
+  }
+  constexpr int KPF = 3;  // K fragments read three steps ahead
+  bf16x8 kf[KPF], vf[3];
+  const char HCA_LDS* kr = c.kb[1 - P] + c.koff;
+  const char HCA_LDS* vr = c.vb[1 - P] + c.voff;
+#pragma unroll
+  for (int k = 0; k < KPF; ++k) kf[k] = lds_k_frag(kr + k * 32);
+  vf[0] = lds_v_frag(vr + vfrag_off(0));
+  vf[1] = lds_v_frag(vr + vfrag_off(1));
+
+  SmWork w;
+  // 32 steps: one score MFMA, one output MFMA, a slice of the softmax
+#pragma unroll
+  for (int j = 0; j < DSTEPS; ++j) {
+    s_mfma(j, sacc, kf[j % KPF], qf[j]);
+    if (j + KPF < DSTEPS) kf[j % KPF] = lds_k_frag(kr + (j + KPF) * 32);
+    {
+      // output step u = j: fragment f = u / 2, head group u % 2 (0 = own)
+      const int f = j >> 1, g = j & 1;
+      const bf16x8 b = g ? par.hi[f >> 3] : own.hi[f >> 3];
+      st.o[g][f & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[f % 3], b, st.o[g][f & 7], 0, 0, 0);
+      if (g == 1 && f + 2 < 16) vf[(f + 2) % 3] = lds_v_frag(vr + vfrag_off(f + 2));
+    }
+    if (j == 0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w.x[i] = fmaxf(sprev[i], sprev[i + 8]);
+    }
+    if (j == 1)
+      w.mx = fmaxf(fmaxf(fmaxf(w.x[0], w.x[1]), fmaxf(w.x[2], w.x[3])),
+                   fmaxf(fmaxf(w.x[4], w.x[5]), fmaxf(w.x[6], w.x[7])));
+    if (j == 2) {
+      const float mx = max_xor32(w.mx) * c.sc2;  // sc2 > 0: max(sc2 s) == sc2 max(s)
+      w.over = false;
+      if (MODE == kLazy) {
+        if (hm && st.m == -INFINITY) st.m = mx;  // first visible keys of the row
+        w.over = hm && mx > st.m + kHeadroom;
+      }
+      w.mx = st.m == -INFINITY ? 0.f : -st.m;  // a row with no visible key yet: 0
+    }
+    if (j >= 3 && j < 11) {  // two exponentials per step
+      const int i = 2 * (j - 3);
+      w.x[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sprev[i], c.sc2, w.mx));
+      w.x[i + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(sprev[i + 1], c.sc2, w.mx));
+    }
+    if (j >= 11 && j < 15) {  // pack the weights (B operand: 0..7, then 8..15)
+      const int q = j - 11;
+      if (q == 0) w.la = w.lb = 0.f;
+      w.ua[q] = pack2_bf16(w.x[2 * q], w.x[2 * q + 1]) & keep;
+      w.ub[q] = pack2_bf16(w.x[8 + 2 * q], w.x[9 + 2 * q]) & keep;
+      w.la = sum2_bf16(w.ua[q], w.la);
+      w.lb = sum2_bf16(w.ub[q], w.lb);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // a VALU read of an MFMA result needs up to 18 wait states; the compiler
+  // does not see inside the inline MFMAs, so they are spent here (24)
+  asm volatile("s_nop 15\n\ts_nop 7" : "+v"(sacc));
+  st.l += w.la + w.lb;
+  own.hi[0] = __builtin_bit_cast(bf16x8, w.ua);
+  own.hi[1] = __builtin_bit_cast(bf16x8, w.ub);
+  char HCA_LDS* pout = c.ws[P] + c.wown;
+  *(u32x4 HCA_LDS*)pout = w.ua;
+  *(u32x4 HCA_LDS*)(pout + 1024) = w.ub;
+  if (MODE == kLazy && __any(w.over) && c.lane == 0) c.flag[0] = 1;
+  wait_vm_all();
+  __syncthreads();
+}
+
+// One software-pipelined pass over all n tiles in schedule MODE (kLazy or
+// kFixed): stages -1 .. n (plus one empty stage when the count is odd).
+// K(0) must be in kb[0], slot ws[0] must hold zero weights and all K and V
+// buffers finite values (the empty parts of the first stages read them).  The pass always runs to its end (an exit in the middle makes
+// the register allocator spill); the caller then reads flag[0] to learn
+// whether a kLazy pass must be redone.
+template <int MODE>
+__device__ __forceinline__ void pipelined_pass(const Ctx& c, const bf16x8 (&qf)[DSTEPS], PState& st) {
+  f32x16 sa = {}, sb = {};  // score accumulators, alternating roles with the parity
+  Wts own;
+  own.hi[0] = own.hi[1] = bf16x8{};
+  int s = -1;
+  do {
+    stage<1, MODE>(c, s, qf, sa, sb, own, st);
+    stage<0, MODE>(c, s + 1, qf, sb, sa, own, st);
+    s += 2;
+  } while (s <= c.n);
+}
+
+// Plain per-tile loop (no overlap between the products): short key lists
+// with two-term weights (LO), and the row-max pass of the exact schedule
+// (kMaxOnly, scores only).  K(0) (and V(0) unless kMaxOnly) must already be
+// in kb[0] / vb[0].  Weight exchange through slot ws[0] (remainders ws[1])
+// with a barrier on each side.  Raises flag[0] like stage().
+template <int P, int MODE, bool LO>
+__device__ __forceinline__ void plain_tile(const Ctx& c, int s, const bf16x8 (&qf)[DSTEPS], PState& st) {
+  constexpr bool PV = MODE != kMaxOnly;
+  if (s + 1 < c.n) issue_tile<4, true, PV>(c.ks, s + 1, c.kb[1 - P], c.vb[1 - P], c.wave, c.lane);
+  const char HCA_LDS* kr = c.kb[P] + c.koff;
+  f32x16 sc;  // one dependent chain: this loop is not the fast path
+  {
+    constexpr int KPF = 2;
+    bf16x8 kf[KPF];
+#pragma unroll
+    for (int k = 0; k < KPF; ++k) kf[k] = lds_k_frag(kr + k * 32);
+#pragma unroll
+    for (int k = 0; k < DSTEPS; ++k) {
+      s_mfma(k, sc, kf[k % KPF], qf[k]);
+      if (k + KPF < DSTEPS) kf[k % KPF] = lds_k_frag(kr + (k + KPF) * 32);
+    }
+    asm volatile("s_nop 15\n\ts_nop 7" : "+v"(sc));
+  }
+  if (tile_needs_mask(s, c.rm.nc, c.rm.nkeys)) mask_scores(sc, c.rm, s, c.lane);
+  float mx = sc[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+  mx = max_xor32(mx) * c.sc2;
+  if (MODE == kMaxOnly) {
+    st.m = fmaxf(st.m, mx);
+    wait_vm_all();
+    __syncthreads();
+    return;
+  }
+  bool over = false;
+  if (MODE == kLazy) {
+    if (st.m == -INFINITY) st.m = mx;
+    over = mx > st.m + kHeadroom;
+  }
+  const float nm = st.m == -INFINITY ? 0.f : -st.m;
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], c.sc2, nm));
+  u32x4 ua, ub, va = {}, vb = {};
+  float ls = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    ua[q] = pack2_bf16(x[2 * q], x[2 * q + 1]);
+    ub[q] = pack2_bf16(x[8 + 2 * q], x[9 + 2 * q]);
+    ls = sum2_bf16(ub[q], sum2_bf16(ua[q], ls));
+    if (LO) {
+      va[q] = pack2_bf16(x[2 * q] - bf16_lo(ua[q]), x[2 * q + 1] - bf16_hi(ua[q]));
+      vb[q] = pack2_bf16(x[8 + 2 * q] - bf16_lo(ub[q]), x[9 + 2 * q] - bf16_hi(ub[q]));
+      ls = sum2_bf16(vb[q], sum2_bf16(va[q], ls));
+    }
+  }
+  st.l += ls;
+  // exchange the weights with the partner wave (slot ws[0]: hi, then lo in ws[1])
+  {
+    char HCA_LDS* o0 = c.ws[0] + c.wown;
+    *(u32x4 HCA_LDS*)o0 = ua;
+    *(u32x4 HCA_LDS*)(o0 + 1024) = ub;
+    if (LO) {
+      char HCA_LDS* o1 = c.ws[1] + c.wown;
+      *(u32x4 HCA_LDS*)o1 = va;
+      *(u32x4 HCA_LDS*)(o1 + 1024) = vb;
+    }
+    if (MODE == kLazy && __any(over) && c.lane == 0) c.flag[0] = 1;
+  }
+  __syncthreads();
+  const char HCA_LDS* vr = c.vb[P] + c.voff;
+#pragma unroll
+  for (int part = 0; part < (LO ? 2 : 1); ++part) {
+    bf16x8 b[2][2];  // [group own/partner][key step]
+    b[0][0] = __builtin_bit_cast(bf16x8, part ? va : ua);
+    b[0][1] = __builtin_bit_cast(bf16x8, part ? vb : ub);
+    b[1][0] = *(const bf16x8 HCA_LDS*)(c.ws[part] + c.wpar);
+    b[1][1] = *(const bf16x8 HCA_LDS*)(c.ws[part] + c.wpar + 1024);
+#pragma unroll
+    for (int f = 0; f < 16; ++f) {
+      const bf16x8 vf = lds_v_frag(vr + vfrag_off(f));
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+        st.o[g][f & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, b[g][f >> 3], st.o[g][f & 7], 0, 0, 0);
+    }
+  }
+  wait_vm_all();
+  __syncthreads();  // partner weights read, buffers of this parity free
+}
+
+template <int MODE, bool LO>
+__device__ __forceinline__ void plain_pass(const Ctx& c, const bf16x8 (&qf)[DSTEPS], PState& st) {
+  int s = 0;
+  for (; s + 1 < c.n; s += 2) {
+    plain_tile<0, MODE, LO>(c, s, qf, st);
+    plain_tile<1, MODE, LO>(c, s + 1, qf, st);
+  }
+  if (s < c.n) plain_tile<0, MODE, LO>(c, s, qf, st);
+}
+
+// Start of a pass: clear the flag and slot ws[0] (zero weights for the
+// first stage's empty output product), load K(0) (and V(0) for the plain
+// loop).
+__device__ __forceinline__ void pass_setup(const Ctx& c, bool with_v) {
+  if (c.lane == 0 && c.wave == 0) c.flag[0] = c.flag[1] = 0;
+  for (int o = threadIdx.x * 16; o < 4 * WSLOT; o += 256 * 16) *(u32x4 HCA_LDS*)(c.ws[0] + o) = u32x4{};
+  if (with_v)
+    issue_tile<4, true, true>(c.ks, 0, c.kb[0], c.vb[0], c.wave, c.lane);
+  else
+    issue_tile<4, true, false>(c.ks, 0, c.kb[0], nullptr, c.wave, c.lane);
+  wait_vm_all();
+  __syncthreads();
+}
+
+// All tiles: single-pass schedule first; if a row's scores grew past the
+// headroom, the exact two-pass schedule (row max, then weights <= 1).  LO:
+// two-term weights in the plain loop (short key lists).
+template <bool LO>
+__device__ __forceinline__ void attend_pair(const Ctx& c, const bf16x8 (&qf)[DSTEPS], PState& st) {
+  zero_state(st);
+  pass_setup(c, LO);
+  if (LO)
+    plain_pass<kLazy, true>(c, qf, st);
+  else
+    pipelined_pass<kLazy>(c, qf, st);
+  if (!c.flag[0]) return;  // read after the pass's last barrier
+  __syncthreads();         // every wave has read the flag
+  zero_state(st);
+  pass_setup(c, false);
+  plain_pass<kMaxOnly, false>(c, qf, st);
+  pass_setup(c, LO);
+  if (LO)
+    plain_pass<kFixed, true>(c, qf, st);
+  else
+    pipelined_pass<kFixed>(c, qf, st);
+}
+
+// O = acc / l for all 64 heads of the wave's position over its column half,
+// rounded to bf16.  1/l of the partner's rows comes through LDS.  The
+// half-rows are staged in the wave's own buffer, one head group (32 rows x
+// OSTR bytes) at a time, and stored two per instruction (lanes 0-31 row 2i,
+// lanes 32-63 row 2i+1; 512 contiguous bytes each).
+__device__ __forceinline__ void store_output(const Ctx& c, const PState& st, float* linv, bf16* obase,
+                                             bool row_ok) {
+  const int lane = c.lane, wave = c.wave, hg = wave & 1;
+  const float lt = st.l + __shfl_xor(st.l, 32);
+  const float inv_own = 1.f / lt;
+  if (lane < 32) linv[wave * 32 + lane] = inv_own;
+  __syncthreads();  // every wave is past its last tile: K/V buffers are free
+  const float inv_par = linv[(wave ^ 1) * 32 + (lane & 31)];
+  if (!row_ok) return;
+  char HCA_LDS* stg = wave == 0 ? c.kb[0] : wave == 1 ? c.kb[1] : wave == 2 ? c.vb[0] : c.vb[1];
+  const int hr = lane >> 5, cw = (lane & 31) * 8;
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const float inv = g ? inv_par : inv_own;
+    char HCA_LDS* rowp = stg + (lane & 31) * OSTR + (lane >> 5) * 8;
+#pragma unroll
+    for (int ct = 0; ct < HCT; ++ct)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = (bf16)(st.o[g][ct][4 * q4 + i] * inv);
+        *(bf16x4 HCA_LDS*)(rowp + (32 * ct + 8 * q4) * 2) = v;
+      }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's LDS writes are done
+    bf16* og = obase + (size_t)(32 * (hg ^ g)) * D;
+#pragma unroll 4
+    for (int i = 0; i < 16; ++i) {
+      const int row = 2 * i + hr;
+      *(bf16x8*)(og + (size_t)row * D + cw) = *(const bf16x8 HCA_LDS*)(stg + row * OSTR + cw * 2);
+    }
+  }
+}
+
+// Keys of position pair (t0, t_last): the later position's complete entries
+// plus the raw rows from the earlier position's window start to t_last.
+__host__ __device__ inline int pair_keys(int t0, int t_last, int window) {
+  const int lo = t0 - window + 1 > 0 ? t0 - window + 1 : 0;
+  return (t_last + 1) / kBlock + (t_last - lo + 1);
+}
+
+// ---------------------------------------------------------------------------
+// Grid (pairs, batch, Hkv), 256 threads: one position pair per workgroup,
+// pair index blockIdx.x + pair0.  LO = true handles the pairs whose key list
+// has at most kTwoTermKeys keys (two-term weights, plain loop), LO = false
+// all others (pipelined); each skips the pairs of the other kind.
+// ---------------------------------------------------------------------------
+template <bool LO>
+__global__ __launch_bounds__(256, 1) void prefill_bf16_kernel(PrefillArgs a, int pair0) {
+  __shared__ __attribute__((aligned(16))) char k0_s[KTILE];
+  __shared__ __attribute__((aligned(16))) char k1_s[KTILE];
+  __shared__ __attribute__((aligned(16))) char v0_s[VTILE];
+  __shared__ __attribute__((aligned(16))) char v1_s[VTILE];
+  __shared__ __attribute__((aligned(16))) char w0_s[4 * WSLOT];
+  __shared__ __attribute__((aligned(16))) char w1_s[4 * WSLOT];
+  __shared__ int flag_s[2];
+  __shared__ float linv_s[4 * 32];
+
+  const int b = blockIdx.y, kvh = blockIdx.z;
+  const int start = a.cu_seqlens[b];
+  const int len = a.cu_seqlens[b + 1] - start;
+  const int pair = (int)blockIdx.x + pair0;
+  if (2 * pair >= len) return;
+  {
+    const int t0 = 2 * pair;
+    const int t_last = t0 + 1 < len ? t0 + 1 : t0;
+    if ((pair_keys(t0, t_last, a.window) <= kTwoTermKeys) != LO) return;
+  }
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pw = wave >> 1, hg = wave & 1;
+  const int t0 = 2 * pair;
+  const bool t1_ok = t0 + 1 < len;
+  const int t_last = t1_ok ? t0 + 1 : t0;
+  const bool row_ok = pw == 0 || t1_ok;
+  const int t = row_ok ? t0 + pw : t0;  // an absent second position recomputes t0
+
+  const int nc = (t_last + 1) / kBlock;      // entries visible to the later position
+  const int lo = max(0, t0 - a.window + 1);  // oldest raw key of the earlier position
+  const int nkeys = nc + (t_last - lo + 1);
+
+  Ctx c;
+  c.ks.rstride = a.hkv * D * (int)sizeof(bf16);
+  {
+    const size_t rs = (size_t)c.ks.rstride;
+    const size_t head_off = (size_t)kvh * D * sizeof(bf16);
+    const int nb = a.cu_blocks[b + 1] - a.cu_blocks[b];
+    c.ks.comp_k = make_rsrc((const char*)a.kc + (size_t)a.cu_blocks[b] * rs + head_off, (unsigned)(nb * rs));
+    c.ks.comp_v = make_rsrc((const char*)a.vc + (size_t)a.cu_blocks[b] * rs + head_off, (unsigned)(nb * rs));
+    c.ks.raw_k = make_rsrc((const char*)a.k + (size_t)start * rs + head_off, (unsigned)(len * rs));
+    c.ks.raw_v = make_rsrc((const char*)a.v + (size_t)start * rs + head_off, (unsigned)(len * rs));
+  }
+  c.ks.nc = nc;
+  c.ks.nkeys = nkeys;
+  c.ks.raw0 = lo;
+  c.ks.ring = 0;
+  c.rm.nc = nc;
+  c.rm.nkeys = nkeys;
+  c.rm.nvis_c = (t + 1) / kBlock;
+  c.rm.r0 = nc + max(t - a.window + 1, lo) - lo;
+  c.rm.r1 = nc + t - lo;
+  c.kb[0] = (char HCA_LDS*)k0_s;
+  c.kb[1] = (char HCA_LDS*)k1_s;
+  c.vb[0] = (char HCA_LDS*)v0_s;
+  c.vb[1] = (char HCA_LDS*)v1_s;
+  c.ws[0] = (char HCA_LDS*)w0_s;
+  c.ws[1] = (char HCA_LDS*)w1_s;
+  c.flag = flag_s;
+  c.lane = lane;
+  c.wave = wave;
+  c.n = (nkeys + NT - 1) / NT;
+  c.koff = (lane & 31) * KSTR + (lane >> 5) * 16;
+  c.voff = (4 * (lane >> 5) + ((lane & 15) >> 2)) * VSTR + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2 +
+           hg * HCT * 64;
+  c.wown = wave * WSLOT + lane * 16;
+  c.wpar = (wave ^ 1) * WSLOT + lane * 16;
+  c.sc2 = a.scale * kLog2e;
+
+  // the empty parts of the first pipeline stages read the K and V buffers:
+  // make them finite
+  for (int o = threadIdx.x * 16; !LO && o < KTILE; o += 256 * 16) {
+    *(u32x4 HCA_LDS*)(c.kb[0] + o) = u32x4{};
+    *(u32x4 HCA_LDS*)(c.kb[1] + o) = u32x4{};
+  }
+  for (int o = threadIdx.x * 16; !LO && o < VTILE; o += 256 * 16) {
+    *(u32x4 HCA_LDS*)(c.vb[0] + o) = u32x4{};
+    *(u32x4 HCA_LDS*)(c.vb[1] + o) = u32x4{};
+  }
+
+  // Q^T fragments of the wave's 32 rows (heads 32hg .. +31 of position t):
+  // lane l holds row l%32, elements 16k + 8(l/32) .. +7
+  const bf16* qbase = (const bf16*)a.q + ((size_t)(start + t) * a.hq + kvh * G) * D;
+  bf16x8 qf[DSTEPS];
+  {
+    const bf16* qrow = qbase + (size_t)(32 * hg + (lane & 31)) * D + 8 * (lane >> 5);
+#pragma unroll
+    for (int k = 0; k < DSTEPS; ++k) qf[k] = *(const bf16x8*)(qrow + 16 * k);
+  }
+  PState st;
+  attend_pair<LO>(c, qf, st);
+  bf16* obase = (bf16*)a.o + ((size_t)(start + t) * a.hq + kvh * G) * D + hg * 256;
+  store_output(c, st, linv_s, obase, row_ok);
+}
+
+}  // namespace
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
+  const int npairs = (a.max_seqlen + 1) / 2;
+  // Key counts grow with the pair index, so the two-term pairs are a prefix
+  // of every sequence: pairs [0, lo_end) may be two-term (a lone last
+  // position has one key less than a full pair), pairs [hi_begin, npairs)
+  // may be not; each kernel checks every pair it is given.
+  auto first_over = [&](bool lone) {  // first pair with more than kTwoTermKeys keys
+    int lo = 0, hi = npairs;
+    while (lo < hi) {
+      const int m = lo + (hi - lo) / 2;
+      if (pair_keys(2 * m, 2 * m + (lone ? 0 : 1), a.window) > kTwoTermKeys)
+        hi = m;
+      else
+        lo = m + 1;
+    }
+    return lo;
+  };
+  const int lo_end = first_over(true), hi_begin = first_over(false);
+  if (lo_end > 0) {
+    prefill_bf16_kernel<true><<<dim3(lo_end, a.batch, a.hkv), 256, 0, s>>>(a, 0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (hi_begin < npairs)
+    prefill_bf16_kernel<false><<<dim3(npairs - hi_begin, a.batch, a.hkv), 256, 0, s>>>(a, hi_begin);
+  return hipGetLastError();
+}
+
+}  // namespace hca

@@ -63,17 +63,22 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a, int cw) {
   const int r0 = tid / TPR;
   __syncthreads();
 
+  // all of this thread's loads are issued before any is used, so a thread
+  // keeps PASSES 16-byte loads in flight (the default schedule would wait
+  // for each load before issuing the next)
+  typedef T vec_t __attribute__((ext_vector_type(VEC)));
+  vec_t xv[PASSES];
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ++ps) xv[ps] = *(const vec_t*)(x + (size_t)(ps * RPP + r0) * rstride);
+  __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of their uses
   float acc[VEC];
 #pragma unroll
   for (int c = 0; c < VEC; ++c) acc[c] = 0.f;
-#pragma unroll 8
-  for (int ps = 0; ps < PASSES; ++ps) {
-    const int row = ps * RPP + r0;
-    const float pr = p_s[row];
-    typedef T vec_t __attribute__((ext_vector_type(VEC)));
-    vec_t xv = *(const vec_t*)(x + (size_t)row * rstride);
 #pragma unroll
-    for (int c = 0; c < VEC; ++c) acc[c] = fmaf(pr, to_f32(xv[c]), acc[c]);
+  for (int ps = 0; ps < PASSES; ++ps) {
+    const float pr = p_s[ps * RPP + r0];
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) acc[c] = fmaf(pr, to_f32(xv[ps][c]), acc[c]);
   }
   // reduce over the rows a wavefront holds (lanes that differ in the bits
   // above log2(TPR)), then over the 4 wavefronts

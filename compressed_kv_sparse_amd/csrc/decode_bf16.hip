@@ -208,12 +208,20 @@ __host__ __device__ inline WsLayout ws_layout(void* ws, int batch, int hkv, int 
   return w;
 }
 
+// Workgroup w runs on XCD w % 8 (round-robin dispatch).  The splits of one
+// (sequence, KV head) unit get ids xcd + 8 (split + max_splits g), unit =
+// xcd + 8 g: they share an XCD and its L2 (the query rows are fetched from
+// HBM once) and are dispatched close together.
 __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a, int tps, int max_splits) {
   __shared__ __attribute__((aligned(16))) char kv0_s[NT * KSTR + NT * VSTR];
   __shared__ __attribute__((aligned(16))) char kv1_s[NT * KSTR + NT * VSTR];
   __shared__ int flag_s[2];
 
-  const int split = blockIdx.x, b = blockIdx.y, kvh = blockIdx.z;
+  const int wg = (int)blockIdx.x;
+  const int split = (wg >> 3) % max_splits;
+  const int unit_id = (wg & 7) + 8 * ((wg >> 3) / max_splits);
+  if (unit_id >= a.batch * a.hkv) return;
+  const int b = unit_id / a.hkv, kvh = unit_id % a.hkv;
   const int L = a.seqlens[b];
   const int t = L - 1;                        // the new token's position
   const int nc = L / kBlock;                  // complete blocks: 128(j+1) <= t+1
@@ -281,15 +289,13 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a, int t
 
 // Merge of the split partials: O = sum_s 2^(m_s - M) l_s O_s / sum_s 2^(m_s - M) l_s
 // with M = max_s m_s, splits taken in order (deterministic).  One workgroup
-// of 256 threads merges kMergeRows heads of one (sequence, KV head); each
-// thread owns 8 columns of one head and issues its split loads independently.
-constexpr int kMergeRows = 4;
-
+// of 256 threads merges two heads of one (sequence, KV head); each thread
+// owns 4 columns of one head and issues its split loads independently.
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int tps, int max_splits) {
   const int unit = blockIdx.y;  // b * Hkv + kvh
   const int b = unit / a.hkv, kvh = unit % a.hkv;
-  const int r = blockIdx.x * kMergeRows + (threadIdx.x >> 6);  // head within the KV group
-  const int c = (threadIdx.x & 63) * 8;
+  const int r = blockIdx.x * 2 + (threadIdx.x >> 7);  // head within the KV group
+  const int c = (threadIdx.x & 127) * 4;
   const int L = a.seqlens[b];
   const int nkeys = L / kBlock + min(a.window, L);
   const int nsplit = ((nkeys + NT - 1) / NT + tps - 1) / tps;
@@ -300,23 +306,18 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int tps
   float M = -INFINITY;
   for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, mrow[sp * G]);
   float den = 0.f;
-  f32x4 n0 = {}, n1 = {};
-#pragma unroll 4
+  f32x4 n0 = {};
+#pragma unroll 8
   for (int sp = 0; sp < nsplit; ++sp) {
     const float wgt = __builtin_amdgcn_exp2f(mrow[sp * G] - M) * lrow[sp * G];
     den += wgt;
-    const float* op = orow + (size_t)sp * G * D;
-    n0 += wgt * *(const f32x4*)op;
-    n1 += wgt * *(const f32x4*)(op + 4);
+    n0 += wgt * *(const f32x4*)(orow + (size_t)sp * G * D);
   }
   const float rden = 1.f / den;
-  bf16x8 v;
+  bf16x4 v;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[i] = (bf16)(n0[i] * rden);
-    v[4 + i] = (bf16)(n1[i] * rden);
-  }
-  *(bf16x8*)((bf16*)a.o + ((size_t)b * a.hq + kvh * G + r) * D + c) = v;
+  for (int i = 0; i < 4; ++i) v[i] = (bf16)(n0[i] * rden);
+  *(bf16x4*)((bf16*)a.o + ((size_t)b * a.hq + kvh * G + r) * D + c) = v;
 }
 
 }  // namespace
@@ -342,12 +343,12 @@ size_t decode_workspace_bytes_bf16(int batch, int hkv, int max_blocks, int windo
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
   const DecodePlan p = decode_plan(a.batch, a.hkv, a.max_blocks, a.window);
-  decode_bf16_kernel<<<dim3(p.max_splits, a.batch, a.hkv), 256, 0, s>>>(a, p.tiles_per_split,
-                                                                      p.max_splits);
+  const long groups = ((long)a.batch * a.hkv + 7) / 8;  // units per XCD slot
+  decode_bf16_kernel<<<(unsigned)(8 * p.max_splits * groups), 256, 0, s>>>(a, p.tiles_per_split,
+                                                                          p.max_splits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  decode_merge_kernel<<<dim3(G / kMergeRows, a.batch * a.hkv), 256, 0, s>>>(a, p.tiles_per_split,
-                                                                          p.max_splits);
+  decode_merge_kernel<<<dim3(G / 2, a.batch * a.hkv), 256, 0, s>>>(a, p.tiles_per_split, p.max_splits);
   return hipGetLastError();
 }
 

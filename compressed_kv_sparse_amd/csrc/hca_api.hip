@@ -59,9 +59,9 @@ hca_status hca_compress(const hca_params* params, int32_t batch, int32_t total_b
   if (st != HCA_OK) return st;
   if (batch < 0 || total_blocks < 0) return HCA_ERR_SHAPE;
   if (params->head_dim % 64) return HCA_ERR_UNSUPPORTED;
-  if ((v == nullptr) != (vc == nullptr)) return HCA_ERR_NULL;
   if ((long)total_blocks * params->num_kv_heads > 0x7fffffffL) return HCA_ERR_SHAPE;
-  if (total_blocks == 0) return HCA_OK;
+  if (total_blocks == 0) return HCA_OK;  // no output rows: any pointer may be NULL
+  if ((v == nullptr) != (vc == nullptr)) return HCA_ERR_NULL;
   if (batch == 0) return HCA_ERR_SHAPE;  // entries without sequences
   if (!cu_seqlens || !cu_blocks || !k || !w || !kc) return HCA_ERR_NULL;
   hca::CompressArgs a;

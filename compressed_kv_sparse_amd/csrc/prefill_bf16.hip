@@ -40,7 +40,8 @@
 //  * Short key lists (<= 64 keys) carry the weights as two bf16 terms
 //    P = hi + lo, lo = bf16(P - hi) (~2^-16 relative instead of 2^-9): rows
 //    that see only a few keys have few large weights whose rounding does not
-//    average out.  They take a plain per-tile loop (at most two tiles).
+//    average out.  They take a plain per-tile loop (at most two tiles) in
+//    the same launch as the pipelined pairs.
 #include "bf16_tiles.h"
 
 namespace hca {
@@ -423,26 +424,20 @@ __host__ __device__ inline int pair_keys(int t0, int t_last, int window) {
 }
 
 // ---------------------------------------------------------------------------
-// Grid (pairs, batch, Hkv), 256 threads: one position pair per workgroup,
-// pair index blockIdx.x + pair0.  LO = true handles the pairs whose key list
-// has at most kTwoTermKeys keys (two-term weights, plain loop), LO = false
-// all others (pipelined); each skips the pairs of the other kind.
+// One position pair of one (sequence, KV head), pair index bx + pair0.  LO =
+// true handles the pairs whose key list has at most kTwoTermKeys keys
+// (two-term weights, plain loop), LO = false all others (pipelined); each
+// skips the pairs of the other kind.
 // ---------------------------------------------------------------------------
 template <bool LO>
-__global__ __launch_bounds__(256, 1) void prefill_bf16_kernel(PrefillArgs a, int pair0) {
-  __shared__ __attribute__((aligned(16))) char k0_s[KTILE];
-  __shared__ __attribute__((aligned(16))) char k1_s[KTILE];
-  __shared__ __attribute__((aligned(16))) char v0_s[VTILE];
-  __shared__ __attribute__((aligned(16))) char v1_s[VTILE];
-  __shared__ __attribute__((aligned(16))) char w0_s[4 * WSLOT];
-  __shared__ __attribute__((aligned(16))) char w1_s[4 * WSLOT];
-  __shared__ int flag_s[2];
-  __shared__ float linv_s[4 * 32];
-
+__device__ __forceinline__ void prefill_body(const PrefillArgs& a, int pair0, int bx, char HCA_LDS* k0_s,
+                                             char HCA_LDS* k1_s, char HCA_LDS* v0_s, char HCA_LDS* v1_s,
+                                             char HCA_LDS* w0_s, char HCA_LDS* w1_s, int* flag_s, float* linv_s) {
   const int b = blockIdx.y, kvh = blockIdx.z;
+
   const int start = a.cu_seqlens[b];
   const int len = a.cu_seqlens[b + 1] - start;
-  const int pair = (int)blockIdx.x + pair0;
+  const int pair = bx + pair0;
   if (2 * pair >= len) return;
   {
     const int t0 = 2 * pair;
@@ -525,6 +520,29 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_kernel(PrefillArgs a, int
   store_output(c, st, linv_s, obase, row_ok);
 }
 
+// Grid (lo_n + npairs - hi_begin, batch, Hkv), 256 threads: workgroup x <
+// lo_n takes two-term pair x, the others pair hi_begin + x - lo_n.  Both
+// kinds share one launch (and one LDS layout); the branch is uniform per
+// workgroup, and the two bodies are separate inlined copies so neither
+// carries the other's register state.
+__global__ __launch_bounds__(256, 1) void prefill_bf16_kernel(PrefillArgs a, int lo_n, int hi_begin) {
+  __shared__ __attribute__((aligned(16))) char k0_s[KTILE];
+  __shared__ __attribute__((aligned(16))) char k1_s[KTILE];
+  __shared__ __attribute__((aligned(16))) char v0_s[VTILE];
+  __shared__ __attribute__((aligned(16))) char v1_s[VTILE];
+  __shared__ __attribute__((aligned(16))) char w0_s[4 * WSLOT];
+  __shared__ __attribute__((aligned(16))) char w1_s[4 * WSLOT];
+  __shared__ int flag_s[2];
+  __shared__ float linv_s[4 * 32];
+#define HCA_LDS_ARGS (char HCA_LDS*)k0_s, (char HCA_LDS*)k1_s, (char HCA_LDS*)v0_s, (char HCA_LDS*)v1_s, \
+    (char HCA_LDS*)w0_s, (char HCA_LDS*)w1_s, flag_s, linv_s
+  if ((int)blockIdx.x < lo_n)
+    prefill_body<true>(a, 0, blockIdx.x, HCA_LDS_ARGS);
+  else
+    prefill_body<false>(a, hi_begin, blockIdx.x - lo_n, HCA_LDS_ARGS);
+#undef HCA_LDS_ARGS
+}
+
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
@@ -532,7 +550,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
   // Key counts grow with the pair index, so the two-term pairs are a prefix
   // of every sequence: pairs [0, lo_end) may be two-term (a lone last
   // position has one key less than a full pair), pairs [hi_begin, npairs)
-  // may be not; each kernel checks every pair it is given.
+  // may be not; each body checks every pair it is given.
   auto first_over = [&](bool lone) {  // first pair with more than kTwoTermKeys keys
     int lo = 0, hi = npairs;
     while (lo < hi) {
@@ -545,13 +563,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
     return lo;
   };
   const int lo_end = first_over(true), hi_begin = first_over(false);
-  if (lo_end > 0) {
-    prefill_bf16_kernel<true><<<dim3(lo_end, a.batch, a.hkv), 256, 0, s>>>(a, 0);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (hi_begin < npairs)
-    prefill_bf16_kernel<false><<<dim3(npairs - hi_begin, a.batch, a.hkv), 256, 0, s>>>(a, hi_begin);
+  prefill_bf16_kernel<<<dim3(lo_end + npairs - hi_begin, a.batch, a.hkv), 256, 0, s>>>(a, lo_end, hi_begin);
   return hipGetLastError();
 }
 

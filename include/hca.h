@@ -88,6 +88,8 @@ typedef struct hca_params {
  *   k, v            device [N_tok, Hkv, d] raw keys / values; v may be NULL
  *   w               device fp32 [Hkv, 128] pooling logits
  *   kc, vc          device [total_blocks, Hkv, d] outputs; vc NULL iff v NULL
+ *                   (with total_blocks == 0 nothing is read or written and
+ *                   every pointer may be NULL)
  *
  * Entry cu_blocks[b]+j, head h = sum_i softmax(w_h)_i * x[cu_seqlens[b]+128j+i, h]
  * accumulated in fp32.  A trailing partial block is not pooled.

@@ -87,6 +87,9 @@ def test_compress_validation(lib):
     assert _compress(lib, _p(), w=NULL) == ERR_NULL
     assert _compress(lib, _p(), batch=0) == ERR_SHAPE        # entries without sequences
     assert _compress(lib, _p(), total_blocks=0) == OK        # nothing to do: no launch
+    # sequences shorter than one block: empty outputs may come as NULL
+    assert _compress(lib, _p(), total_blocks=0, kc=NULL, vc=NULL) == OK
+    assert _compress(lib, _p(), batch=0, total_blocks=0, cu=NULL, cub=NULL) == OK
 
 
 def test_prefill_validation(lib):

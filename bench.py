@@ -220,10 +220,27 @@ def cpu_baseline_decode(c, inp, seconds):
             "kind": "oracle", "sample": f"{done} of {len(lens)} queries in {t_all:.1f} s"}
 
 
+def warm_up(torch, step, warmup, min_s):
+    """W untimed steps, continued until at least min_s seconds of GPU work have
+    run: the clocks of an idle GPU take tens of milliseconds to ramp, and a
+    few short steps would leave the timed region on cold clocks.  Returns the
+    number of warmup steps run."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or time.perf_counter() - t0 < min_s:
+        step(n)
+        n += 1
+        if n >= warmup and n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
 # ---------------------------------------------------------------------------
 # workloads
 # ---------------------------------------------------------------------------
-def run_prefill(torch, hca, c, steps, warmup, clock, lens=None):
+def run_prefill(torch, hca, c, steps, warmup, clock, min_warm_s, lens=None):
     from hca_workloads import prefill_inputs
 
     inp = prefill_inputs(c, "cuda", lens=lens)
@@ -241,19 +258,17 @@ def run_prefill(torch, hca, c, steps, warmup, clock, lens=None):
                                                             inp["max_seqlen"], inp["q"], inp["k"],
                                                             inp["v"], kc, vc, o=o))
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    nwarm = warm_up(torch, lambda i: step(), warmup, min_warm_s)
     clock.reset()
     t0 = time.perf_counter()
     for _ in range(steps):
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return inp, wall
+    return inp, wall, nwarm
 
 
-def run_decode(torch, hca, c, steps, warmup, clock, n_sets=4):
+def run_decode(torch, hca, c, steps, warmup, clock, min_warm_s, n_sets=4):
     """Rotates n_sets independent caches so repeats do not hit in the 256 MiB
     last-level cache."""
     from hca_workloads import decode_inputs
@@ -270,16 +285,14 @@ def run_decode(torch, hca, c, steps, warmup, clock, n_sets=4):
                                                           s["kw"], s["vw"], workspace=ws[i % n_sets],
                                                           o=outs[i % n_sets]))
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
+    nwarm = warm_up(torch, step, warmup, min_warm_s)
     clock.reset()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(i)
+        step(nwarm + i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return sets[0], wall
+    return sets[0], wall, nwarm
 
 
 def main():
@@ -287,6 +300,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--min-warmup-s", type=float, default=0.3,
+                    help="continue the warmup until this much GPU time has run (clock ramp)")
     ap.add_argument("--workload", default="prefill_8k", choices=WORKLOADS)
     ap.add_argument("--no-decode", action="store_true", help="skip the decode_64x128k companion")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -331,7 +346,8 @@ def main():
 
     if c.has_prefill:
         log(f"[bench] {c.name}: prefill lens={list(c.prefill_lens)} steps={args.steps}")
-        inp, wall = run_prefill(torch, hca, c, args.steps, args.warmup, clock)
+        inp, wall, nwarm = run_prefill(torch, hca, c, args.steps, args.warmup, clock, args.min_warmup_s)
+        result["warmup_steps_run"] = nwarm
         lens = inp["lens"]
         pb, pf = prefill_work(c, lens, e)
         cb, cf = compress_work(c, lens, e)
@@ -365,14 +381,14 @@ def main():
     if dcfg is not None:
         log(f"[bench] {dcfg.name}: decode steps={args.steps}")
         clock.reset()
-        dinp, dwall = run_decode(torch, hca, dcfg, args.steps, args.warmup, clock)
+        dinp, dwall, dwarm = run_decode(torch, hca, dcfg, args.steps, args.warmup, clock, args.min_warmup_s)
         db, df = decode_work(dcfg, dinp["lens"], 2)
         t_dec = clock.mean_ms("decode")
         kernels["decode"] = roofline("decode", dcfg.name, db, df, t_dec, "hbm")
         dec = {"workload": dcfg.name, "queries_per_s": round(len(dinp["lens"]) / (t_dec * 1e-3), 1),
                "unit": "queries/s", "ms_per_call": round(t_dec, 5), "batch": len(dinp["lens"]),
                "context_lens": dinp["lens"] if len(dinp["lens"]) <= 8 else f"{dinp['lens'][0]} each",
-               "roofline": kernels["decode"]}
+               "warmup_steps_run": dwarm, "roofline": kernels["decode"]}
         if not args.no_cpu_baseline:
             dec["cpu_baseline"] = cpu_baseline_decode(dcfg, dinp, min(10.0, args.cpu_seconds))
         if c.has_prefill:

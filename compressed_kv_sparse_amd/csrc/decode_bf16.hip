@@ -289,12 +289,18 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a, int t
 
 // Merge of the split partials: O = sum_s 2^(m_s - M) l_s O_s / sum_s 2^(m_s - M) l_s
 // with M = max_s m_s, splits taken in order (deterministic).  One workgroup
-// of 256 threads merges two heads of one (sequence, KV head); each thread
-// owns 4 columns of one head and issues its split loads independently.
+// of 256 threads merges two heads of one (sequence, KV head) unit; each
+// thread owns 4 columns of one head.  Splits are read kMergeBatch at a time
+// with all loads of a batch in flight together; the merge of unit u runs on
+// XCD u % 8 like its split workgroups, whose L2 may still hold the partials.
+constexpr int kMergeBatch = 8;
+
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int tps, int max_splits) {
-  const int unit = blockIdx.y;  // b * Hkv + kvh
+  const int wg = (int)blockIdx.x;
+  const int unit = (wg & 7) + 8 * ((wg >> 3) / (G / 2));  // b * Hkv + kvh
+  if (unit >= a.batch * a.hkv) return;
   const int b = unit / a.hkv, kvh = unit % a.hkv;
-  const int r = blockIdx.x * 2 + (threadIdx.x >> 7);  // head within the KV group
+  const int r = ((wg >> 3) % (G / 2)) * 2 + (threadIdx.x >> 7);  // head within the KV group
   const int c = (threadIdx.x & 127) * 4;
   const int L = a.seqlens[b];
   const int nkeys = L / kBlock + min(a.window, L);
@@ -303,15 +309,37 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int tps
   const float* mrow = w.m + (size_t)unit * max_splits * G + r;
   const float* lrow = w.l + (size_t)unit * max_splits * G + r;
   const float* orow = w.o + ((size_t)unit * max_splits * G + r) * D + c;
-  float M = -INFINITY;
-  for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, mrow[sp * G]);
-  float den = 0.f;
+  // running M with rescaling between batches (exact when one batch covers
+  // all splits, as in the common case)
+  float M = -INFINITY, den = 0.f;
   f32x4 n0 = {};
-#pragma unroll 8
-  for (int sp = 0; sp < nsplit; ++sp) {
-    const float wgt = __builtin_amdgcn_exp2f(mrow[sp * G] - M) * lrow[sp * G];
-    den += wgt;
-    n0 += wgt * *(const f32x4*)(orow + (size_t)sp * G * D);
+  for (int s0 = 0; s0 < nsplit; s0 += kMergeBatch) {
+    float mv[kMergeBatch], lv[kMergeBatch];
+    f32x4 ov[kMergeBatch];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const int sp = min(s0 + j, nsplit - 1);  // repeats of the last split are dropped below
+      mv[j] = mrow[(size_t)sp * G];
+      lv[j] = lrow[(size_t)sp * G];
+      ov[j] = *(const f32x4*)(orow + (size_t)sp * G * D);
+    }
+    float Mb = M;
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j)
+      if (s0 + j < nsplit) Mb = fmaxf(Mb, mv[j]);
+    if (Mb != M) {  // rescale what earlier batches added
+      const float f = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mb);
+      den *= f;
+      n0 *= f;
+      M = Mb;
+    }
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      if (s0 + j >= nsplit) break;
+      const float wgt = __builtin_amdgcn_exp2f(mv[j] - M) * lv[j];
+      den += wgt;
+      n0 += wgt * ov[j];
+    }
   }
   const float rden = 1.f / den;
   bf16x4 v;
@@ -348,7 +376,7 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
                                                                           p.max_splits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  decode_merge_kernel<<<dim3(G / 2, a.batch * a.hkv), 256, 0, s>>>(a, p.tiles_per_split, p.max_splits);
+  decode_merge_kernel<<<(unsigned)(8 * (G / 2) * groups), 256, 0, s>>>(a, p.tiles_per_split, p.max_splits);
   return hipGetLastError();
 }
 

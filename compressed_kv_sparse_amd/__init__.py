@@ -13,11 +13,16 @@ from .hca import (  # noqa: F401
     HcaParams,
     hca_attend_decode,
     hca_attend_prefill,
+    hca_attend_prefill_chunk,
     hca_compress,
+    hca_compress_chunk,
     hca_decode_workspace_bytes,
+    hca_prefill_chunk_workspace_bytes,
+    hca_ring_append,
     hca_status_string,
     hca_version,
     library,
     make_params,
     new_decode_workspace,
+    new_prefill_chunk_workspace,
 )

@@ -50,15 +50,19 @@ __device__ __forceinline__ void fold(Running& r, const float* qv, const float* k
 __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
   const int lane = threadIdx.x;
   const int qh = blockIdx.x % a.hq;
-  const int t = blockIdx.x / a.hq;          // position within the sequence
+  const int i = blockIdx.x / a.hq;          // query row within the sequence (chunk)
   const int b = blockIdx.y;
   const int start = a.cu_seqlens[b];
-  if (t >= a.cu_seqlens[b + 1] - start) return;
+  if (i >= a.cu_seqlens[b + 1] - start) return;
+  const int p0 = a.pos0 ? a.pos0[b] : 0;
+  const int t = p0 + i;                     // its position
   const int g = a.hq / a.hkv, kvh = qh / g;
   const size_t rs = (size_t)a.hkv * a.d;   // elements between raw/compressed rows
-  const float* q = (const float*)a.q + ((size_t)(start + t) * a.hq + qh) * a.d;
-  const float* k = (const float*)a.k + (size_t)start * rs + (size_t)kvh * a.d;
-  const float* v = (const float*)a.v + (size_t)start * rs + (size_t)kvh * a.d;
+  const float* q = (const float*)a.q + ((size_t)(start + i) * a.hq + qh) * a.d;
+  // raw row of position s: start + b * halo + s - (p0 - halo)
+  const long raw0 = (long)start + (long)b * a.halo - (p0 - a.halo);
+  const float* k = (const float*)a.k + (size_t)kvh * a.d;
+  const float* v = (const float*)a.v + (size_t)kvh * a.d;
   const float* kc = (const float*)a.kc + (size_t)a.cu_blocks[b] * rs + (size_t)kvh * a.d;
   const float* vc = (const float*)a.vc + (size_t)a.cu_blocks[b] * rs + (size_t)kvh * a.d;
 
@@ -75,9 +79,9 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
   for (int j = 0; j < n; ++j) fold(r, qv, kc + (size_t)j * rs, vc + (size_t)j * rs, a.d, lane, a.scale);
   // raw window max(0, t-W+1) .. t
   for (int s = max(0, t - a.window + 1); s <= t; ++s)
-    fold(r, qv, k + (size_t)s * rs, v + (size_t)s * rs, a.d, lane, a.scale);
+    fold(r, qv, k + (size_t)(raw0 + s) * rs, v + (size_t)(raw0 + s) * rs, a.d, lane, a.scale);
 
-  float* o = (float*)a.o + ((size_t)(start + t) * a.hq + qh) * a.d;
+  float* o = (float*)a.o + ((size_t)(start + i) * a.hq + qh) * a.d;
   const float inv = 1.f / r.l;
 #pragma unroll
   for (int i = 0; i < kMaxPerLane; ++i) {

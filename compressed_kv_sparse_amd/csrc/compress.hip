@@ -11,12 +11,18 @@
 //     workgroup keeps 128 rows x CW elements in flight over a few passes;
 //   - fp32 partial sums are reduced first across the rows held by one
 //     wavefront (lane shuffles) and then across the 4 wavefronts through LDS.
+//
+// Chunk mode (CHUNK = true) pools the blocks that n new rows at positions
+// p0 .. p0+n-1 of a sequence complete: block j with p0 <= 128j+127 <= p0+n-1.
+// Its rows at positions >= p0 are the new rows; the earlier ones (at most
+// 127) come from the sequence's raw ring, where position s sits in slot
+// s % ring_cap.  The entry goes to index cu_blocks[b] + j of the cache.
 #include "hca_internal.h"
 
 namespace hca {
 namespace {
 
-template <typename T, int TPR>
+template <typename T, int TPR, bool CHUNK>
 __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a, int cw) {
   constexpr int VEC = 16 / sizeof(T);     // elements per 16-byte load
   constexpr int RPP = 256 / TPR;          // rows per pass
@@ -29,9 +35,33 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a, int cw) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int entry_head = blockIdx.x;              // entry * hkv + head
   const int h = entry_head % a.hkv;
-  const int entry = entry_head / a.hkv;
   const int c0 = blockIdx.y * cw;                 // first column of the slice
   const int which = blockIdx.z;                   // 0: K -> Kc, 1: V -> Vc
+  const size_t rstride = (size_t)a.hkv * a.d;     // elements between tokens
+  int entry, seq, j;                              // output entry; its sequence and block
+  if (CHUNK) {
+    // blockIdx.x = (b * max_new + x) * hkv + h: the x-th block completed by
+    // sequence b's new rows, if there is one
+    const int bx = entry_head / a.hkv;
+    seq = bx / a.max_new;
+    const int p0 = a.pos0[seq];
+    const int n = a.cu_seqlens[seq + 1] - a.cu_seqlens[seq];
+    j = p0 / kBlock + bx % a.max_new;
+    // not completed by these rows, or past the sequence's cache capacity:
+    // the whole workgroup leaves
+    if (kBlock * (j + 1) > p0 + n || j >= a.cu_blocks[seq + 1] - a.cu_blocks[seq]) return;
+    entry = a.cu_blocks[seq] + j;
+  } else {
+    entry = entry_head / a.hkv;
+    // which sequence owns this entry: largest b with cu_blocks[b] <= entry
+    int lo = 0, hi = a.batch;  // invariant: cu_blocks[lo] <= entry < cu_blocks[hi]
+    while (hi - lo > 1) {
+      int mid = (lo + hi) >> 1;
+      if (a.cu_blocks[mid] <= entry) lo = mid; else hi = mid;
+    }
+    seq = lo;
+    j = entry - a.cu_blocks[lo];
+  }
 
   // pooling weights p = softmax(w_h), max-subtracted, in fp32
   float wv = tid < kBlock ? a.w[h * kBlock + tid] : -INFINITY;
@@ -49,17 +79,7 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a, int cw) {
   sm = stat_s[0] + stat_s[1] + stat_s[2] + stat_s[3];
   if (tid < kBlock) p_s[tid] = e / sm;
 
-  // which sequence owns this entry: largest b with cu_blocks[b] <= entry
-  int lo = 0, hi = a.batch;  // invariant: cu_blocks[lo] <= entry < cu_blocks[hi]
-  while (hi - lo > 1) {
-    int mid = (lo + hi) >> 1;
-    if (a.cu_blocks[mid] <= entry) lo = mid; else hi = mid;
-  }
-  const int j = entry - a.cu_blocks[lo];
-  const size_t tok0 = (size_t)a.cu_seqlens[lo] + (size_t)kBlock * j;
-  const size_t rstride = (size_t)a.hkv * a.d;     // elements between tokens
-  const T* x = (const T*)a.x[which] + tok0 * rstride + (size_t)h * a.d + c0 +
-               (tid % TPR) * VEC;
+  const size_t col = (size_t)h * a.d + c0 + (tid % TPR) * VEC;  // this thread's first element in a row
   const int r0 = tid / TPR;
   __syncthreads();
 
@@ -68,8 +88,23 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a, int cw) {
   // for each load before issuing the next)
   typedef T vec_t __attribute__((ext_vector_type(VEC)));
   vec_t xv[PASSES];
+  if (CHUNK) {
+    const int p0 = a.pos0[seq], tok0 = a.cu_seqlens[seq];
+    const T* xnew = (const T*)a.x[which] + col;
+    const T* ring = (const T*)a.ring[which] + col;
 #pragma unroll
-  for (int ps = 0; ps < PASSES; ++ps) xv[ps] = *(const vec_t*)(x + (size_t)(ps * RPP + r0) * rstride);
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int pos = kBlock * j + ps * RPP + r0;
+      const bool is_new = pos >= p0;
+      const size_t row = is_new ? (size_t)(tok0 + (pos - p0)) : (size_t)seq * a.ring_cap + pos % a.ring_cap;
+      xv[ps] = *(const vec_t*)((is_new ? xnew : ring) + row * rstride);
+    }
+  } else {
+    const size_t tok0 = (size_t)a.cu_seqlens[seq] + (size_t)kBlock * j;
+    const T* x = (const T*)a.x[which] + tok0 * rstride + col;
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) xv[ps] = *(const vec_t*)(x + (size_t)(ps * RPP + r0) * rstride);
+  }
   __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of their uses
   float acc[VEC];
 #pragma unroll
@@ -99,12 +134,12 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a, int cw) {
   }
 }
 
-template <typename T>
+template <typename T, bool CHUNK>
 hipError_t launch_typed(const CompressArgs& a, hipStream_t s) {
   constexpr int VEC = 16 / sizeof(T);
   // Largest column slice (at most 64 threads x 16 bytes per row, dividing d)
   // that still gives at least ~1024 workgroups; never below 64 elements.
-  const long work = (long)a.total_blocks * a.hkv * (a.x[1] ? 2 : 1);
+  const long work = (long)a.total_blocks * a.hkv * (a.x[1] ? 2 : 1);  // chunk mode: an upper bound
   int cw = 64;
   for (int c = 64 * VEC; c >= 64; c >>= 1) {
     if (a.d % c) continue;
@@ -114,10 +149,10 @@ hipError_t launch_typed(const CompressArgs& a, hipStream_t s) {
   dim3 grid(a.total_blocks * a.hkv, a.d / cw, a.x[1] ? 2 : 1);
   const int tpr = cw / VEC;
   switch (tpr) {
-    case 64: compress_kernel<T, 64><<<grid, 256, 0, s>>>(a, cw); break;
-    case 32: compress_kernel<T, 32><<<grid, 256, 0, s>>>(a, cw); break;
-    case 16: compress_kernel<T, 16><<<grid, 256, 0, s>>>(a, cw); break;
-    case 8: compress_kernel<T, 8><<<grid, 256, 0, s>>>(a, cw); break;
+    case 64: compress_kernel<T, 64, CHUNK><<<grid, 256, 0, s>>>(a, cw); break;
+    case 32: compress_kernel<T, 32, CHUNK><<<grid, 256, 0, s>>>(a, cw); break;
+    case 16: compress_kernel<T, 16, CHUNK><<<grid, 256, 0, s>>>(a, cw); break;
+    case 8: compress_kernel<T, 8, CHUNK><<<grid, 256, 0, s>>>(a, cw); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -126,7 +161,13 @@ hipError_t launch_typed(const CompressArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_compress(int dtype, const CompressArgs& a, hipStream_t s) {
-  return dtype == 1 ? launch_typed<bf16>(a, s) : launch_typed<float>(a, s);
+  return dtype == 1 ? launch_typed<bf16, false>(a, s) : launch_typed<float, false>(a, s);
+}
+
+// Chunk mode: a.total_blocks = batch * max_new candidate blocks (the grid),
+// most of them possibly empty.
+hipError_t launch_compress_chunk(int dtype, const CompressArgs& a, hipStream_t s) {
+  return dtype == 1 ? launch_typed<bf16, true>(a, s) : launch_typed<float, true>(a, s);
 }
 
 }  // namespace hca

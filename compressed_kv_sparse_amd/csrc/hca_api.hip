@@ -34,6 +34,16 @@ bool mfma_shape(const hca_params* p) {
 
 hca_status from_hip(hipError_t e) { return e == hipSuccess ? HCA_OK : HCA_ERR_HIP; }
 
+int elem_bytes(const hca_params* p) { return p->dtype == HCA_BF16 ? 2 : 4; }
+
+// Bytes of one staged plane (K or V) of a chunk call: every sequence's
+// window - 1 halo rows plus its new rows, 256-byte aligned.
+size_t staged_plane_bytes(const hca_params* p, int32_t batch, int32_t total_rows) {
+  const size_t rows = (size_t)total_rows + (size_t)batch * (size_t)(p->window - 1);
+  const size_t bytes = rows * (size_t)p->num_kv_heads * (size_t)p->head_dim * (size_t)elem_bytes(p);
+  return (bytes + 255) / 256 * 256;
+}
+
 }  // namespace
 
 extern "C" {
@@ -64,7 +74,7 @@ hca_status hca_compress(const hca_params* params, int32_t batch, int32_t total_b
   if ((v == nullptr) != (vc == nullptr)) return HCA_ERR_NULL;
   if (batch == 0) return HCA_ERR_SHAPE;  // entries without sequences
   if (!cu_seqlens || !cu_blocks || !k || !w || !kc) return HCA_ERR_NULL;
-  hca::CompressArgs a;
+  hca::CompressArgs a{};
   a.batch = batch;
   a.total_blocks = total_blocks;
   a.hkv = params->num_kv_heads;
@@ -92,7 +102,7 @@ hca_status hca_attend_prefill(const hca_params* params, int32_t batch, int32_t m
   if (batch == 0 || max_seqlen == 0) return HCA_OK;
   if (!cu_seqlens || !cu_blocks || !q || !k || !v || !o) return HCA_ERR_NULL;
   if (max_seqlen >= hca::kBlock && (!kc || !vc)) return HCA_ERR_NULL;
-  hca::PrefillArgs a;
+  hca::PrefillArgs a{};  // whole sequences: pos0 NULL, halo 0
   a.batch = batch;
   a.max_seqlen = max_seqlen;
   a.hq = params->num_q_heads;
@@ -133,7 +143,7 @@ hca_status hca_attend_decode(const hca_params* params, int32_t batch, int32_t ma
   if (batch == 0) return HCA_OK;
   if (!seqlens || !cu_blocks || !q || !kw || !vw || !o) return HCA_ERR_NULL;
   if (max_blocks > 0 && (!kc || !vc)) return HCA_ERR_NULL;
-  hca::DecodeArgs a;
+  hca::DecodeArgs a{};
   a.batch = batch;
   a.max_blocks = max_blocks;
   a.hq = params->num_q_heads;
@@ -158,6 +168,133 @@ hca_status hca_attend_decode(const hca_params* params, int32_t batch, int32_t ma
   if (!workspace || workspace_bytes < need) return HCA_ERR_WORKSPACE;
   if (((uintptr_t)workspace) & 255) return HCA_ERR_WORKSPACE;
   return from_hip(hca::launch_decode_bf16(a, s));
+}
+
+hca_status hca_compress_chunk(const hca_params* params, int32_t batch, int32_t max_rows,
+                              const int32_t* cu_seqlens, const int32_t* pos0, const int32_t* cu_blocks,
+                              const void* k, const void* v, const float* w, const void* kw,
+                              const void* vw, int32_t ring_cap, void* kc, void* vc, void* stream) {
+  hca_status st = check_params(params);
+  if (st != HCA_OK) return st;
+  if (batch < 0 || max_rows < 0 || batch > 65535) return HCA_ERR_SHAPE;
+  if (params->head_dim % 64) return HCA_ERR_UNSUPPORTED;
+  if (ring_cap < hca::kBlock) return HCA_ERR_SHAPE;  // a straddling block's older rows
+  const long max_new = ((long)max_rows + hca::kBlock - 1) / hca::kBlock;
+  if ((long)batch * max_new * params->num_kv_heads > 0x7fffffffL) return HCA_ERR_SHAPE;
+  if (batch == 0 || max_rows == 0) return HCA_OK;
+  if ((v == nullptr) != (vc == nullptr) || (v == nullptr) != (vw == nullptr)) return HCA_ERR_NULL;
+  if (!cu_seqlens || !pos0 || !cu_blocks || !k || !w || !kw || !kc) return HCA_ERR_NULL;
+  hca::CompressArgs a{};
+  a.batch = batch;
+  a.total_blocks = (int)(batch * max_new);
+  a.hkv = params->num_kv_heads;
+  a.d = params->head_dim;
+  a.cu_seqlens = cu_seqlens;
+  a.cu_blocks = cu_blocks;
+  a.x[0] = k;
+  a.x[1] = v;
+  a.xc[0] = kc;
+  a.xc[1] = vc;
+  a.w = w;
+  a.pos0 = pos0;
+  a.ring[0] = kw;
+  a.ring[1] = vw;
+  a.ring_cap = ring_cap;
+  a.max_new = (int)max_new;
+  return from_hip(hca::launch_compress_chunk(params->dtype, a, (hipStream_t)stream));
+}
+
+hca_status hca_ring_append(const hca_params* params, int32_t batch, int32_t max_rows,
+                           const int32_t* cu_seqlens, const int32_t* pos0, const void* k, const void* v,
+                           void* kw, void* vw, int32_t ring_cap, void* stream) {
+  hca_status st = check_params(params);
+  if (st != HCA_OK) return st;
+  if (batch < 0 || max_rows < 0 || batch > 65535 || ring_cap < 1) return HCA_ERR_SHAPE;
+  if (params->head_dim % 64) return HCA_ERR_UNSUPPORTED;
+  if (batch == 0 || max_rows == 0) return HCA_OK;
+  if ((v == nullptr) != (vw == nullptr)) return HCA_ERR_NULL;
+  if (!cu_seqlens || !pos0 || !k || !kw) return HCA_ERR_NULL;
+  hca::ChunkRowsArgs a{};
+  a.batch = batch;
+  a.max_rows = max_rows;
+  a.row_elems = params->num_kv_heads * params->head_dim;
+  a.elem_bytes = elem_bytes(params);
+  a.ring_cap = ring_cap;
+  a.cu_seqlens = cu_seqlens;
+  a.pos0 = pos0;
+  a.x[0] = k;
+  a.x[1] = v;
+  a.ring[0] = kw;
+  a.ring[1] = vw;
+  return from_hip(hca::launch_ring_append(a, (hipStream_t)stream));
+}
+
+size_t hca_prefill_chunk_workspace_bytes(const hca_params* params, int32_t batch, int32_t total_rows) {
+  if (check_params(params) != HCA_OK || batch < 0 || total_rows < 0) return 0;
+  return 2 * staged_plane_bytes(params, batch, total_rows);
+}
+
+hca_status hca_attend_prefill_chunk(const hca_params* params, int32_t batch, int32_t max_seqlen,
+                                    int32_t total_rows, const int32_t* cu_seqlens, const int32_t* pos0,
+                                    const int32_t* cu_blocks, const void* q, const void* k, const void* v,
+                                    const void* kc, const void* vc, const void* kw, const void* vw,
+                                    int32_t ring_cap, void* o, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  hca_status st = check_params(params);
+  if (st != HCA_OK) return st;
+  if (batch < 0 || max_seqlen < 0 || total_rows < 0 || batch > 65535) return HCA_ERR_SHAPE;
+  if (ring_cap < params->window) return HCA_ERR_SHAPE;
+  if (params->head_dim % 64) return HCA_ERR_UNSUPPORTED;
+  if (params->dtype == HCA_BF16 && !mfma_shape(params)) return HCA_ERR_UNSUPPORTED;
+  if (params->dtype == HCA_F32 && (long)max_seqlen * params->num_q_heads > 0x7fffffffL)
+    return HCA_ERR_SHAPE;
+  const long halo = params->window - 1;
+  if (((long)total_rows + (long)batch * halo) * params->num_kv_heads * params->head_dim * elem_bytes(params) >
+      0xffffffffL)
+    return HCA_ERR_SHAPE;  // staged rows are addressed with 32-bit buffer offsets
+  if (batch == 0 || max_seqlen == 0 || total_rows == 0) return HCA_OK;
+  if (!cu_seqlens || !pos0 || !cu_blocks || !q || !k || !v || !kc || !vc || !kw || !vw || !o)
+    return HCA_ERR_NULL;
+  const size_t plane = staged_plane_bytes(params, batch, total_rows);
+  if (!workspace || workspace_bytes < 2 * plane || (((uintptr_t)workspace) & 255)) return HCA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  hca::ChunkRowsArgs c{};
+  c.batch = batch;
+  c.max_rows = max_seqlen;
+  c.row_elems = params->num_kv_heads * params->head_dim;
+  c.elem_bytes = elem_bytes(params);
+  c.ring_cap = ring_cap;
+  c.halo = (int)halo;
+  c.cu_seqlens = cu_seqlens;
+  c.pos0 = pos0;
+  c.x[0] = k;
+  c.x[1] = v;
+  c.ring[0] = const_cast<void*>(kw);  // only read by the staging copy
+  c.ring[1] = const_cast<void*>(vw);
+  c.stage[0] = workspace;
+  c.stage[1] = (char*)workspace + plane;
+  hipError_t e = hca::launch_stage_chunk(c, s);
+  if (e != hipSuccess) return from_hip(e);
+  hca::PrefillArgs a{};
+  a.batch = batch;
+  a.max_seqlen = max_seqlen;
+  a.hq = params->num_q_heads;
+  a.hkv = params->num_kv_heads;
+  a.d = params->head_dim;
+  a.window = params->window;
+  a.scale = scale_of(params);
+  a.cu_seqlens = cu_seqlens;
+  a.cu_blocks = cu_blocks;
+  a.q = q;
+  a.k = c.stage[0];
+  a.v = c.stage[1];
+  a.kc = kc;
+  a.vc = vc;
+  a.o = o;
+  a.pos0 = pos0;
+  a.halo = (int)halo;
+  return from_hip(params->dtype == HCA_BF16 ? hca::launch_prefill_bf16(a, s)
+                                            : hca::launch_prefill_f32(a, s));
 }
 
 }  // extern "C"

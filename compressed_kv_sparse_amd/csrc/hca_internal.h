@@ -48,8 +48,14 @@ struct CompressArgs {
   const void* x[2];  // K, V (x[1] may be null)
   void* xc[2];       // Kc, Vc
   const float* w;
+  // chunk mode only: position of each sequence's first new row, the raw
+  // rings [B, ring_cap, Hkv, d] and the most blocks one sequence completes
+  const int* pos0;
+  const void* ring[2];
+  int ring_cap, max_new;
 };
 hipError_t launch_compress(int dtype, const CompressArgs& a, hipStream_t s);
+hipError_t launch_compress_chunk(int dtype, const CompressArgs& a, hipStream_t s);
 
 struct PrefillArgs {
   int batch, max_seqlen, hq, hkv, d, window;
@@ -62,9 +68,32 @@ struct PrefillArgs {
   const void* kc;
   const void* vc;
   void* o;
+  // Chunks of longer sequences: query row i of sequence b sits at position
+  // pos0[b] + i (pos0 NULL: 0).  The raw rows of sequence b start at row
+  // cu_seqlens[b] + b * halo of k / v and hold positions pos0[b] - halo
+  // onward (halo raw rows precede each chunk; 0 for whole sequences).
+  const int* pos0;
+  int halo;
 };
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
+
+// Chunk support (chunk.hip).  Rows: cu_seqlens [B+1] counts the new rows
+// of each sequence, pos0 [B] their first position; rings [B, ring_cap, Hkv,
+// d] hold position s in slot s % ring_cap.
+struct ChunkRowsArgs {
+  int batch, max_rows, row_elems, elem_bytes, ring_cap, halo;
+  const int* cu_seqlens;
+  const int* pos0;
+  const void* x[2];   // new K, V rows [N, Hkv, d]
+  void* ring[2];      // raw rings (read by the staging copy, written by the append)
+  void* stage[2];     // staged K, V rows (see PrefillArgs)
+};
+// Copy the halo rows (from the rings) and the new rows of every sequence
+// into the staging buffers.
+hipError_t launch_stage_chunk(const ChunkRowsArgs& a, hipStream_t s);
+// Write the last min(n, ring_cap) new rows of every sequence into its ring.
+hipError_t launch_ring_append(const ChunkRowsArgs& a, hipStream_t s);
 
 struct DecodeArgs {
   int batch, max_blocks, hq, hkv, d, window, ring;

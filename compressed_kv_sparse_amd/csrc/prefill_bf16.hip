@@ -436,22 +436,24 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, int pair0, in
   const int b = blockIdx.y, kvh = blockIdx.z;
 
   const int start = a.cu_seqlens[b];
-  const int len = a.cu_seqlens[b + 1] - start;
+  const int len = a.cu_seqlens[b + 1] - start;  // query rows (positions p0 .. p0+len-1)
   const int pair = bx + pair0;
   if (2 * pair >= len) return;
+  const int p0 = a.pos0 ? a.pos0[b] : 0;
   {
-    const int t0 = 2 * pair;
-    const int t_last = t0 + 1 < len ? t0 + 1 : t0;
+    const int t0 = p0 + 2 * pair;
+    const int t_last = 2 * pair + 1 < len ? t0 + 1 : t0;
     if ((pair_keys(t0, t_last, a.window) <= kTwoTermKeys) != LO) return;
   }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int pw = wave >> 1, hg = wave & 1;
-  const int t0 = 2 * pair;
-  const bool t1_ok = t0 + 1 < len;
+  const bool t1_ok = 2 * pair + 1 < len;
+  const int t0 = p0 + 2 * pair;  // positions
   const int t_last = t1_ok ? t0 + 1 : t0;
   const bool row_ok = pw == 0 || t1_ok;
   const int t = row_ok ? t0 + pw : t0;  // an absent second position recomputes t0
+  const int qrow = start + (t - p0);    // its query / output row
 
   const int nc = (t_last + 1) / kBlock;      // entries visible to the later position
   const int lo = max(0, t0 - a.window + 1);  // oldest raw key of the earlier position
@@ -465,12 +467,14 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, int pair0, in
     const int nb = a.cu_blocks[b + 1] - a.cu_blocks[b];
     c.ks.comp_k = make_rsrc((const char*)a.kc + (size_t)a.cu_blocks[b] * rs + head_off, (unsigned)(nb * rs));
     c.ks.comp_v = make_rsrc((const char*)a.vc + (size_t)a.cu_blocks[b] * rs + head_off, (unsigned)(nb * rs));
-    c.ks.raw_k = make_rsrc((const char*)a.k + (size_t)start * rs + head_off, (unsigned)(len * rs));
-    c.ks.raw_v = make_rsrc((const char*)a.v + (size_t)start * rs + head_off, (unsigned)(len * rs));
+    // raw rows of the sequence: positions p0 - halo onward
+    const size_t row0 = (size_t)start + (size_t)b * a.halo;
+    c.ks.raw_k = make_rsrc((const char*)a.k + row0 * rs + head_off, (unsigned)((len + a.halo) * rs));
+    c.ks.raw_v = make_rsrc((const char*)a.v + row0 * rs + head_off, (unsigned)((len + a.halo) * rs));
   }
   c.ks.nc = nc;
   c.ks.nkeys = nkeys;
-  c.ks.raw0 = lo;
+  c.ks.raw0 = lo - (p0 - a.halo);
   c.ks.ring = 0;
   c.rm.nc = nc;
   c.rm.nkeys = nkeys;
@@ -507,7 +511,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, int pair0, in
 
   // Q^T fragments of the wave's 32 rows (heads 32hg .. +31 of position t):
   // lane l holds row l%32, elements 16k + 8(l/32) .. +7
-  const bf16* qbase = (const bf16*)a.q + ((size_t)(start + t) * a.hq + kvh * G) * D;
+  const bf16* qbase = (const bf16*)a.q + ((size_t)qrow * a.hq + kvh * G) * D;
   bf16x8 qf[DSTEPS];
   {
     const bf16* qrow = qbase + (size_t)(32 * hg + (lane & 31)) * D + 8 * (lane >> 5);
@@ -516,7 +520,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, int pair0, in
   }
   PState st;
   attend_pair<LO>(c, qf, st);
-  bf16* obase = (bf16*)a.o + ((size_t)(start + t) * a.hq + kvh * G) * D + hg * 256;
+  bf16* obase = (bf16*)a.o + ((size_t)qrow * a.hq + kvh * G) * D + hg * 256;
   store_output(c, st, linv_s, obase, row_ok);
 }
 
@@ -562,7 +566,9 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
     }
     return lo;
   };
-  const int lo_end = first_over(true), hi_begin = first_over(false);
+  // Chunks start at pos0 >= 0: any of the first lo_end pairs may be of
+  // either kind, so the pipelined body also gets all of them.
+  const int lo_end = first_over(true), hi_begin = a.pos0 ? 0 : first_over(false);
   prefill_bf16_kernel<<<dim3(lo_end + npairs - hi_begin, a.batch, a.hkv), 256, 0, s>>>(a, lo_end, hi_begin);
   return hipGetLastError();
 }

@@ -21,7 +21,9 @@ LIB_PATH = os.path.join(HERE, "libhca.so")
 HCA_F32, HCA_BF16 = 0, 1
 _DTYPES = {torch.float32: HCA_F32, torch.bfloat16: HCA_BF16}
 EXPORTS = ("hca_compress", "hca_attend_prefill", "hca_decode_workspace_bytes",
-           "hca_attend_decode", "hca_status_string", "hca_version")
+           "hca_attend_decode", "hca_compress_chunk", "hca_ring_append",
+           "hca_prefill_chunk_workspace_bytes", "hca_attend_prefill_chunk",
+           "hca_status_string", "hca_version")
 
 
 class HcaLibraryMissing(ImportError):
@@ -76,6 +78,15 @@ def library() -> ctypes.CDLL:
     lib.hca_decode_workspace_bytes.restype = sz
     lib.hca_attend_decode.argtypes = [P, i32, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
     lib.hca_attend_decode.restype = ctypes.c_int
+    lib.hca_compress_chunk.argtypes = [P, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp]
+    lib.hca_compress_chunk.restype = ctypes.c_int
+    lib.hca_ring_append.argtypes = [P, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp]
+    lib.hca_ring_append.restype = ctypes.c_int
+    lib.hca_prefill_chunk_workspace_bytes.argtypes = [P, i32, i32]
+    lib.hca_prefill_chunk_workspace_bytes.restype = sz
+    lib.hca_attend_prefill_chunk.argtypes = [P, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                             i32, vp, vp, sz, vp]
+    lib.hca_attend_prefill_chunk.restype = ctypes.c_int
     lib.hca_status_string.argtypes = [ctypes.c_int]
     lib.hca_status_string.restype = ctypes.c_char_p
     lib.hca_version.argtypes = []
@@ -170,3 +181,57 @@ def hca_attend_decode(params: HcaParams, seqlens, cu_blocks, max_blocks: int, q,
 
 def default_scale(head_dim: int) -> float:
     return 1.0 / math.sqrt(head_dim)
+
+
+# ---------------------------------------------------------------------------
+# Serving with a cache: new rows at positions pos0[b] .. pos0[b] + n_b - 1.
+# ---------------------------------------------------------------------------
+def hca_compress_chunk(params: HcaParams, cu_seqlens, pos0, cu_blocks, max_rows: int, k, w, kw, kc,
+                       v=None, vw=None, vc=None, stream=None):
+    """Pool the blocks the new rows complete into kc (vc), in place."""
+    batch = pos0.numel()
+    st = library().hca_compress_chunk(ctypes.byref(params), batch, int(max_rows), _ptr(cu_seqlens),
+                                      _ptr(pos0), _ptr(cu_blocks), _ptr(k), _ptr(v), _ptr(w), _ptr(kw),
+                                      _ptr(vw), int(kw.shape[1]), _ptr(kc), _ptr(vc), _stream(stream))
+    _check("hca_compress_chunk", st)
+    return kc, vc
+
+
+def hca_ring_append(params: HcaParams, cu_seqlens, pos0, max_rows: int, k, kw, v=None, vw=None,
+                    stream=None):
+    """Write the newest rows into the rings kw (vw), in place."""
+    batch = pos0.numel()
+    st = library().hca_ring_append(ctypes.byref(params), batch, int(max_rows), _ptr(cu_seqlens),
+                                   _ptr(pos0), _ptr(k), _ptr(v), _ptr(kw), _ptr(vw), int(kw.shape[1]),
+                                   _stream(stream))
+    _check("hca_ring_append", st)
+    return kw, vw
+
+
+def hca_prefill_chunk_workspace_bytes(params: HcaParams, batch: int, total_rows: int) -> int:
+    return int(library().hca_prefill_chunk_workspace_bytes(ctypes.byref(params), int(batch),
+                                                           int(total_rows)))
+
+
+def new_prefill_chunk_workspace(params: HcaParams, batch: int, total_rows: int, device=None):
+    n = hca_prefill_chunk_workspace_bytes(params, batch, total_rows)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device or torch.cuda.current_device())
+
+
+def hca_attend_prefill_chunk(params: HcaParams, cu_seqlens, pos0, cu_blocks, max_seqlen: int, q, k, v,
+                             kc, vc, kw, vw, workspace=None, o=None, stream=None):
+    """Attention of the new rows over the cache.  Returns o [N, Hq, d]."""
+    batch = pos0.numel()
+    total = q.shape[0]
+    if o is None:
+        o = torch.empty_like(q)
+    if workspace is None:
+        workspace = new_prefill_chunk_workspace(params, batch, total, q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = library().hca_attend_prefill_chunk(ctypes.byref(params), batch, int(max_seqlen), int(total),
+                                            _ptr(cu_seqlens), _ptr(pos0), _ptr(cu_blocks), _ptr(q), _ptr(k),
+                                            _ptr(v), _ptr(kc), _ptr(vc), _ptr(kw), _ptr(vw),
+                                            int(kw.shape[1]), _ptr(o), _ptr(workspace), ws_bytes,
+                                            _stream(stream))
+    _check("hca_attend_prefill_chunk", st)
+    return o

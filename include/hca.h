@@ -154,6 +154,94 @@ HCA_API hca_status hca_attend_decode(const hca_params* params, int32_t batch, in
                              const void* kw, const void* vw, int32_t ring_cap,
                              void* o, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Serving with a cache: chunks of new tokens and decode steps.
+ *
+ * A sequence's HCA cache is its compressed entries (one per complete block,
+ * release blog, section 2.1) plus a raw ring [B, ring_cap, Hkv, d] holding
+ * position s in slot s % ring_cap (the recent raw tokens the window needs).
+ * New rows of sequence b are n_b = cu_seqlens[b+1] - cu_seqlens[b] tokens at
+ * positions pos0[b] .. pos0[b] + n_b - 1, packed in k / v [N, Hkv, d].
+ *
+ *   a chunk:        hca_compress_chunk, hca_attend_prefill_chunk, hca_ring_append
+ *   a decode step:  hca_compress_chunk and hca_ring_append with one row per
+ *                   sequence, then hca_attend_decode
+ *
+ * The ring must hold positions pos0[b] - ring_cap .. pos0[b] - 1 (those >= 0)
+ * when a call starts; hca_ring_append writes the new rows last, since the
+ * other two calls read the older rows the new ones replace.  The output of a
+ * chunk equals rows pos0[b] .. pos0[b] + n_b - 1 of hca_attend_prefill over
+ * the whole sequence.
+ */
+
+/*
+ * hca_compress_chunk - pool every block the new rows complete: block j with
+ * pos0[b] <= 128j + 127 <= pos0[b] + n_b - 1 becomes entry cu_blocks[b] + j
+ * (same arithmetic as hca_compress).  Rows of the block before pos0[b] are
+ * read from the ring, so ring_cap >= 128.
+ *
+ *   batch, max_rows  host: B and max_b n_b
+ *   cu_seqlens       device int32 [B+1], offsets of the new rows
+ *   pos0             device int32 [B], position of each sequence's first new row
+ *   cu_blocks        device int32 [B+1], cache layout: sequence b owns entries
+ *                    [cu_blocks[b], cu_blocks[b+1]), at least floor((pos0[b] + n_b)/128)
+ *   k, v             device [N, Hkv, d] new rows; v may be NULL (then vw, vc too)
+ *   w                device fp32 [Hkv, 128] pooling logits
+ *   kw, vw           device rings [B, ring_cap, Hkv, d] (read only)
+ *   kc, vc           device caches; only the completed entries are written
+ *                    (never an index past cu_blocks[b+1])
+ */
+HCA_API hca_status hca_compress_chunk(const hca_params* params, int32_t batch, int32_t max_rows,
+                              const int32_t* cu_seqlens, const int32_t* pos0,
+                              const int32_t* cu_blocks, const void* k, const void* v,
+                              const float* w, const void* kw, const void* vw, int32_t ring_cap,
+                              void* kc, void* vc, void* stream);
+
+/*
+ * hca_ring_append - write the last min(n_b, ring_cap) new rows of every
+ * sequence into its ring (position s -> slot s % ring_cap); other slots are
+ * left as they are.  Pure data movement, bit-exact.
+ *
+ *   k, v      device [N, Hkv, d] new rows; v may be NULL (then vw too)
+ *   kw, vw    device rings [B, ring_cap, Hkv, d], written
+ */
+HCA_API hca_status hca_ring_append(const hca_params* params, int32_t batch, int32_t max_rows,
+                           const int32_t* cu_seqlens, const int32_t* pos0,
+                           const void* k, const void* v, void* kw, void* vw,
+                           int32_t ring_cap, void* stream);
+
+/*
+ * hca_prefill_chunk_workspace_bytes - scratch size for hca_attend_prefill_chunk
+ * with `batch` sequences and `total_rows` = cu_seqlens[B] new rows: the
+ * window - 1 ring rows before each chunk and the chunk's rows, staged as one
+ * run per sequence (K and V).  Returns 0 for invalid params.
+ */
+HCA_API size_t hca_prefill_chunk_workspace_bytes(const hca_params* params, int32_t batch,
+                                         int32_t total_rows);
+
+/*
+ * hca_attend_prefill_chunk - HCA attention for the new rows of every
+ * sequence (queries at positions pos0[b] ..), over its cache: entries 0 ..
+ * floor((t+1)/128) - 1 (the ones completed inside the chunk must already be
+ * pooled by hca_compress_chunk) and raw tokens max(0, t-W+1) .. t, from the
+ * ring before pos0[b] and from k / v after.
+ *
+ *   batch, max_seqlen, total_rows  host: B, max_b n_b, cu_seqlens[B]
+ *   q               device [N, Hq, d]; o device [N, Hq, d] output
+ *   k, v            device [N, Hkv, d] new rows
+ *   kc, vc          device caches as for hca_compress_chunk
+ *   kw, vw          device rings, ring_cap >= window (read only)
+ *   workspace       device scratch of >= hca_prefill_chunk_workspace_bytes,
+ *                   256-byte aligned, any contents
+ */
+HCA_API hca_status hca_attend_prefill_chunk(const hca_params* params, int32_t batch,
+                                    int32_t max_seqlen, int32_t total_rows,
+                                    const int32_t* cu_seqlens, const int32_t* pos0,
+                                    const int32_t* cu_blocks, const void* q, const void* k,
+                                    const void* v, const void* kc, const void* vc,
+                                    const void* kw, const void* vw, int32_t ring_cap, void* o,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 HCA_API const char* hca_status_string(hca_status status);
 

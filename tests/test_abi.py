@@ -144,3 +144,67 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "libhca.so"))
     with pytest.raises(hca.HcaLibraryMissing):
         binding.library()
+
+
+def _compress_chunk(lib, params, batch=1, max_rows=1, ring=128, ptrs=None):
+    p = [DUMMY] * 11 if ptrs is None else ptrs
+    pp = ctypes.byref(params) if params is not None else None
+    return lib.hca_compress_chunk(pp, batch, max_rows, p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7],
+                                  ring, p[8], p[9], None)
+
+
+def _ring_append(lib, params, batch=1, max_rows=1, ring=128, ptrs=None):
+    p = [DUMMY] * 6 if ptrs is None else ptrs
+    pp = ctypes.byref(params) if params is not None else None
+    return lib.hca_ring_append(pp, batch, max_rows, p[0], p[1], p[2], p[3], p[4], p[5], ring, None)
+
+
+def _prefill_chunk(lib, params, batch=1, max_seqlen=64, total=64, ring=128, ws=DUMMY, ws_bytes=1 << 40,
+                   ptrs=None):
+    p = [DUMMY] * 10 if ptrs is None else ptrs
+    pp = ctypes.byref(params) if params is not None else None
+    return lib.hca_attend_prefill_chunk(pp, batch, max_seqlen, total, *p, ring, DUMMY, ws, ws_bytes, None)
+
+
+def test_chunk_validation(lib):
+    """Host-side checks of the serving-path entry points (nothing is launched)."""
+    assert _compress_chunk(lib, None) == ERR_NULL
+    assert _compress_chunk(lib, _p(), ring=127) == ERR_SHAPE        # a block's older rows need 128 slots
+    assert _compress_chunk(lib, _p(head_dim=100)) == ERR_UNSUPPORTED
+    assert _compress_chunk(lib, _p(), batch=-1) == ERR_SHAPE
+    assert _compress_chunk(lib, _p(), max_rows=0) == OK              # nothing to pool
+    assert _compress_chunk(lib, _p(), batch=0) == OK
+    ptrs = [DUMMY] * 11
+    ptrs[4] = NULL  # v without vw / vc
+    assert _compress_chunk(lib, _p(), ptrs=ptrs) == ERR_NULL
+    ptrs = [DUMMY] * 11
+    ptrs[1] = NULL  # pos0
+    assert _compress_chunk(lib, _p(), ptrs=ptrs) == ERR_NULL
+
+    assert _ring_append(lib, None) == ERR_NULL
+    assert _ring_append(lib, _p(), ring=0) == ERR_SHAPE
+    assert _ring_append(lib, _p(), max_rows=0) == OK
+    ptrs = [DUMMY] * 6
+    ptrs[5] = NULL  # vw without v
+    assert _ring_append(lib, _p(), ptrs=ptrs) == ERR_NULL
+
+    assert _prefill_chunk(lib, None) == ERR_NULL
+    assert _prefill_chunk(lib, _p(), ring=100) == ERR_SHAPE          # ring shorter than the window
+    assert _prefill_chunk(lib, _p(head_dim=256)) == ERR_UNSUPPORTED  # bf16 path: d == 512 only
+    assert _prefill_chunk(lib, _p(), batch=0) == OK
+    assert _prefill_chunk(lib, _p(), ws=NULL) == ERR_WORKSPACE
+    assert _prefill_chunk(lib, _p(), ws_bytes=16) == ERR_WORKSPACE
+    assert _prefill_chunk(lib, _p(), ws=ctypes.c_void_p(0x1010)) == ERR_WORKSPACE
+    ptrs = [DUMMY] * 10
+    ptrs[1] = NULL  # pos0
+    assert _prefill_chunk(lib, _p(), ptrs=ptrs) == ERR_NULL
+
+
+def test_chunk_workspace_sizes(lib):
+    p = _p()
+    # window - 1 halo rows per sequence plus the new rows, K and V, 1 KiB rows
+    assert hca.hca_prefill_chunk_workspace_bytes(p, 1, 1000) == 2 * (1000 + 127) * 1024
+    assert hca.hca_prefill_chunk_workspace_bytes(p, 3, 10) == 2 * (10 + 3 * 127) * 1024
+    assert hca.hca_prefill_chunk_workspace_bytes(p, -1, 10) == 0
+    f32 = _p(dtype=hca.HCA_F32, num_q_heads=4, head_dim=64, window=64)
+    assert hca.hca_prefill_chunk_workspace_bytes(f32, 2, 5) == 2 * (((5 + 2 * 63) * 64 * 4 + 255) // 256 * 256)

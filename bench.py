@@ -36,11 +36,16 @@ METRIC = "HCA prefill tokens/s (%MFMA peak) + decode queries/s (%HBM peak), 1 GP
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3
-WORKLOADS = ("prefill_8k", "prefill_128k", "decode_64x128k", "mixed_1m", "tiny_f32")
+WORKLOADS = ("prefill_8k", "prefill_128k", "decode_64x128k", "mixed_1m", "tiny_f32", "chunk_32k_at_224k")
+_CS = "compressed_kv_sparse_amd/csrc/"
 KERNEL_SOURCES = {
-    "prefill": ("compressed_kv_sparse_amd/csrc/prefill_bf16.hip", "compressed_kv_sparse_amd/csrc/bf16_tiles.h"),
-    "decode": ("compressed_kv_sparse_amd/csrc/decode_bf16.hip", "compressed_kv_sparse_amd/csrc/bf16_tiles.h"),
-    "compress": ("compressed_kv_sparse_amd/csrc/compress.hip",),
+    "prefill": (_CS + "prefill_bf16.hip", _CS + "bf16_tiles.h"),
+    "decode": (_CS + "decode_bf16.hip", _CS + "bf16_tiles.h"),
+    "compress": (_CS + "compress.hip",),
+    "prefill_chunk": (_CS + "chunk.hip", _CS + "prefill_bf16.hip", _CS + "bf16_tiles.h"),
+    "compress_chunk": (_CS + "compress.hip",),
+    "ring_append": (_CS + "chunk.hip",),
+    "decode_maintenance": (_CS + "compress.hip", _CS + "chunk.hip"),
 }
 
 
@@ -76,6 +81,20 @@ def prefill_work(c, lens, e):
 def compress_work(c, lens, e):
     nblk = sum(l // c.block for l in lens)
     return nblk * c.hkv * (2 * c.block * c.d * e + 2 * c.d * e), nblk * c.hkv * 4 * c.block * c.d
+
+
+def chunk_work(c, p0, n, e):
+    """(bytes, flops) of one hca_attend_prefill_chunk call: Q read + O write,
+    the chunk's raw K+V and the window-1 ring rows before it read once, every
+    visible compressed entry read once; 4*d*Hq flops per visible (query, key)
+    pair."""
+    L = p0 + n
+    byt = n * (2 * c.hq * c.d * e + 2 * c.hkv * c.d * e) + min(c.window - 1, p0) * 2 * c.hkv * c.d * e
+    byt += (L // c.block) * 2 * c.hkv * c.d * e
+    pairs = 0
+    for t in range(p0, L):
+        pairs += (t + 1) // c.block + min(c.window, t + 1)
+    return byt, pairs * 4 * c.d * c.hq
 
 
 def decode_work(c, lens, e):
@@ -136,7 +155,7 @@ def measured_traffic(kernel, workload):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_sha") != source_sha(KERNEL_SOURCES[kernel]):
+    if kernel not in KERNEL_SOURCES or kv.get("source_sha") != source_sha(KERNEL_SOURCES[kernel]):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -268,6 +287,89 @@ def run_prefill(torch, hca, c, steps, warmup, clock, min_warm_s, lens=None):
     return inp, wall, nwarm
 
 
+def run_chunk(torch, hca, c, steps, warmup, clock, min_warm_s):
+    """A continuation chunk: the cache holds the entries of the blocks before
+    pos0 and a ring of the raw rows before pos0.  One step = hca_compress_chunk
+    (the 256 blocks the chunk completes) + hca_attend_prefill_chunk +
+    hca_ring_append.  The append writes a second ring, so every step starts
+    from the same cache state and repeats the same work."""
+    from hca_workloads import chunk_inputs
+
+    ci = chunk_inputs(c, "cuda")
+    p0, n, R, L = ci["pos0"], ci["n"], c.ring, ci["length"]
+    bf = torch.bfloat16
+    p = hca.make_params(c.hq, c.hkv, c.d, c.window, bf)
+
+    def i32(x):
+        return torch.tensor(x, dtype=torch.int32, device="cuda")
+
+    cap = L // c.block
+    kc = torch.empty((cap, c.hkv, c.d), dtype=bf, device="cuda")
+    vc = torch.empty_like(kc)
+    nb0 = p0 // c.block
+    hca.hca_compress(p, i32([0, p0]), i32([0, nb0]), nb0, ci["k"][:p0], ci["w"], v=ci["v"][:p0],
+                     kc=kc[:nb0], vc=vc[:nb0])
+    slots = torch.arange(p0 - R, p0, device="cuda") % R
+    kwa = torch.zeros((1, R, c.hkv, c.d), dtype=bf, device="cuda")
+    vwa = torch.zeros_like(kwa)
+    kwa[0, slots] = ci["k"][p0 - R:p0]
+    vwa[0, slots] = ci["v"][p0 - R:p0]
+    kwb, vwb = torch.empty_like(kwa), torch.empty_like(vwa)
+    kch, vch = ci["k"][p0:L].contiguous(), ci["v"][p0:L].contiguous()
+    cu, pos0, cub = i32([0, n]), i32([p0]), i32([0, cap])
+    ws = hca.new_prefill_chunk_workspace(p, 1, n)
+    o = torch.empty_like(ci["q"])
+
+    def step(i):
+        clock.run("compress", lambda: hca.hca_compress_chunk(p, cu, pos0, cub, n, kch, ci["w"], kwa, kc, v=vch,
+                                                             vw=vwa, vc=vc))
+        clock.run("prefill", lambda: hca.hca_attend_prefill_chunk(p, cu, pos0, cub, n, ci["q"], kch, vch, kc, vc,
+                                                                  kwa, vwa, workspace=ws, o=o))
+        clock.run("ring_append", lambda: hca.hca_ring_append(p, cu, pos0, n, kch, kwb, v=vch, vw=vwb))
+
+    nwarm = warm_up(torch, step, warmup, min_warm_s)
+    clock.reset()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return ci, wall, nwarm
+
+
+def cpu_baseline_chunk(c, ci, seconds):
+    """The oracle on seeded-random query rows of the chunk, plus the pooling
+    of the 256 blocks the chunk completes, prorated per chunk token."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    p0, n, L = ci["pos0"], ci["n"], ci["length"]
+    k, v, w = ci["k"].cpu(), ci["v"].cpu(), ci["w"].cpu()
+    cu = [0, L]
+    kc = oracle.compress(k, w, cu)  # all entries (the oracle's own pooling)
+    vc = oracle.compress(v, w, cu)
+    t0 = time.perf_counter()
+    lo = p0 - p0 % c.block
+    oracle.compress(k[lo:L], w, [0, L - lo])  # the blocks the chunk completes, timed
+    oracle.compress(v[lo:L], w, [0, L - lo])
+    t_pool = time.perf_counter() - t0
+    order = np.random.default_rng(7).permutation(n)
+    done, t_att, step = 0, 0.0, 16
+    while t_att < seconds and done < n:
+        rel = sorted(int(x) for x in order[done:done + step])
+        q_rows = ci["q"].index_select(0, torch.tensor(rel, device=ci["q"].device)).cpu()
+        t1 = time.perf_counter()
+        oracle.attend_prefill(q_rows, k, v, kc, vc, cu, c.window, rows=[p0 + r for r in rel], q_holds_rows_only=True)
+        t_att += time.perf_counter() - t1
+        done += len(rel)
+    per_tok = t_att / done + t_pool / n
+    return {"value": round(1.0 / per_tok, 3), "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{done} of {n} chunk query rows (seeded random) attended in {t_att:.1f} s plus pooling "
+                      f"of the chunk's {L // c.block - p0 // c.block} blocks in {t_pool:.1f} s, prorated per token"}
+
+
 def run_decode(torch, hca, c, steps, warmup, clock, min_warm_s, n_sets=4):
     """Rotates n_sets independent caches so repeats do not hit in the 256 MiB
     last-level cache."""
@@ -278,8 +380,27 @@ def run_decode(torch, hca, c, steps, warmup, clock, min_warm_s, n_sets=4):
     ws = [hca.new_decode_workspace(p, len(s["lens"]), s["max_blocks"]) for s in sets]
     outs = [torch.empty_like(s["q"]) for s in sets]
 
+    # Cache maintenance of the step (timed apart, not part of decode): the new
+    # token's row goes through hca_compress_chunk (it completes a block when
+    # L is a multiple of 128) and hca_ring_append.  The caches already hold
+    # that token, so both rewrite what is there and every step is the same.
+    upd = []
+    for s in sets:
+        b = len(s["lens"])
+        pos = [L - 1 for L in s["lens"]]
+        slot = torch.tensor([x % s["kw"].shape[1] for x in pos], dtype=torch.long, device="cuda")
+        rows = torch.arange(b, device="cuda")
+        upd.append({"cu": torch.arange(b + 1, dtype=torch.int32, device="cuda"),
+                    "pos0": torch.tensor(pos, dtype=torch.int32, device="cuda"),
+                    "k": s["kw"][rows, slot].contiguous(), "v": s["vw"][rows, slot].contiguous(),
+                    "w": torch.randn((c.hkv, c.block), device="cuda") * c.w_std})
+
     def step(i):
-        s = sets[i % n_sets]
+        s, u = sets[i % n_sets], upd[i % n_sets]
+        clock.run("decode_maintenance", lambda: (
+            hca.hca_compress_chunk(p, u["cu"], u["pos0"], s["cu_blocks"], 1, u["k"], u["w"], s["kw"], s["kc"],
+                                   v=u["v"], vw=s["vw"], vc=s["vc"]),
+            hca.hca_ring_append(p, u["cu"], u["pos0"], 1, u["k"], s["kw"], v=u["v"], vw=s["vw"])))
         clock.run("decode", lambda: hca.hca_attend_decode(p, s["seqlens"], s["cu_blocks"],
                                                           s["max_blocks"], s["q"], s["kc"], s["vc"],
                                                           s["kw"], s["vw"], workspace=ws[i % n_sets],
@@ -344,7 +465,36 @@ def main():
               "dtype": c.dtype, "data": "synthetic (seeded random tensors of the workload's shapes)"}
     kernels = {}
 
-    if c.has_prefill:
+    if c.chunk_pos0:
+        log(f"[bench] {c.name}: chunk of {c.prefill_lens[0]} tokens at position {c.chunk_pos0}, steps={args.steps}")
+        ci, wall, nwarm = run_chunk(torch, hca, c, args.steps, args.warmup, clock, args.min_warmup_s)
+        result["warmup_steps_run"] = nwarm
+        p0, n = ci["pos0"], ci["n"]
+        pb, pf = chunk_work(c, p0, n, e)
+        nblk = (p0 + n) // c.block - p0 // c.block
+        cb, cf = nblk * c.hkv * (2 * c.block * c.d * e + 2 * c.d * e), nblk * c.hkv * 4 * c.block * c.d
+        rb = 2 * 2 * min(n, c.ring) * c.hkv * c.d * e  # K and V rows read and written
+        t_pre, t_cmp, t_app = clock.mean_ms("prefill"), clock.mean_ms("compress"), clock.mean_ms("ring_append")
+        ms_step = wall * 1e3 / args.steps
+        bound = "hbm" if pf / pb < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "mfma"
+        kernels["prefill"] = roofline("prefill_chunk", c.name, pb, pf, t_pre, bound)
+        kernels["prefill"]["mfma_frac"] = round(pf / (t_pre * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+        kernels["prefill"]["hbm_frac"] = round(pb / (t_pre * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        kernels["compress"] = roofline("compress_chunk", c.name, cb, cf, t_cmp, "hbm")
+        kernels["ring_append"] = roofline("ring_append", c.name, rb, 0, t_app, "hbm")
+        result.update({"value": round(n / (ms_step * 1e-3), 1), "unit": "tokens/s",
+                       "ms_per_step": round(ms_step, 4)})
+        result["config"] = {"workload": c.name, "batch": 1, "chunk_tokens": n, "pos0": p0, "seq_len": p0 + n,
+                            "cache_entries_before": p0 // c.block, "ring": c.ring, "q_heads": c.hq,
+                            "kv_heads": c.hkv, "head_dim": c.d, "window": c.window, "block": c.block,
+                            "parallelism": "none (1 GPU)"}
+        result["roofline"] = kernels["prefill"]
+        if not args.no_cpu_baseline:
+            log(f"[bench] cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")
+            result["cpu_baseline"] = cpu_baseline_chunk(c, ci, args.cpu_seconds)
+        del ci
+        torch.cuda.empty_cache()
+    elif c.has_prefill:
         log(f"[bench] {c.name}: prefill lens={list(c.prefill_lens)} steps={args.steps}")
         inp, wall, nwarm = run_prefill(torch, hca, c, args.steps, args.warmup, clock, args.min_warmup_s)
         result["warmup_steps_run"] = nwarm
@@ -385,6 +535,11 @@ def main():
         db, df = decode_work(dcfg, dinp["lens"], 2)
         t_dec = clock.mean_ms("decode")
         kernels["decode"] = roofline("decode", dcfg.name, db, df, t_dec, "hbm")
+        # the step's cache maintenance (pool the completed block, append the
+        # new row): one new K, V row in and 128 ring rows + the entry per sequence
+        t_mnt = clock.mean_ms("decode_maintenance")
+        mb = len(dinp["lens"]) * dcfg.hkv * dcfg.d * 2 * (2 * 128 + 2 + 2 + 2)
+        kernels["decode_maintenance"] = roofline("decode_maintenance", dcfg.name, mb, 0, t_mnt, "hbm")
         dec = {"workload": dcfg.name, "queries_per_s": round(len(dinp["lens"]) / (t_dec * 1e-3), 1),
                "unit": "queries/s", "ms_per_call": round(t_dec, 5), "batch": len(dinp["lens"]),
                "context_lens": dinp["lens"] if len(dinp["lens"]) <= 8 else f"{dinp['lens'][0]} each",

@@ -10,6 +10,7 @@ the pages publish no dataset for this layer, so every tensor is random.
 """
 from .configs import CONFIGS, HcaConfig, get_config  # noqa: F401
 from .gen import (  # noqa: F401
+    chunk_inputs,
     cu_from_lengths,
     decode_inputs,
     draw_lengths,

@@ -1,4 +1,4 @@
-"""The five named HCA workloads.
+"""The five named HCA workloads, plus a continuation chunk of the serving path.
 
 Each entry fixes shapes, dtype, window and value distributions.  Seeds are
 1000 + index.  "rms" means every [d] head vector of Q/K/V is drawn N(0,1) in
@@ -31,6 +31,9 @@ class HcaConfig:
     decode_len: int = 0
     decode_len_range: tuple = ()
     ring: int = 0
+    # continuation chunk: the prefill part is one chunk whose first token sits
+    # at this position of a longer sequence (0: a fresh sequence)
+    chunk_pos0: int = 0
     notes: str = field(default="", compare=False)
 
     @property
@@ -68,6 +71,11 @@ CONFIGS = {
         prefill_lens=(32768,), rms=True, w_std=0.5,
         decode_batch=8, decode_len_range=(262144, 1048576), ring=128,
         notes="decode B=8, contexts U[262144, 1048576] + one 32768-token prefill chunk"),
+    "chunk_32k_at_224k": HcaConfig(
+        index=6, name="chunk_32k_at_224k", dtype="bf16", hq=64, hkv=1, d=512, window=128,
+        prefill_lens=(32768,), rms=True, w_std=0.5, ring=128, chunk_pos0=229376,
+        notes="one 32768-token chunk at positions 229376..262143 over a cache of 1792 entries "
+              "+ a 128-slot ring; the chunk completes 256 more blocks"),
 }
 
 

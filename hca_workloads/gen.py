@@ -127,3 +127,24 @@ def ring_from_raw(raw, length: int, ring: int):
     for s in range(max(0, length - ring), length):
         out[s % ring] = raw[s]
     return out
+
+
+def chunk_inputs(cfg, device="cpu", seed=None):
+    """A continuation chunk: raw K, V [L, Hkv, d] and pooling logits of a whole
+    sequence of L = chunk_pos0 + n tokens, and the queries [n, Hq, d] of its
+    last n positions (the chunk).  Distributions as for prefill_inputs."""
+    seed = cfg.seed if seed is None else seed
+    dt = _DT[cfg.dtype]
+    g = _gen(seed, device)
+    n = int(cfg.prefill_lens[0])
+    L = int(cfg.chunk_pos0) + n
+    return {
+        "pos0": int(cfg.chunk_pos0),
+        "n": n,
+        "length": L,
+        "q": _normal((n, cfg.hq, cfg.d), g, device, cfg.rms, dt),
+        "k": _normal((L, cfg.hkv, cfg.d), g, device, cfg.rms, dt),
+        "v": _normal((L, cfg.hkv, cfg.d), g, device, cfg.rms, dt),
+        "w": torch.randn((cfg.hkv, cfg.block), generator=g, device=device,
+                         dtype=torch.float32) * cfg.w_std,
+    }

@@ -64,9 +64,12 @@ struct KeySource {
 };
 
 // A buffer resource over `bytes` bytes from `base` (raw, untyped access;
-// the fourth word is the gfx9 default data format).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+// the fourth word is the gfx9 default data format).  The record size is 32
+// bits: larger ranges are clamped (the host limits the rows a kernel
+// addresses to offsets below 2^31).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, size_t bytes) {
+  const unsigned n = bytes > 0xffffffffull ? 0xffffffffu : (unsigned)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
 }
 
 // Which slots a row (one query position t) may see: compressed slots

@@ -242,10 +242,10 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a, int t
     const size_t rs = (size_t)ks.rstride;
     const size_t head_off = (size_t)kvh * D * sizeof(bf16);
     const int nb = a.cu_blocks[b + 1] - a.cu_blocks[b];
-    ks.comp_k = make_rsrc((const char*)a.kc + (size_t)a.cu_blocks[b] * rs + head_off, (unsigned)(nb * rs));
-    ks.comp_v = make_rsrc((const char*)a.vc + (size_t)a.cu_blocks[b] * rs + head_off, (unsigned)(nb * rs));
-    ks.raw_k = make_rsrc((const char*)a.kw + (size_t)b * a.ring * rs + head_off, (unsigned)(a.ring * rs));
-    ks.raw_v = make_rsrc((const char*)a.vw + (size_t)b * a.ring * rs + head_off, (unsigned)(a.ring * rs));
+    ks.comp_k = make_rsrc((const char*)a.kc + (size_t)a.cu_blocks[b] * rs + head_off, (size_t)nb * rs);
+    ks.comp_v = make_rsrc((const char*)a.vc + (size_t)a.cu_blocks[b] * rs + head_off, (size_t)nb * rs);
+    ks.raw_k = make_rsrc((const char*)a.kw + (size_t)b * a.ring * rs + head_off, (size_t)a.ring * rs);
+    ks.raw_v = make_rsrc((const char*)a.vw + (size_t)b * a.ring * rs + head_off, (size_t)a.ring * rs);
   }
   ks.nc = nc;
   ks.nkeys = nkeys;

@@ -32,6 +32,12 @@ bool mfma_shape(const hca_params* p) {
   return p->head_dim == 512 && p->num_q_heads / p->num_kv_heads == 64;
 }
 
+// The matrix-core kernels address a sequence's rows (raw, ring or cached
+// entries) with 32-bit byte offsets from the sequence's first row.
+bool mfma_rows_fit(const hca_params* p, long rows) {
+  return rows * (long)p->num_kv_heads * p->head_dim * 2 < 0x7fffffffL;
+}
+
 hca_status from_hip(hipError_t e) { return e == hipSuccess ? HCA_OK : HCA_ERR_HIP; }
 
 int elem_bytes(const hca_params* p) { return p->dtype == HCA_BF16 ? 2 : 4; }
@@ -99,6 +105,7 @@ hca_status hca_attend_prefill(const hca_params* params, int32_t batch, int32_t m
   if (params->dtype == HCA_BF16 && !mfma_shape(params)) return HCA_ERR_UNSUPPORTED;
   if (params->dtype == HCA_F32 && (long)max_seqlen * params->num_q_heads > 0x7fffffffL)
     return HCA_ERR_SHAPE;
+  if (params->dtype == HCA_BF16 && !mfma_rows_fit(params, max_seqlen)) return HCA_ERR_SHAPE;
   if (batch == 0 || max_seqlen == 0) return HCA_OK;
   if (!cu_seqlens || !cu_blocks || !q || !k || !v || !o) return HCA_ERR_NULL;
   if (max_seqlen >= hca::kBlock && (!kc || !vc)) return HCA_ERR_NULL;
@@ -140,6 +147,8 @@ hca_status hca_attend_decode(const hca_params* params, int32_t batch, int32_t ma
   if (batch < 0 || max_blocks < 0 || batch > 65535) return HCA_ERR_SHAPE;
   if (ring_cap < params->window) return HCA_ERR_SHAPE;
   if (params->dtype == HCA_BF16 && !mfma_shape(params)) return HCA_ERR_UNSUPPORTED;
+  if (params->dtype == HCA_BF16 && !(mfma_rows_fit(params, ring_cap) && mfma_rows_fit(params, max_blocks)))
+    return HCA_ERR_SHAPE;
   if (batch == 0) return HCA_OK;
   if (!seqlens || !cu_blocks || !q || !kw || !vw || !o) return HCA_ERR_NULL;
   if (max_blocks > 0 && (!kc || !vc)) return HCA_ERR_NULL;
@@ -249,6 +258,7 @@ hca_status hca_attend_prefill_chunk(const hca_params* params, int32_t batch, int
   if (params->dtype == HCA_F32 && (long)max_seqlen * params->num_q_heads > 0x7fffffffL)
     return HCA_ERR_SHAPE;
   const long halo = params->window - 1;
+  if (params->dtype == HCA_BF16 && !mfma_rows_fit(params, (long)max_seqlen + halo)) return HCA_ERR_SHAPE;
   if (((long)total_rows + (long)batch * halo) * params->num_kv_heads * params->head_dim * elem_bytes(params) >
       0xffffffffL)
     return HCA_ERR_SHAPE;  // staged rows are addressed with 32-bit buffer offsets

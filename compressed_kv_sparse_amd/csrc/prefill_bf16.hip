@@ -465,12 +465,12 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, int pair0, in
     const size_t rs = (size_t)c.ks.rstride;
     const size_t head_off = (size_t)kvh * D * sizeof(bf16);
     const int nb = a.cu_blocks[b + 1] - a.cu_blocks[b];
-    c.ks.comp_k = make_rsrc((const char*)a.kc + (size_t)a.cu_blocks[b] * rs + head_off, (unsigned)(nb * rs));
-    c.ks.comp_v = make_rsrc((const char*)a.vc + (size_t)a.cu_blocks[b] * rs + head_off, (unsigned)(nb * rs));
+    c.ks.comp_k = make_rsrc((const char*)a.kc + (size_t)a.cu_blocks[b] * rs + head_off, (size_t)nb * rs);
+    c.ks.comp_v = make_rsrc((const char*)a.vc + (size_t)a.cu_blocks[b] * rs + head_off, (size_t)nb * rs);
     // raw rows of the sequence: positions p0 - halo onward
     const size_t row0 = (size_t)start + (size_t)b * a.halo;
-    c.ks.raw_k = make_rsrc((const char*)a.k + row0 * rs + head_off, (unsigned)((len + a.halo) * rs));
-    c.ks.raw_v = make_rsrc((const char*)a.v + row0 * rs + head_off, (unsigned)((len + a.halo) * rs));
+    c.ks.raw_k = make_rsrc((const char*)a.k + row0 * rs + head_off, (size_t)(len + a.halo) * rs);
+    c.ks.raw_v = make_rsrc((const char*)a.v + row0 * rs + head_off, (size_t)(len + a.halo) * rs);
   }
   c.ks.nc = nc;
   c.ks.nkeys = nkeys;

@@ -111,6 +111,16 @@ def test_prefill_validation(lib):
     assert _prefill(lib, f32, max_seqlen=(1 << 30)) == ERR_SHAPE  # grid would overflow
 
 
+def test_row_offsets_fit_32_bits(lib):
+    """The matrix-core kernels address rows with 32-bit byte offsets (1 KiB
+    rows per KV head): longer sequences are refused, not wrapped."""
+    assert _prefill(lib, _p(), max_seqlen=(1 << 21)) == ERR_SHAPE
+    assert _prefill(lib, _p(num_q_heads=128, num_kv_heads=2), max_seqlen=(1 << 20)) == ERR_SHAPE
+    assert _decode(lib, _p(), max_blocks=(1 << 21)) == ERR_SHAPE
+    assert _decode(lib, _p(), ring=(1 << 21)) == ERR_SHAPE
+    assert _prefill_chunk(lib, _p(), max_seqlen=(1 << 21) - 64, total=(1 << 21)) == ERR_SHAPE
+
+
 def test_decode_validation(lib):
     assert _decode(lib, None) == ERR_NULL
     assert _decode(lib, _p(), ring=64) == ERR_SHAPE              # ring shorter than the window

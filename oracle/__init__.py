@@ -12,6 +12,7 @@ from .hca_oracle import (  # noqa: F401
     cache_entries,
     compress,
     cu_blocks_from_cu_seqlens,
+    head_mix_and_gate,
     pooling_weights,
     visible_sets,
 )

@@ -33,6 +33,15 @@ R4  the two key sets are concatenated (no de-duplication) under one softmax
 R5  query head h reads KV head h // (Hq / Hkv).
 R6  decode: a sequence of length L has its query at position L-1; raw
     position s lives in ring slot s mod R.
+R7  attention epilogue (release blog, section 2.1, last paragraph; Zhidx
+    article, Low-Rank Gated Attention and Virtual Head Attention
+    paragraphs): the pages give an output gate computed from the query
+    latent and a cross-head low-rank mixing with an identity skip, applied
+    after attention; they fix no rank and no gate granularity.  Here the
+    mixing acts among the G heads that share a KV head, O' = O + U (V^T O)
+    with U, V [G, r] per KV head, and the gate is one logit per (token,
+    head) taken through a sigmoid after the mixing: y = sigmoid(g) O'.
+    The gate projection itself runs upstream (its logits are an input).
 
 Arithmetic is float64 throughout; inputs are decoded exactly (bf16 -> f64 is
 exact).  Matrix products and reductions are numpy library calls; nothing is
@@ -234,3 +243,24 @@ def cache_entries(length: int, window: int, block: int = BLOCK) -> int:
     complete block plus the raw window (release blog, section 2.1: a fraction
     of a full layer's cache)."""
     return length // block + min(window, length)
+
+
+def head_mix_and_gate(o, mix_u=None, mix_v=None, gate=None):
+    """R7: y[t, h] = sigmoid(gate[t, h]) * (o[t, h] + sum_r U[h, r] sum_h' V[h', r] o[t, h'])
+    within each KV head's group of G query heads.
+
+    o: [N, Hq, d]; mix_u, mix_v: [Hkv, G, r] (None: no mixing); gate:
+    [N, Hq] logits (None: no gate).  Returns float64 [N, Hq, d].
+    """
+    o = _f64(o)
+    out = o.copy()
+    if mix_u is not None:
+        u, v = _f64(mix_u), _f64(mix_v)
+        hkv, g, _ = u.shape
+        for h in range(hkv):
+            grp = o[:, h * g:(h + 1) * g, :]              # [N, G, d]
+            z = np.einsum("ngd,gr->nrd", grp, v[h])       # V^T O   [N, r, d]
+            out[:, h * g:(h + 1) * g, :] = grp + np.einsum("gr,nrd->ngd", u[h], z)
+    if gate is not None:
+        out = out * (1.0 / (1.0 + np.exp(-_f64(gate))))[:, :, None]
+    return out

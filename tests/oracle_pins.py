@@ -334,9 +334,49 @@ def pin_page_entry_counts(orc):
         assert orc.cache_entries(int(ctx), 128) == n
 
 
+def pin_head_mix_dense(orc):
+    """R7 against a dense formulation: per token, the [Hq, Hq] block-diagonal
+    matrix I + U V^T (one block per KV head) applied with torch, then the
+    gate.  Non-symmetric U, V and varying gates catch an exchanged U / V,
+    a transposed product and the gate applied before the mixing."""
+    r = _rng(61)
+    n, hkv, g, rank, d = 5, 2, 6, 3, 7
+    o = r.standard_normal((n, hkv * g, d))
+    u = r.standard_normal((hkv, g, rank))
+    v = r.standard_normal((hkv, g, rank)) * 0.5
+    gate = r.standard_normal((n, hkv * g)) * 2
+    m = torch.zeros((hkv * g, hkv * g), dtype=torch.float64)
+    for h in range(hkv):
+        m[h * g:(h + 1) * g, h * g:(h + 1) * g] = torch.eye(g, dtype=torch.float64) + \
+            torch.from_numpy(u[h]) @ torch.from_numpy(v[h]).T
+    ref = torch.einsum("ij,njd->nid", m, torch.from_numpy(o)) * torch.sigmoid(torch.from_numpy(gate))[:, :, None]
+    got = orc.head_mix_and_gate(o, u, v, gate)
+    assert _rel(got, ref.numpy()) < 1e-12, _rel(got, ref.numpy())
+
+
+def pin_head_mix_special_cases(orc):
+    """Closed forms: no mixing and no gate is the identity; U = 0 is the
+    identity; a rank-1 mix with U = e_a, V = e_b adds head b to head a only;
+    a zero gate logit halves the output and a large one keeps it."""
+    r = _rng(62)
+    o = r.standard_normal((3, 4, 5))
+    assert np.array_equal(orc.head_mix_and_gate(o), o)
+    z = np.zeros((1, 4, 2))
+    assert np.allclose(orc.head_mix_and_gate(o, z, r.standard_normal((1, 4, 2))), o, rtol=0, atol=0)
+    u = np.zeros((1, 4, 1))
+    v = np.zeros((1, 4, 1))
+    u[0, 1, 0] = 1.0
+    v[0, 3, 0] = 1.0
+    want = o.copy()
+    want[:, 1] += o[:, 3]
+    assert np.allclose(orc.head_mix_and_gate(o, u, v), want, rtol=0, atol=1e-15)
+    assert np.allclose(orc.head_mix_and_gate(o, gate=np.zeros((3, 4))), 0.5 * o, rtol=0, atol=1e-15)
+    assert np.allclose(orc.head_mix_and_gate(o, gate=np.full((3, 4), 60.0)), o, rtol=1e-15, atol=0)
+
+
 ALL_PINS = [
     pin_brute_force, pin_causal_sdpa, pin_constant_blocks, pin_uniform_logits_avg_pool,
     pin_dominant_logit, pin_permutation, pin_row_sums, pin_zero_query_mean,
     pin_constant_values, pin_coverage, pin_decode_is_last_prefill_row, pin_hand_example,
-    pin_page_entry_counts,
+    pin_page_entry_counts, pin_head_mix_dense, pin_head_mix_special_cases,
 ]

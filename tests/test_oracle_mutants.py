@@ -51,6 +51,14 @@ MUTANTS = [
      "for j in range(-(-(end - start) // block)):"),
     ("cache entry count ignores the window", "return length // block + min(window, length)",
      "return length // block"),
+    ("head mix with U and V exchanged", 'out[:, h * g:(h + 1) * g, :] = grp + np.einsum("gr,nrd->ngd", u[h], z)',
+     'out[:, h * g:(h + 1) * g, :] = grp + np.einsum("gr,nrd->ngd", v[h], np.einsum("ngd,gr->nrd", grp, u[h]))'),
+    ("head mix without the identity skip", 'out[:, h * g:(h + 1) * g, :] = grp + np.einsum("gr,nrd->ngd", u[h], z)',
+     'out[:, h * g:(h + 1) * g, :] = np.einsum("gr,nrd->ngd", u[h], z)'),
+    ("gate through exp instead of sigmoid", "out = out * (1.0 / (1.0 + np.exp(-_f64(gate))))[:, :, None]",
+     "out = out * np.exp(_f64(gate))[:, :, None]"),
+    ("gate applied before the mixing", "    out = o.copy()\n    if mix_u is not None:",
+     "    if gate is not None:\n        o = o * (1.0 / (1.0 + np.exp(-_f64(gate))))[:, :, None]\n        gate = None\n    out = o.copy()\n    if mix_u is not None:"),
 ]
 
 

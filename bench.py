@@ -37,6 +37,7 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3
 WORKLOADS = ("prefill_8k", "prefill_128k", "decode_64x128k", "mixed_1m", "tiny_f32", "chunk_32k_at_224k")
+EPILOGUE_RANK = 16  # head-mixing rank of the fused-epilogue measurement (the pages give none)
 _CS = "compressed_kv_sparse_amd/csrc/"
 KERNEL_SOURCES = {
     "prefill": (_CS + "prefill_bf16.hip", _CS + "bf16_tiles.h"),
@@ -81,6 +82,10 @@ def prefill_work(c, lens, e):
 def compress_work(c, lens, e):
     nblk = sum(l // c.block for l in lens)
     return nblk * c.hkv * (2 * c.block * c.d * e + 2 * c.d * e), nblk * c.hkv * 4 * c.block * c.d
+
+
+def ntok_of(lens):
+    return int(sum(lens))
 
 
 def chunk_work(c, p0, n, e):
@@ -284,6 +289,21 @@ def run_prefill(torch, hca, c, steps, warmup, clock, min_warm_s, lens=None):
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if c.dtype == "bf16":
+        # the same attention with the fused epilogue (gate + rank-16 head
+        # mixing), timed apart: its cost over the plain launch
+        g = torch.Generator(device="cuda").manual_seed(c.seed + 29)
+        gate = torch.randn((inp["q"].shape[0], c.hq), generator=g, device="cuda")
+        u = torch.randn((c.hkv, c.hq // c.hkv, EPILOGUE_RANK), generator=g, device="cuda") * 0.1
+        v = torch.randn_like(u) * 0.1
+        for _ in range(3):
+            hca.hca_attend_prefill_gated_vha(p, inp["cu_seqlens"], inp["cu_blocks"], inp["max_seqlen"], inp["q"],
+                                             inp["k"], inp["v"], kc, vc, gate=gate, vha_u=u, vha_v=v, o=o)
+        for _ in range(steps):
+            clock.run("prefill_gated_vha", lambda: hca.hca_attend_prefill_gated_vha(
+                p, inp["cu_seqlens"], inp["cu_blocks"], inp["max_seqlen"], inp["q"], inp["k"], inp["v"], kc, vc,
+                gate=gate, vha_u=u, vha_v=v, o=o))
+        torch.cuda.synchronize()
     return inp, wall, nwarm
 
 
@@ -509,6 +529,13 @@ def main():
         kernels["prefill"]["mfma_frac"] = round(pf / (t_pre * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
         kernels["prefill"]["hbm_frac"] = round(pb / (t_pre * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
         kernels["compress"] = roofline("compress", c.name, cb, cf, t_cmp, "hbm")
+        if clock.pairs.get("prefill_gated_vha"):
+            t_epi = clock.mean_ms("prefill_gated_vha")
+            # + gate logits read; + 2 mixing products per (token, column): 4 * Hq * rank flops
+            eb = pb + ntok_of(lens) * c.hq * 4
+            ef = pf + ntok_of(lens) * c.d * 4 * c.hq * EPILOGUE_RANK
+            kernels["prefill_gated_vha"] = roofline("prefill_gated_vha", c.name, eb, ef, t_epi, bound)
+            kernels["prefill_gated_vha"]["overhead_vs_prefill"] = round(t_epi / t_pre - 1.0, 4)
         result.update({"value": round(ntok / (ms_step * 1e-3), 1), "unit": "tokens/s",
                        "ms_per_step": round(ms_step, 4)})
         result["config"] = {"workload": c.name, "batch": len(lens), "seq_len": max(lens),

@@ -13,6 +13,7 @@ from .hca import (  # noqa: F401
     HcaParams,
     hca_attend_decode,
     hca_attend_prefill,
+    hca_attend_prefill_gated_vha,
     hca_attend_prefill_chunk,
     hca_compress,
     hca_compress_chunk,

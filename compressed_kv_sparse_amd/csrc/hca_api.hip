@@ -95,10 +95,25 @@ hca_status hca_compress(const hca_params* params, int32_t batch, int32_t total_b
   return from_hip(hca::launch_compress(params->dtype, a, (hipStream_t)stream));
 }
 
+hca_status hca_attend_prefill_gated_vha(const hca_params* params, int32_t batch, int32_t max_seqlen,
+                                        const int32_t* cu_seqlens, const int32_t* cu_blocks, const void* q,
+                                        const void* k, const void* v, const void* kc, const void* vc,
+                                        const float* gate, const float* vha_u, const float* vha_v,
+                                        int32_t vha_rank, void* o, void* stream);
+
 hca_status hca_attend_prefill(const hca_params* params, int32_t batch, int32_t max_seqlen,
                               const int32_t* cu_seqlens, const int32_t* cu_blocks, const void* q,
                               const void* k, const void* v, const void* kc, const void* vc,
                               void* o, void* stream) {
+  return hca_attend_prefill_gated_vha(params, batch, max_seqlen, cu_seqlens, cu_blocks, q, k, v, kc, vc,
+                                      nullptr, nullptr, nullptr, 0, o, stream);
+}
+
+hca_status hca_attend_prefill_gated_vha(const hca_params* params, int32_t batch, int32_t max_seqlen,
+                                        const int32_t* cu_seqlens, const int32_t* cu_blocks, const void* q,
+                                        const void* k, const void* v, const void* kc, const void* vc,
+                                        const float* gate, const float* vha_u, const float* vha_v,
+                                        int32_t vha_rank, void* o, void* stream) {
   hca_status st = check_params(params);
   if (st != HCA_OK) return st;
   if (batch < 0 || max_seqlen < 0 || batch > 65535) return HCA_ERR_SHAPE;
@@ -106,6 +121,10 @@ hca_status hca_attend_prefill(const hca_params* params, int32_t batch, int32_t m
   if (params->dtype == HCA_F32 && (long)max_seqlen * params->num_q_heads > 0x7fffffffL)
     return HCA_ERR_SHAPE;
   if (params->dtype == HCA_BF16 && !mfma_rows_fit(params, max_seqlen)) return HCA_ERR_SHAPE;
+  if ((vha_u == nullptr) != (vha_v == nullptr)) return HCA_ERR_NULL;
+  if (vha_u && (vha_rank < 1 || vha_rank > 32)) return HCA_ERR_SHAPE;
+  // the fused epilogue lives in the matrix-core kernel (a whole KV group per workgroup)
+  if ((gate || vha_u) && params->dtype != HCA_BF16) return HCA_ERR_UNSUPPORTED;
   if (batch == 0 || max_seqlen == 0) return HCA_OK;
   if (!cu_seqlens || !cu_blocks || !q || !k || !v || !o) return HCA_ERR_NULL;
   if (max_seqlen >= hca::kBlock && (!kc || !vc)) return HCA_ERR_NULL;
@@ -125,6 +144,10 @@ hca_status hca_attend_prefill(const hca_params* params, int32_t batch, int32_t m
   a.kc = kc;
   a.vc = vc;
   a.o = o;
+  a.gate = gate;
+  a.mix_u = vha_u;
+  a.mix_v = vha_v;
+  a.mix_rank = vha_u ? vha_rank : 0;
   hipStream_t s = (hipStream_t)stream;
   return from_hip(params->dtype == HCA_BF16 ? hca::launch_prefill_bf16(a, s)
                                             : hca::launch_prefill_f32(a, s));

@@ -74,6 +74,13 @@ struct PrefillArgs {
   // onward (halo raw rows precede each chunk; 0 for whole sequences).
   const int* pos0;
   int halo;
+  // Optional epilogue (bf16 path): per-head gate logits [N, Hq] fp32 and a
+  // cross-head low-rank mixing U, V [Hkv, 64, mix_rank] fp32, mix_rank <= 32
+  // (NULL: none).
+  const float* gate;
+  const float* mix_u;
+  const float* mix_v;
+  int mix_rank;
 };
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);

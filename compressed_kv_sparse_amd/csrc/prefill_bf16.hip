@@ -377,13 +377,37 @@ __device__ __forceinline__ void attend_pair(const Ctx& c, const bf16x8 (&qf)[DST
     pipelined_pass<kFixed>(c, qf, st);
 }
 
+// Attention epilogue (release blog "ERNIE 5.5 Flash Base", section 2.1,
+// last paragraph: a per-head output gate and a cross-head low-rank mixing
+// with identity skip after attention): y = sigmoid(g) (O + U (V^T O)) over
+// the 64 heads of the position, O = acc / l, for the wave's 256 columns.
+// The wave holds all 64 heads (st.o[0]: heads 32hg + l%32, st.o[1]: the
+// partner group) as O^T tiles, lane = head.  Per 32-column tile ct, two
+// matrix-core products:
+//   Z [ranks x cols] = V^T O: A = V^T (constant), B = O read back transposed
+//     from bf16 rows (one per head) staged in the wave's own LDS buffer;
+//   y^T = acc^T + Z^T (U^T diag(l)): A = Z^T straight from Z's accumulators
+//     (lane = column), B = U scaled by each head's l, C = the tile of acc
+//     (read, never written back), so that y / l = O + U Z.
+// The ranks run in the k-slot order Z's accumulator layout gives (lane
+// group h: ranks 4h..4h+3, 8+4h..8+4h+3 of each 16), and V^T follows the
+// head order of the transposed reads.  y is scaled, rounded and written over
+// the tile's staged columns (already read), then all 64 rows are stored.
+constexpr int MSTR = 520;  // LDS bytes per staged head row (64 rows fill a K buffer)
+
+__device__ __forceinline__ int kslot_index(int h, int j) { return j < 4 ? 4 * h + j : 8 + 4 * h + (j - 4); }
+
+__device__ __forceinline__ float sigmoid(float x) { return 1.f / (1.f + __expf(-x)); }
+
 // O = acc / l for all 64 heads of the wave's position over its column half,
 // rounded to bf16.  1/l of the partner's rows comes through LDS.  The
 // half-rows are staged in the wave's own buffer, one head group (32 rows x
 // OSTR bytes) at a time, and stored two per instruction (lanes 0-31 row 2i,
-// lanes 32-63 row 2i+1; 512 contiguous bytes each).
-__device__ __forceinline__ void store_output(const Ctx& c, const PState& st, float* linv, bf16* obase,
-                                             bool row_ok) {
+// lanes 32-63 row 2i+1; 512 contiguous bytes each).  EPI: the head mixing
+// and the per-head gate first (output row qrow of the query tensor).
+template <bool EPI>
+__device__ __forceinline__ void store_output(const Ctx& c, PState& st, float* linv, bf16* obase,
+                                             bool row_ok, const PrefillArgs& a, int kvh, int qrow) {
   const int lane = c.lane, wave = c.wave, hg = wave & 1;
   const float lt = st.l + __shfl_xor(st.l, 32);
   const float inv_own = 1.f / lt;
@@ -392,6 +416,104 @@ __device__ __forceinline__ void store_output(const Ctx& c, const PState& st, flo
   const float inv_par = linv[(wave ^ 1) * 32 + (lane & 31)];
   if (!row_ok) return;
   char HCA_LDS* stg = wave == 0 ? c.kb[0] : wave == 1 ? c.kb[1] : wave == 2 ? c.vb[0] : c.vb[1];
+  if constexpr (EPI) {
+    const int h = lane >> 5, r = lane & 31;
+    const bool mix = a.mix_u != nullptr;
+    const int rank = a.mix_rank;
+    float sc[2] = {inv_own, inv_par};  // output scale of head group g: 1/l, times the gate
+    if (a.gate) {
+      const float* gr = a.gate + (size_t)qrow * a.hq + kvh * G + r;
+      sc[0] *= sigmoid(gr[32 * hg]);
+      sc[1] *= sigmoid(gr[32 * (hg ^ 1)]);
+    }
+    bf16x8 vt[4], ut[2][2];
+    if (mix) {
+      // stage O / l as bf16 rows: row = head (0..63), the wave's 256 columns
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const float inv = g ? inv_par : inv_own;
+        char HCA_LDS* rowp = stg + (32 * (hg ^ g) + r) * MSTR + h * 8;
+#pragma unroll
+        for (int ct = 0; ct < HCT; ++ct)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            bf16x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = (bf16)(st.o[g][ct][4 * q4 + i] * inv);
+            *(bf16x4 HCA_LDS*)(rowp + (32 * ct + 8 * q4) * 2) = v;
+          }
+      }
+      const float* vg = a.mix_v + (size_t)kvh * G * rank;
+      const float* ug = a.mix_u + (size_t)kvh * G * rank;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)  // A = V^T, k-step s: heads 16s + kslot_index(h, j)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vt[s][j] = (bf16)(r < rank ? vg[(16 * s + kslot_index(h, j)) * rank + r] : 0.f);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {  // B = U^T diag(l) of head group g, k-step s2: ranks 16 s2 + kslot_index(h, j)
+        const int hd = 32 * (hg ^ g) + r;
+        const float l = 1.f / (g ? inv_par : inv_own);
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int rr = 16 * s2 + kslot_index(h, j);
+            ut[g][s2][j] = (bf16)(rr < rank ? ug[hd * rank + rr] * l : 0.f);
+          }
+      }
+    }
+    const int off = (4 * h + ((lane & 15) >> 2)) * MSTR + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ct = 0; ct < HCT; ++ct) {
+      bf16x8 za[2];
+      if (mix) {
+        f32x16 z = {};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const char HCA_LDS* base = stg + off + 16 * s * MSTR + 64 * ct;
+          const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 HCA_LDS*)base);
+          const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 HCA_LDS*)(base + 8 * MSTR));
+          const bf16x8 bq = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+          z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt[s], bq, z, 0, 0, 0);
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) za[s2][j] = (bf16)z[8 * s2 + j];
+      }
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        f32x16 y = st.o[g][ct];
+        if (mix) {
+          y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za[0], ut[g][0], y, 0, 0, 0);
+          if (rank > 16) y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za[1], ut[g][1], y, 0, 0, 0);
+        }
+        char HCA_LDS* rowp = stg + (32 * (hg ^ g) + r) * MSTR + h * 8 + 64 * ct;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          bf16x4 v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = (bf16)(y[4 * q4 + i] * sc[g]);
+          *(bf16x4 HCA_LDS*)(rowp + 16 * q4) = v;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one column tile at a time
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's LDS writes are done
+    // 64 rows x 512 bytes: lanes 0-31 row 2i, lanes 32-63 row 2i+1
+    const int cw = r * 8;
+#pragma unroll 4
+    for (int i = 0; i < 32; ++i) {
+      const int row = 2 * i + h;
+      const char HCA_LDS* src = stg + row * MSTR + cw * 2;  // 8-byte aligned rows
+      typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 v0 = *(const u32x2 HCA_LDS*)src, v1 = *(const u32x2 HCA_LDS*)(src + 8);
+      const u32x4 v = {v0[0], v0[1], v1[0], v1[1]};
+      *(u32x4*)(obase + (size_t)row * D + cw) = v;
+    }
+    return;
+  }
   const int hr = lane >> 5, cw = (lane & 31) * 8;
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
@@ -429,7 +551,7 @@ __host__ __device__ inline int pair_keys(int t0, int t_last, int window) {
 // (two-term weights, plain loop), LO = false all others (pipelined); each
 // skips the pairs of the other kind.
 // ---------------------------------------------------------------------------
-template <bool LO>
+template <bool LO, bool EPI>
 __device__ __forceinline__ void prefill_body(const PrefillArgs& a, int pair0, int bx, char HCA_LDS* k0_s,
                                              char HCA_LDS* k1_s, char HCA_LDS* v0_s, char HCA_LDS* v1_s,
                                              char HCA_LDS* w0_s, char HCA_LDS* w1_s, int* flag_s, float* linv_s) {
@@ -521,7 +643,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, int pair0, in
   PState st;
   attend_pair<LO>(c, qf, st);
   bf16* obase = (bf16*)a.o + ((size_t)qrow * a.hq + kvh * G) * D + hg * 256;
-  store_output(c, st, linv_s, obase, row_ok);
+  store_output<EPI>(c, st, linv_s, obase, row_ok, a, kvh, qrow);
 }
 
 // Grid (lo_n + npairs - hi_begin, batch, Hkv), 256 threads: workgroup x <
@@ -529,6 +651,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, int pair0, in
 // kinds share one launch (and one LDS layout); the branch is uniform per
 // workgroup, and the two bodies are separate inlined copies so neither
 // carries the other's register state.
+template <bool EPI>
 __global__ __launch_bounds__(256, 1) void prefill_bf16_kernel(PrefillArgs a, int lo_n, int hi_begin) {
   __shared__ __attribute__((aligned(16))) char k0_s[KTILE];
   __shared__ __attribute__((aligned(16))) char k1_s[KTILE];
@@ -541,9 +664,9 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_kernel(PrefillArgs a, int
 #define HCA_LDS_ARGS (char HCA_LDS*)k0_s, (char HCA_LDS*)k1_s, (char HCA_LDS*)v0_s, (char HCA_LDS*)v1_s, \
     (char HCA_LDS*)w0_s, (char HCA_LDS*)w1_s, flag_s, linv_s
   if ((int)blockIdx.x < lo_n)
-    prefill_body<true>(a, 0, blockIdx.x, HCA_LDS_ARGS);
+    prefill_body<true, EPI>(a, 0, blockIdx.x, HCA_LDS_ARGS);
   else
-    prefill_body<false>(a, hi_begin, blockIdx.x - lo_n, HCA_LDS_ARGS);
+    prefill_body<false, EPI>(a, hi_begin, blockIdx.x - lo_n, HCA_LDS_ARGS);
 #undef HCA_LDS_ARGS
 }
 
@@ -569,7 +692,11 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
   // Chunks start at pos0 >= 0: any of the first lo_end pairs may be of
   // either kind, so the pipelined body also gets all of them.
   const int lo_end = first_over(true), hi_begin = a.pos0 ? 0 : first_over(false);
-  prefill_bf16_kernel<<<dim3(lo_end + npairs - hi_begin, a.batch, a.hkv), 256, 0, s>>>(a, lo_end, hi_begin);
+  const dim3 grid(lo_end + npairs - hi_begin, a.batch, a.hkv);
+  if (a.gate || a.mix_u)
+    prefill_bf16_kernel<true><<<grid, 256, 0, s>>>(a, lo_end, hi_begin);
+  else
+    prefill_bf16_kernel<false><<<grid, 256, 0, s>>>(a, lo_end, hi_begin);
   return hipGetLastError();
 }
 

@@ -22,7 +22,7 @@ HCA_F32, HCA_BF16 = 0, 1
 _DTYPES = {torch.float32: HCA_F32, torch.bfloat16: HCA_BF16}
 EXPORTS = ("hca_compress", "hca_attend_prefill", "hca_decode_workspace_bytes",
            "hca_attend_decode", "hca_compress_chunk", "hca_ring_append",
-           "hca_prefill_chunk_workspace_bytes", "hca_attend_prefill_chunk",
+           "hca_prefill_chunk_workspace_bytes", "hca_attend_prefill_chunk", "hca_attend_prefill_gated_vha",
            "hca_status_string", "hca_version")
 
 
@@ -74,6 +74,9 @@ def library() -> ctypes.CDLL:
     lib.hca_compress.restype = ctypes.c_int
     lib.hca_attend_prefill.argtypes = [P, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.hca_attend_prefill.restype = ctypes.c_int
+    lib.hca_attend_prefill_gated_vha.argtypes = [P, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32,
+                                                 vp, vp]
+    lib.hca_attend_prefill_gated_vha.restype = ctypes.c_int
     lib.hca_decode_workspace_bytes.argtypes = [P, i32, i32]
     lib.hca_decode_workspace_bytes.restype = sz
     lib.hca_attend_decode.argtypes = [P, i32, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
@@ -149,6 +152,22 @@ def hca_attend_prefill(params: HcaParams, cu_seqlens, cu_blocks, max_seqlen: int
                                       _ptr(cu_blocks), _ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc),
                                       _ptr(o), _stream(stream))
     _check("hca_attend_prefill", st)
+    return o
+
+
+def hca_attend_prefill_gated_vha(params: HcaParams, cu_seqlens, cu_blocks, max_seqlen: int, q, k, v, kc, vc,
+                                 gate=None, vha_u=None, vha_v=None, o=None, stream=None):
+    """hca_attend_prefill with the fused output gate (logits [N_tok, Hq]) and
+    Virtual Head Attention mixing (U, V [Hkv, G, rank]).  Returns o."""
+    batch = cu_seqlens.numel() - 1
+    if o is None:
+        o = torch.empty_like(q)
+    rank = 0 if vha_u is None else int(vha_u.shape[-1])
+    st = library().hca_attend_prefill_gated_vha(ctypes.byref(params), batch, int(max_seqlen), _ptr(cu_seqlens),
+                                                _ptr(cu_blocks), _ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc),
+                                                _ptr(gate), _ptr(vha_u), _ptr(vha_v), rank, _ptr(o),
+                                                _stream(stream))
+    _check("hca_attend_prefill_gated_vha", st)
     return o
 
 

@@ -120,6 +120,34 @@ HCA_API hca_status hca_attend_prefill(const hca_params* params, int32_t batch, i
                               const void* kc, const void* vc, void* o, void* stream);
 
 /*
+ * hca_attend_prefill_gated_vha - hca_attend_prefill with the attention
+ * epilogue fused into the output stage (release blog, section 2.1, last
+ * paragraph: a low-rank gated attention output gate and Virtual Head
+ * Attention, a cross-head low-rank mixing with identity skip applied after
+ * attention and fused into the attention kernel at inference).  With O the
+ * attention output of one token and the G = Hq / Hkv heads of one KV head:
+ *
+ *   y[h] = sigmoid(gate[t, h]) * (O[h] + sum_r U[h, r] sum_h' V[h', r] O[h'])
+ *
+ *   gate            device fp32 [N_tok, Hq] gate logits (the gate projection
+ *                   of the query latent runs upstream), or NULL: no gate
+ *   vha_u, vha_v    device fp32 [Hkv, G, vha_rank] mixing factors, both or
+ *                   neither NULL; 1 <= vha_rank <= 32
+ *
+ * The pages fix neither the rank nor the gate granularity: one gate logit
+ * per (token, head), mixing within a KV head's group, mixing before the gate.
+ * HCA_BF16 only (HCA_ERR_UNSUPPORTED for HCA_F32 with an epilogue); with no
+ * gate and no mixing it is hca_attend_prefill.
+ */
+HCA_API hca_status hca_attend_prefill_gated_vha(const hca_params* params, int32_t batch,
+                                        int32_t max_seqlen, const int32_t* cu_seqlens,
+                                        const int32_t* cu_blocks, const void* q, const void* k,
+                                        const void* v, const void* kc, const void* vc,
+                                        const float* gate, const float* vha_u,
+                                        const float* vha_v, int32_t vha_rank, void* o,
+                                        void* stream);
+
+/*
  * hca_decode_workspace_bytes - size in bytes of the scratch buffer that
  * hca_attend_decode needs for `batch` sequences whose longest cache holds
  * `max_blocks` entries.  Returns 0 for invalid params.

@@ -218,3 +218,18 @@ def test_chunk_workspace_sizes(lib):
     assert hca.hca_prefill_chunk_workspace_bytes(p, -1, 10) == 0
     f32 = _p(dtype=hca.HCA_F32, num_q_heads=4, head_dim=64, window=64)
     assert hca.hca_prefill_chunk_workspace_bytes(f32, 2, 5) == 2 * (((5 + 2 * 63) * 64 * 4 + 255) // 256 * 256)
+
+
+def test_gated_vha_validation(lib):
+    def call(params, gate=DUMMY, u=DUMMY, v=DUMMY, rank=8, max_seqlen=256):
+        pp = ctypes.byref(params) if params is not None else None
+        return lib.hca_attend_prefill_gated_vha(pp, 1, max_seqlen, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY,
+                                                gate, u, v, rank, DUMMY, None)
+    assert call(None) == ERR_NULL
+    assert call(_p(), u=NULL) == ERR_NULL                    # U and V come together
+    assert call(_p(), rank=0) == ERR_SHAPE
+    assert call(_p(), rank=33) == ERR_SHAPE
+    assert call(_p(dtype=hca.HCA_F32, num_q_heads=4, head_dim=64)) == ERR_UNSUPPORTED  # bf16 kernel only
+    assert call(_p(), max_seqlen=0) == OK
+    # no epilogue: plain prefill, also in fp32
+    assert call(_p(dtype=hca.HCA_F32, num_q_heads=4, head_dim=64), gate=NULL, u=NULL, v=NULL, max_seqlen=0) == OK

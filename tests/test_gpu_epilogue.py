@@ -1,0 +1,90 @@
+"""GPU parity of the fused attention epilogue (hca_attend_prefill_gated_vha):
+a per-head sigmoid output gate and the cross-head low-rank mixing with
+identity skip, against the oracle's attention followed by its
+head_mix_and_gate."""
+from __future__ import annotations
+
+import dataclasses
+
+import pytest
+import torch
+
+import compressed_kv_sparse_amd as hca
+import oracle
+from hca_workloads import CONFIGS, prefill_inputs
+from parity_util import assert_close, params_for
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _case(lens, hkv, seed):
+    c = dataclasses.replace(CONFIGS["prefill_8k"], hkv=hkv, hq=64 * hkv)
+    inp = prefill_inputs(c, DEV, lens=lens, seed=seed)
+    p = params_for(c)
+    kc, vc = hca.hca_compress(p, inp["cu_seqlens"], inp["cu_blocks"], inp["total_blocks"], inp["k"], inp["w"],
+                              v=inp["v"])
+    return c, inp, p, kc, vc
+
+
+def _factors(hkv, rank, seed, scale=0.1):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    u = torch.randn((hkv, 64, rank), generator=g, device=DEV) * scale
+    v = torch.randn((hkv, 64, rank), generator=g, device=DEV) * scale
+    return u, v
+
+
+def _oracle(c, inp, u=None, v=None, gate=None):
+    cu = inp["cu_seqlens_host"]
+    w = inp["w"].cpu()
+    o = oracle.attend_prefill(inp["q"].cpu(), inp["k"].cpu(), inp["v"].cpu(), oracle.compress(inp["k"].cpu(), w, cu),
+                              oracle.compress(inp["v"].cpu(), w, cu), cu, c.window)
+    return oracle.head_mix_and_gate(o, None if u is None else u.cpu(), None if v is None else v.cpu(),
+                                    None if gate is None else gate.cpu())
+
+
+@pytest.mark.parametrize("lens,hkv,rank,with_gate", [
+    ([300, 1000], 1, 8, False),
+    ([513], 1, 32, False),        # two rank steps
+    ([700, 129], 1, 1, True),
+    ([1000], 1, 16, True),
+    ([400, 77], 2, 24, True),     # two KV heads: mixing stays inside each group
+])
+def test_gated_vha_bf16(lens, hkv, rank, with_gate):
+    c, inp, p, kc, vc = _case(lens, hkv, seed=401)
+    u, v = _factors(hkv, rank, seed=402)
+    gate = None
+    if with_gate:
+        g = torch.Generator(device=DEV).manual_seed(403)
+        gate = torch.randn((sum(lens), 64 * hkv), generator=g, device=DEV) * 2
+    o = hca.hca_attend_prefill_gated_vha(p, inp["cu_seqlens"], inp["cu_blocks"], inp["max_seqlen"], inp["q"],
+                                         inp["k"], inp["v"], kc, vc, gate=gate, vha_u=u, vha_v=v)
+    torch.cuda.synchronize()
+    # the first rows of a sequence can have |O| > 4 (few visible keys), where
+    # bf16 rounding alone reaches 0.0156
+    assert_close(o, _oracle(c, inp, u, v, gate), torch.bfloat16,
+                 f"gated VHA lens={lens} Hkv={hkv} rank={rank} gate={with_gate}", beyond_rounding=True)
+
+
+def test_gate_only():
+    c, inp, p, kc, vc = _case([900, 64], 1, seed=411)
+    g = torch.Generator(device=DEV).manual_seed(412)
+    gate = torch.randn((964, 64), generator=g, device=DEV) * 3
+    o = hca.hca_attend_prefill_gated_vha(p, inp["cu_seqlens"], inp["cu_blocks"], inp["max_seqlen"], inp["q"],
+                                         inp["k"], inp["v"], kc, vc, gate=gate)
+    torch.cuda.synchronize()
+    assert_close(o, _oracle(c, inp, gate=gate), torch.bfloat16, "gate only", beyond_rounding=True)
+
+
+def test_zero_mixing_is_plain_prefill():
+    """U = 0: the epilogue adds exact zeros, so its separate store path must
+    reproduce the plain kernel's output bit for bit."""
+    c, inp, p, kc, vc = _case([777, 130], 1, seed=421)
+    u, v = _factors(1, 8, seed=422)
+    u.zero_()
+    o_mix = hca.hca_attend_prefill_gated_vha(p, inp["cu_seqlens"], inp["cu_blocks"], inp["max_seqlen"], inp["q"],
+                                             inp["k"], inp["v"], kc, vc, vha_u=u, vha_v=v)
+    o_plain = hca.hca_attend_prefill(p, inp["cu_seqlens"], inp["cu_blocks"], inp["max_seqlen"], inp["q"], inp["k"],
+                                     inp["v"], kc, vc)
+    torch.cuda.synchronize()
+    assert torch.equal(o_mix.view(torch.int16), o_plain.view(torch.int16))

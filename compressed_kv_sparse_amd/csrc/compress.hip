@@ -28,9 +28,8 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a, int cw) {
   constexpr int RPP = 256 / TPR;          // rows per pass
   constexpr int PASSES = kBlock / RPP;
   static_assert(kBlock % RPP == 0, "rows per pass must divide the block");
-  __shared__ float p_s[kBlock];
+  __shared__ float p_s[4][kBlock];  // one copy per wavefront
   __shared__ float red_s[4][TPR * VEC];
-  __shared__ float stat_s[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int entry_head = blockIdx.x;              // entry * hkv + head
@@ -63,25 +62,8 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a, int cw) {
     j = entry - a.cu_blocks[lo];
   }
 
-  // pooling weights p = softmax(w_h), max-subtracted, in fp32
-  float wv = tid < kBlock ? a.w[h * kBlock + tid] : -INFINITY;
-  float mx = wv;
-  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  if (lane == 0) stat_s[wave] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(stat_s[0], stat_s[1]), fmaxf(stat_s[2], stat_s[3]));
-  float e = tid < kBlock ? expf(wv - mx) : 0.f;
-  float sm = e;
-  for (int off = 32; off > 0; off >>= 1) sm += __shfl_xor(sm, off);
-  __syncthreads();
-  if (lane == 0) stat_s[wave] = sm;
-  __syncthreads();
-  sm = stat_s[0] + stat_s[1] + stat_s[2] + stat_s[3];
-  if (tid < kBlock) p_s[tid] = e / sm;
-
   const size_t col = (size_t)h * a.d + c0 + (tid % TPR) * VEC;  // this thread's first element in a row
   const int r0 = tid / TPR;
-  __syncthreads();
 
   // all of this thread's loads are issued before any is used, so a thread
   // keeps PASSES 16-byte loads in flight (the default schedule would wait
@@ -106,12 +88,28 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a, int cw) {
     for (int ps = 0; ps < PASSES; ++ps) xv[ps] = *(const vec_t*)(x + (size_t)(ps * RPP + r0) * rstride);
   }
   __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of their uses
+
+  // pooling weights p = softmax(w_h), max-subtracted, in fp32, while the
+  // rows are in flight.  Every wavefront computes all 128 weights (two per
+  // lane, wave-wide max and sum) and writes them to p_s itself: the waves
+  // write identical values and each reads only after its own writes, so no
+  // barrier (which would also wait for the row loads) is needed.
+  {
+    const float w0 = a.w[h * kBlock + lane], w1 = a.w[h * kBlock + 64 + lane];
+    float mx = fmaxf(w0, w1);
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    const float e0 = expf(w0 - mx), e1 = expf(w1 - mx);
+    float sm = e0 + e1;
+    for (int off = 32; off > 0; off >>= 1) sm += __shfl_xor(sm, off);
+    p_s[wave][lane] = e0 / sm;
+    p_s[wave][64 + lane] = e1 / sm;
+  }
   float acc[VEC];
 #pragma unroll
   for (int c = 0; c < VEC; ++c) acc[c] = 0.f;
 #pragma unroll
   for (int ps = 0; ps < PASSES; ++ps) {
-    const float pr = p_s[ps * RPP + r0];
+    const float pr = p_s[wave][ps * RPP + r0];
 #pragma unroll
     for (int c = 0; c < VEC; ++c) acc[c] = fmaf(pr, to_f32(xv[ps][c]), acc[c]);
   }

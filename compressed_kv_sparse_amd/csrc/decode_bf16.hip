@@ -185,13 +185,16 @@ __device__ __forceinline__ void attend_tiles16(const KeySource& ks, int t_begin,
 // ---------------------------------------------------------------------------
 // Decode: split kernel grid (max_splits, batch, Hkv), 256 threads (4
 // wavefronts x 16 heads), then the merge kernel.
-// Workspace: fp32 m and l [B*Hkv][splits][64], then fp32 O [B*Hkv][splits]
+// Workspace: fp32 m and l [B*Hkv][splits][64], then bf16 O [B*Hkv][splits]
 // [64][512] normalised by its own l (a convex combination of value rows).
+// O / l in bf16 halves the partial traffic (written, then read back by the
+// merge); its rounding (<= 2^-9 relative) survives the merge's convex
+// combination unchanged, next to the output's own bf16 rounding.
 // ---------------------------------------------------------------------------
 struct WsLayout {
   float* m;
   float* l;
-  float* o;
+  bf16* o;
 };
 
 __host__ __device__ inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -204,7 +207,7 @@ __host__ __device__ inline WsLayout ws_layout(void* ws, int batch, int hkv, int 
   p += round_up(units * splits * G * sizeof(float), 256);
   w.l = (float*)p;
   p += round_up(units * splits * G * sizeof(float), 256);
-  w.o = (float*)p;
+  w.o = (bf16*)p;
   return w;
 }
 
@@ -282,9 +285,14 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a, int t
     w.l[prow] = l_tot;
   }
   const float inv = 1.f / l_tot;
-  float* po = w.o + prow * D + 4 * (lane >> 4);
+  bf16* po = w.o + prow * D + 4 * (lane >> 4);
 #pragma unroll
-  for (int ct = 0; ct < CTILES16; ++ct) *(f32x4*)(po + 16 * ct) = st.o[ct] * inv;
+  for (int ct = 0; ct < CTILES16; ++ct) {
+    bf16x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (bf16)(st.o[ct][i] * inv);
+    *(bf16x4*)(po + 16 * ct) = v;
+  }
 }
 
 // Merge of the split partials: O = sum_s 2^(m_s - M) l_s O_s / sum_s 2^(m_s - M) l_s
@@ -308,7 +316,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int tps
   const WsLayout w = ws_layout(a.ws, a.batch, a.hkv, max_splits);
   const float* mrow = w.m + (size_t)unit * max_splits * G + r;
   const float* lrow = w.l + (size_t)unit * max_splits * G + r;
-  const float* orow = w.o + ((size_t)unit * max_splits * G + r) * D + c;
+  const bf16* orow = w.o + ((size_t)unit * max_splits * G + r) * D + c;
   // running M with rescaling between batches (exact when one batch covers
   // all splits, as in the common case)
   float M = -INFINITY, den = 0.f;
@@ -321,7 +329,9 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int tps
       const int sp = min(s0 + j, nsplit - 1);  // repeats of the last split are dropped below
       mv[j] = mrow[(size_t)sp * G];
       lv[j] = lrow[(size_t)sp * G];
-      ov[j] = *(const f32x4*)(orow + (size_t)sp * G * D);
+      const bf16x4 ob = *(const bf16x4*)(orow + (size_t)sp * G * D);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ov[j][i] = (float)ob[i];
     }
     float Mb = M;
 #pragma unroll
@@ -366,7 +376,7 @@ size_t decode_workspace_bytes_bf16(int batch, int hkv, int max_blocks, int windo
   const DecodePlan p = decode_plan(batch, hkv, max_blocks, window);
   const size_t units = (size_t)batch * hkv;
   return 2 * round_up(units * p.max_splits * G * sizeof(float), 256) +
-         units * p.max_splits * G * D * sizeof(float);
+         units * p.max_splits * G * D * sizeof(bf16);
 }
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {

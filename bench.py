@@ -433,6 +433,25 @@ def run_decode(torch, hca, c, steps, warmup, clock, min_warm_s, n_sets=4):
         step(nwarm + i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # the same decode with the fused epilogue (gate + rank-16 head mixing in
+    # the merge), timed apart
+    g = torch.Generator(device="cuda").manual_seed(c.seed + 31)
+    gates = [torch.randn((len(x["lens"]), c.hq), generator=g, device="cuda") for x in sets]
+    u = torch.randn((c.hkv, c.hq // c.hkv, EPILOGUE_RANK), generator=g, device="cuda") * 0.1
+    v = torch.randn_like(u) * 0.1
+
+    def step_epi(i):
+        s, k = sets[i % n_sets], i % n_sets
+        clock.run("decode_gated_vha", lambda: hca.hca_attend_decode_gated_vha(
+            p, s["seqlens"], s["cu_blocks"], s["max_blocks"], s["q"], s["kc"], s["vc"], s["kw"], s["vw"],
+            gate=gates[k], vha_u=u, vha_v=v, workspace=ws[k], o=outs[k]))
+
+    for i in range(n_sets):
+        step_epi(i)
+    clock.pairs.pop("decode_gated_vha", None)
+    for i in range(steps):
+        step_epi(i)
+    torch.cuda.synchronize()
     return sets[0], wall, nwarm
 
 
@@ -564,6 +583,10 @@ def main():
         kernels["decode"] = roofline("decode", dcfg.name, db, df, t_dec, "hbm")
         # the step's cache maintenance (pool the completed block, append the
         # new row): one new K, V row in and 128 ring rows + the entry per sequence
+        if clock.pairs.get("decode_gated_vha"):
+            t_de = clock.mean_ms("decode_gated_vha")
+            kernels["decode_gated_vha"] = roofline("decode_gated_vha", dcfg.name, db, df, t_de, "hbm")
+            kernels["decode_gated_vha"]["overhead_vs_decode"] = round(t_de / t_dec - 1.0, 4)
         t_mnt = clock.mean_ms("decode_maintenance")
         mb = len(dinp["lens"]) * dcfg.hkv * dcfg.d * 2 * (2 * 128 + 2 + 2 + 2)
         kernels["decode_maintenance"] = roofline("decode_maintenance", dcfg.name, mb, 0, t_mnt, "hbm")

@@ -12,9 +12,11 @@ from .hca import (  # noqa: F401
     HcaLibraryMissing,
     HcaParams,
     hca_attend_decode,
+    hca_attend_decode_gated_vha,
     hca_attend_prefill,
     hca_attend_prefill_gated_vha,
     hca_attend_prefill_chunk,
+    hca_attend_prefill_chunk_gated_vha,
     hca_compress,
     hca_compress_chunk,
     hca_decode_workspace_bytes,

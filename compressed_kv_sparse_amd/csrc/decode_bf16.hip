@@ -303,17 +303,9 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a, int t
 // XCD u % 8 like its split workgroups, whose L2 may still hold the partials.
 constexpr int kMergeBatch = 8;
 
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int tps, int max_splits) {
-  const int wg = (int)blockIdx.x;
-  const int unit = (wg & 7) + 8 * ((wg >> 3) / (G / 2));  // b * Hkv + kvh
-  if (unit >= a.batch * a.hkv) return;
-  const int b = unit / a.hkv, kvh = unit % a.hkv;
-  const int r = ((wg >> 3) % (G / 2)) * 2 + (threadIdx.x >> 7);  // head within the KV group
-  const int c = (threadIdx.x & 127) * 4;
-  const int L = a.seqlens[b];
-  const int nkeys = L / kBlock + min(a.window, L);
-  const int nsplit = ((nkeys + NT - 1) / NT + tps - 1) / tps;
-  const WsLayout w = ws_layout(a.ws, a.batch, a.hkv, max_splits);
+// Merged O (normalised) of head r, columns c .. c+3 of one unit.
+__device__ __forceinline__ f32x4 merge_cols(const WsLayout& w, int unit, int r, int c, int nsplit,
+                                           int max_splits) {
   const float* mrow = w.m + (size_t)unit * max_splits * G + r;
   const float* lrow = w.l + (size_t)unit * max_splits * G + r;
   const bf16* orow = w.o + ((size_t)unit * max_splits * G + r) * D + c;
@@ -351,11 +343,87 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int tps
       n0 += wgt * ov[j];
     }
   }
-  const float rden = 1.f / den;
+  return n0 * (1.f / den);
+}
+
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int tps, int max_splits) {
+  const int wg = (int)blockIdx.x;
+  const int unit = (wg & 7) + 8 * ((wg >> 3) / (G / 2));  // b * Hkv + kvh
+  if (unit >= a.batch * a.hkv) return;
+  const int b = unit / a.hkv, kvh = unit % a.hkv;
+  const int r = ((wg >> 3) % (G / 2)) * 2 + (threadIdx.x >> 7);  // head within the KV group
+  const int c = (threadIdx.x & 127) * 4;
+  const int L = a.seqlens[b];
+  const int nkeys = L / kBlock + min(a.window, L);
+  const int nsplit = ((nkeys + NT - 1) / NT + tps - 1) / tps;
+  const WsLayout w = ws_layout(a.ws, a.batch, a.hkv, max_splits);
+  const f32x4 n = merge_cols(w, unit, r, c, nsplit, max_splits);
   bf16x4 v;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = (bf16)(n0[i] * rden);
+  for (int i = 0; i < 4; ++i) v[i] = (bf16)n[i];
   *(bf16x4*)((bf16*)a.o + ((size_t)b * a.hq + kvh * G + r) * D + c) = v;
+}
+
+// Merge with the attention epilogue (release blog "ERNIE 5.5 Flash Base",
+// section 2.1, last paragraph: per-head output gate and Virtual Head
+// Attention, a cross-head low-rank mixing with identity skip):
+// y[h] = sigmoid(gate[b, h]) (O[h] + sum_r U[h, r] sum_h' V[h', r] O[h']).
+// One workgroup covers all 64 heads of a unit for 32 columns (the mixing
+// runs across heads); thread t merges head t/4, columns 8(t%4) .. +7, the
+// merged tile goes through LDS, Z = V^T O and U Z are fp32 dot products.
+// Grid 8 x 16 column slices x unit groups, XCD-aware like the split kernel.
+__global__ __launch_bounds__(256) void decode_merge_epi_kernel(DecodeArgs a, int tps, int max_splits) {
+  __shared__ float o_s[G][33];
+  __shared__ float z_s[32][33];
+  __shared__ float v_s[G][33];  // V of the unit's KV head, [head][rank]
+  const int wg = (int)blockIdx.x;
+  const int unit = (wg & 7) + 8 * ((wg >> 3) / (D / 32));
+  if (unit >= a.batch * a.hkv) return;
+  const int slice = (wg >> 3) % (D / 32);
+  const int b = unit / a.hkv, kvh = unit % a.hkv;
+  const int tid = threadIdx.x, hr = tid >> 2, cq = (tid & 3) * 8;
+  const int L = a.seqlens[b];
+  const int nkeys = L / kBlock + min(a.window, L);
+  const int nsplit = ((nkeys + NT - 1) / NT + tps - 1) / tps;
+  const WsLayout w = ws_layout(a.ws, a.batch, a.hkv, max_splits);
+  const int c0 = 32 * slice + cq;
+  float y[8];
+  {
+    const f32x4 m0 = merge_cols(w, unit, hr, c0, nsplit, max_splits);
+    const f32x4 m1 = merge_cols(w, unit, hr, c0 + 4, nsplit, max_splits);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      y[i] = m0[i];
+      y[4 + i] = m1[i];
+    }
+  }
+  if (a.mix_u) {
+    const int rank = a.mix_rank;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o_s[hr][cq + i] = y[i];
+    const float* vg = a.mix_v + (size_t)kvh * G * rank;
+    for (int e = tid; e < G * rank; e += 256) v_s[e / rank][e % rank] = vg[e];
+    __syncthreads();
+    for (int e = tid; e < rank * 32; e += 256) {  // Z[rk][c] = sum_h V[h][rk] O[h][c]
+      const int rk = e >> 5, c = e & 31;
+      float z = 0.f;
+#pragma unroll 16
+      for (int h = 0; h < G; ++h) z = fmaf(v_s[h][rk], o_s[h][c], z);
+      z_s[rk][c] = z;
+    }
+    __syncthreads();
+    const float* ug = a.mix_u + ((size_t)kvh * G + hr) * rank;
+    for (int rk = 0; rk < rank; ++rk) {
+      const float u = ug[rk];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = fmaf(u, z_s[rk][cq + i], y[i]);
+    }
+  }
+  const float gsc = a.gate ? 1.f / (1.f + __expf(-a.gate[(size_t)b * a.hq + kvh * G + hr])) : 1.f;
+  bf16x8 v;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (bf16)(y[i] * gsc);
+  *(bf16x8*)((bf16*)a.o + ((size_t)b * a.hq + kvh * G + hr) * D + c0) = v;
 }
 
 }  // namespace
@@ -386,7 +454,10 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
                                                                           p.max_splits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  decode_merge_kernel<<<(unsigned)(8 * (G / 2) * groups), 256, 0, s>>>(a, p.tiles_per_split, p.max_splits);
+  if (a.gate || a.mix_u)
+    decode_merge_epi_kernel<<<(unsigned)(8 * (D / 32) * groups), 256, 0, s>>>(a, p.tiles_per_split, p.max_splits);
+  else
+    decode_merge_kernel<<<(unsigned)(8 * (G / 2) * groups), 256, 0, s>>>(a, p.tiles_per_split, p.max_splits);
   return hipGetLastError();
 }
 

@@ -40,6 +40,15 @@ bool mfma_rows_fit(const hca_params* p, long rows) {
 
 hca_status from_hip(hipError_t e) { return e == hipSuccess ? HCA_OK : HCA_ERR_HIP; }
 
+// Arguments of the fused attention epilogue (gate logits, mixing factors).
+hca_status check_epilogue(const hca_params* p, const float* gate, const float* u, const float* v, int32_t rank) {
+  if ((u == nullptr) != (v == nullptr)) return HCA_ERR_NULL;
+  if (u && (rank < 1 || rank > 32)) return HCA_ERR_SHAPE;
+  // fused into the matrix-core kernels (a whole KV group per workgroup)
+  if ((gate || u) && p->dtype != HCA_BF16) return HCA_ERR_UNSUPPORTED;
+  return HCA_OK;
+}
+
 int elem_bytes(const hca_params* p) { return p->dtype == HCA_BF16 ? 2 : 4; }
 
 // Bytes of one staged plane (K or V) of a chunk call: every sequence's
@@ -121,10 +130,8 @@ hca_status hca_attend_prefill_gated_vha(const hca_params* params, int32_t batch,
   if (params->dtype == HCA_F32 && (long)max_seqlen * params->num_q_heads > 0x7fffffffL)
     return HCA_ERR_SHAPE;
   if (params->dtype == HCA_BF16 && !mfma_rows_fit(params, max_seqlen)) return HCA_ERR_SHAPE;
-  if ((vha_u == nullptr) != (vha_v == nullptr)) return HCA_ERR_NULL;
-  if (vha_u && (vha_rank < 1 || vha_rank > 32)) return HCA_ERR_SHAPE;
-  // the fused epilogue lives in the matrix-core kernel (a whole KV group per workgroup)
-  if ((gate || vha_u) && params->dtype != HCA_BF16) return HCA_ERR_UNSUPPORTED;
+  st = check_epilogue(params, gate, vha_u, vha_v, vha_rank);
+  if (st != HCA_OK) return st;
   if (batch == 0 || max_seqlen == 0) return HCA_OK;
   if (!cu_seqlens || !cu_blocks || !q || !k || !v || !o) return HCA_ERR_NULL;
   if (max_seqlen >= hca::kBlock && (!kc || !vc)) return HCA_ERR_NULL;
@@ -160,11 +167,28 @@ size_t hca_decode_workspace_bytes(const hca_params* params, int32_t batch, int32
   return hca::decode_workspace_bytes_bf16(batch, params->num_kv_heads, max_blocks, params->window);
 }
 
+hca_status hca_attend_decode_gated_vha(const hca_params* params, int32_t batch, int32_t max_blocks,
+                                       const int32_t* seqlens, const int32_t* cu_blocks, const void* q,
+                                       const void* kc, const void* vc, const void* kw, const void* vw,
+                                       int32_t ring_cap, const float* gate, const float* vha_u,
+                                       const float* vha_v, int32_t vha_rank, void* o, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
 hca_status hca_attend_decode(const hca_params* params, int32_t batch, int32_t max_blocks,
                              const int32_t* seqlens, const int32_t* cu_blocks, const void* q,
                              const void* kc, const void* vc, const void* kw, const void* vw,
                              int32_t ring_cap, void* o, void* workspace, size_t workspace_bytes,
                              void* stream) {
+  return hca_attend_decode_gated_vha(params, batch, max_blocks, seqlens, cu_blocks, q, kc, vc, kw, vw, ring_cap,
+                                     nullptr, nullptr, nullptr, 0, o, workspace, workspace_bytes, stream);
+}
+
+hca_status hca_attend_decode_gated_vha(const hca_params* params, int32_t batch, int32_t max_blocks,
+                                       const int32_t* seqlens, const int32_t* cu_blocks, const void* q,
+                                       const void* kc, const void* vc, const void* kw, const void* vw,
+                                       int32_t ring_cap, const float* gate, const float* vha_u,
+                                       const float* vha_v, int32_t vha_rank, void* o, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
   hca_status st = check_params(params);
   if (st != HCA_OK) return st;
   if (batch < 0 || max_blocks < 0 || batch > 65535) return HCA_ERR_SHAPE;
@@ -172,6 +196,8 @@ hca_status hca_attend_decode(const hca_params* params, int32_t batch, int32_t ma
   if (params->dtype == HCA_BF16 && !mfma_shape(params)) return HCA_ERR_UNSUPPORTED;
   if (params->dtype == HCA_BF16 && !(mfma_rows_fit(params, ring_cap) && mfma_rows_fit(params, max_blocks)))
     return HCA_ERR_SHAPE;
+  st = check_epilogue(params, gate, vha_u, vha_v, vha_rank);
+  if (st != HCA_OK) return st;
   if (batch == 0) return HCA_OK;
   if (!seqlens || !cu_blocks || !q || !kw || !vw || !o) return HCA_ERR_NULL;
   if (max_blocks > 0 && (!kc || !vc)) return HCA_ERR_NULL;
@@ -193,6 +219,10 @@ hca_status hca_attend_decode(const hca_params* params, int32_t batch, int32_t ma
   a.vw = vw;
   a.o = o;
   a.ws = workspace;
+  a.gate = gate;
+  a.mix_u = vha_u;
+  a.mix_v = vha_v;
+  a.mix_rank = vha_u ? vha_rank : 0;
   hipStream_t s = (hipStream_t)stream;
   if (params->dtype == HCA_F32) return from_hip(hca::launch_decode_f32(a, s));
   const size_t need =
@@ -266,12 +296,28 @@ size_t hca_prefill_chunk_workspace_bytes(const hca_params* params, int32_t batch
   return 2 * staged_plane_bytes(params, batch, total_rows);
 }
 
+hca_status hca_attend_prefill_chunk_gated_vha(
+    const hca_params* params, int32_t batch, int32_t max_seqlen, int32_t total_rows, const int32_t* cu_seqlens,
+    const int32_t* pos0, const int32_t* cu_blocks, const void* q, const void* k, const void* v, const void* kc,
+    const void* vc, const void* kw, const void* vw, int32_t ring_cap, const float* gate, const float* vha_u,
+    const float* vha_v, int32_t vha_rank, void* o, void* workspace, size_t workspace_bytes, void* stream);
+
 hca_status hca_attend_prefill_chunk(const hca_params* params, int32_t batch, int32_t max_seqlen,
                                     int32_t total_rows, const int32_t* cu_seqlens, const int32_t* pos0,
                                     const int32_t* cu_blocks, const void* q, const void* k, const void* v,
                                     const void* kc, const void* vc, const void* kw, const void* vw,
                                     int32_t ring_cap, void* o, void* workspace, size_t workspace_bytes,
                                     void* stream) {
+  return hca_attend_prefill_chunk_gated_vha(params, batch, max_seqlen, total_rows, cu_seqlens, pos0, cu_blocks, q,
+                                            k, v, kc, vc, kw, vw, ring_cap, nullptr, nullptr, nullptr, 0, o,
+                                            workspace, workspace_bytes, stream);
+}
+
+hca_status hca_attend_prefill_chunk_gated_vha(
+    const hca_params* params, int32_t batch, int32_t max_seqlen, int32_t total_rows, const int32_t* cu_seqlens,
+    const int32_t* pos0, const int32_t* cu_blocks, const void* q, const void* k, const void* v, const void* kc,
+    const void* vc, const void* kw, const void* vw, int32_t ring_cap, const float* gate, const float* vha_u,
+    const float* vha_v, int32_t vha_rank, void* o, void* workspace, size_t workspace_bytes, void* stream) {
   hca_status st = check_params(params);
   if (st != HCA_OK) return st;
   if (batch < 0 || max_seqlen < 0 || total_rows < 0 || batch > 65535) return HCA_ERR_SHAPE;
@@ -282,6 +328,8 @@ hca_status hca_attend_prefill_chunk(const hca_params* params, int32_t batch, int
     return HCA_ERR_SHAPE;
   const long halo = params->window - 1;
   if (params->dtype == HCA_BF16 && !mfma_rows_fit(params, (long)max_seqlen + halo)) return HCA_ERR_SHAPE;
+  st = check_epilogue(params, gate, vha_u, vha_v, vha_rank);
+  if (st != HCA_OK) return st;
   if (((long)total_rows + (long)batch * halo) * params->num_kv_heads * params->head_dim * elem_bytes(params) >
       0xffffffffL)
     return HCA_ERR_SHAPE;  // staged rows are addressed with 32-bit buffer offsets
@@ -326,6 +374,10 @@ hca_status hca_attend_prefill_chunk(const hca_params* params, int32_t batch, int
   a.o = o;
   a.pos0 = pos0;
   a.halo = (int)halo;
+  a.gate = gate;
+  a.mix_u = vha_u;
+  a.mix_v = vha_v;
+  a.mix_rank = vha_u ? vha_rank : 0;
   return from_hip(params->dtype == HCA_BF16 ? hca::launch_prefill_bf16(a, s)
                                             : hca::launch_prefill_f32(a, s));
 }

@@ -114,6 +114,12 @@ struct DecodeArgs {
   const void* vw;
   void* o;
   void* ws;
+  // Optional epilogue (bf16 path), as in PrefillArgs: gate logits [B, Hq]
+  // fp32, mixing U, V [Hkv, 64, mix_rank] fp32 (NULL: none).
+  const float* gate;
+  const float* mix_u;
+  const float* mix_v;
+  int mix_rank;
 };
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);

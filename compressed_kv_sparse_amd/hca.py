@@ -23,6 +23,7 @@ _DTYPES = {torch.float32: HCA_F32, torch.bfloat16: HCA_BF16}
 EXPORTS = ("hca_compress", "hca_attend_prefill", "hca_decode_workspace_bytes",
            "hca_attend_decode", "hca_compress_chunk", "hca_ring_append",
            "hca_prefill_chunk_workspace_bytes", "hca_attend_prefill_chunk", "hca_attend_prefill_gated_vha",
+           "hca_attend_decode_gated_vha", "hca_attend_prefill_chunk_gated_vha",
            "hca_status_string", "hca_version")
 
 
@@ -77,6 +78,12 @@ def library() -> ctypes.CDLL:
     lib.hca_attend_prefill_gated_vha.argtypes = [P, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32,
                                                  vp, vp]
     lib.hca_attend_prefill_gated_vha.restype = ctypes.c_int
+    lib.hca_attend_decode_gated_vha.argtypes = [P, i32, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, i32,
+                                                vp, vp, sz, vp]
+    lib.hca_attend_decode_gated_vha.restype = ctypes.c_int
+    lib.hca_attend_prefill_chunk_gated_vha.argtypes = [P, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                       i32, vp, vp, vp, i32, vp, vp, sz, vp]
+    lib.hca_attend_prefill_chunk_gated_vha.restype = ctypes.c_int
     lib.hca_decode_workspace_bytes.argtypes = [P, i32, i32]
     lib.hca_decode_workspace_bytes.restype = sz
     lib.hca_attend_decode.argtypes = [P, i32, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
@@ -198,6 +205,24 @@ def hca_attend_decode(params: HcaParams, seqlens, cu_blocks, max_blocks: int, q,
     return o
 
 
+def hca_attend_decode_gated_vha(params: HcaParams, seqlens, cu_blocks, max_blocks: int, q, kc, vc, kw, vw,
+                                gate=None, vha_u=None, vha_v=None, workspace=None, o=None, stream=None):
+    """hca_attend_decode with the fused gate (logits [B, Hq]) and head mixing."""
+    batch = seqlens.numel()
+    if o is None:
+        o = torch.empty_like(q)
+    if workspace is None:
+        workspace = new_decode_workspace(params, batch, max_blocks, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rank = 0 if vha_u is None else int(vha_u.shape[-1])
+    st = library().hca_attend_decode_gated_vha(ctypes.byref(params), batch, int(max_blocks), _ptr(seqlens),
+                                               _ptr(cu_blocks), _ptr(q), _ptr(kc), _ptr(vc), _ptr(kw), _ptr(vw),
+                                               int(kw.shape[1]), _ptr(gate), _ptr(vha_u), _ptr(vha_v), rank,
+                                               _ptr(o), _ptr(workspace), ws_bytes, _stream(stream))
+    _check("hca_attend_decode_gated_vha", st)
+    return o
+
+
 def default_scale(head_dim: int) -> float:
     return 1.0 / math.sqrt(head_dim)
 
@@ -253,4 +278,24 @@ def hca_attend_prefill_chunk(params: HcaParams, cu_seqlens, pos0, cu_blocks, max
                                             int(kw.shape[1]), _ptr(o), _ptr(workspace), ws_bytes,
                                             _stream(stream))
     _check("hca_attend_prefill_chunk", st)
+    return o
+
+
+def hca_attend_prefill_chunk_gated_vha(params: HcaParams, cu_seqlens, pos0, cu_blocks, max_seqlen: int, q, k, v,
+                                       kc, vc, kw, vw, gate=None, vha_u=None, vha_v=None, workspace=None, o=None,
+                                       stream=None):
+    """hca_attend_prefill_chunk with the fused gate (logits [N, Hq]) and head mixing."""
+    batch = pos0.numel()
+    total = q.shape[0]
+    if o is None:
+        o = torch.empty_like(q)
+    if workspace is None:
+        workspace = new_prefill_chunk_workspace(params, batch, total, q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    rank = 0 if vha_u is None else int(vha_u.shape[-1])
+    st = library().hca_attend_prefill_chunk_gated_vha(
+        ctypes.byref(params), batch, int(max_seqlen), int(total), _ptr(cu_seqlens), _ptr(pos0), _ptr(cu_blocks),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), _ptr(kw), _ptr(vw), int(kw.shape[1]), _ptr(gate),
+        _ptr(vha_u), _ptr(vha_v), rank, _ptr(o), _ptr(workspace), ws_bytes, _stream(stream))
+    _check("hca_attend_prefill_chunk_gated_vha", st)
     return o

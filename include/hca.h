@@ -270,6 +270,28 @@ HCA_API hca_status hca_attend_prefill_chunk(const hca_params* params, int32_t ba
                                     const void* kw, const void* vw, int32_t ring_cap, void* o,
                                     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * hca_attend_decode_gated_vha, hca_attend_prefill_chunk_gated_vha - the
+ * decode and chunk calls with the attention epilogue of
+ * hca_attend_prefill_gated_vha (same arguments and meaning; gate logits are
+ * [B, Hq] for decode and [N, Hq] for a chunk).  Decode applies it in the
+ * merge of the split partials (fp32 mixing), chunks in the prefill kernel.
+ * HCA_BF16 only.
+ */
+HCA_API hca_status hca_attend_decode_gated_vha(const hca_params* params, int32_t batch,
+                                       int32_t max_blocks, const int32_t* seqlens,
+                                       const int32_t* cu_blocks, const void* q, const void* kc,
+                                       const void* vc, const void* kw, const void* vw,
+                                       int32_t ring_cap, const float* gate, const float* vha_u,
+                                       const float* vha_v, int32_t vha_rank, void* o,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+HCA_API hca_status hca_attend_prefill_chunk_gated_vha(
+    const hca_params* params, int32_t batch, int32_t max_seqlen, int32_t total_rows,
+    const int32_t* cu_seqlens, const int32_t* pos0, const int32_t* cu_blocks, const void* q,
+    const void* k, const void* v, const void* kc, const void* vc, const void* kw, const void* vw,
+    int32_t ring_cap, const float* gate, const float* vha_u, const float* vha_v, int32_t vha_rank,
+    void* o, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 HCA_API const char* hca_status_string(hca_status status);
 

@@ -233,3 +233,23 @@ def test_gated_vha_validation(lib):
     assert call(_p(), max_seqlen=0) == OK
     # no epilogue: plain prefill, also in fp32
     assert call(_p(dtype=hca.HCA_F32, num_q_heads=4, head_dim=64), gate=NULL, u=NULL, v=NULL, max_seqlen=0) == OK
+
+
+def test_decode_and_chunk_epilogue_validation(lib):
+    f32 = _p(dtype=hca.HCA_F32, num_q_heads=4, head_dim=64)
+    # decode: params, batch, max_blocks, seqlens, cu_blocks, q, kc, vc, kw, vw, ring, gate, u, v, rank, o, ws, ws_bytes, stream
+    def dec(params, u=DUMMY, v=DUMMY, rank=8, batch=1):
+        return lib.hca_attend_decode_gated_vha(ctypes.byref(params), batch, 4, *([DUMMY] * 7), 128, DUMMY, u, v,
+                                               rank, DUMMY, DUMMY, 1 << 40, None)
+    assert dec(_p(), v=NULL) == ERR_NULL
+    assert dec(_p(), rank=40) == ERR_SHAPE
+    assert dec(f32) == ERR_UNSUPPORTED
+    assert dec(_p(), batch=0) == OK
+
+    def chk(params, u=DUMMY, v=DUMMY, rank=8, batch=1):
+        return lib.hca_attend_prefill_chunk_gated_vha(ctypes.byref(params), batch, 64, 64, *([DUMMY] * 10), 128,
+                                                      DUMMY, u, v, rank, DUMMY, DUMMY, 1 << 40, None)
+    assert chk(_p(), u=NULL) == ERR_NULL
+    assert chk(_p(), rank=0) == ERR_SHAPE
+    assert chk(_p(dtype=hca.HCA_F32, num_q_heads=4, head_dim=64, window=64)) == ERR_UNSUPPORTED
+    assert chk(_p(), batch=0) == OK

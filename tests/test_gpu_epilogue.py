@@ -11,7 +11,7 @@ import torch
 
 import compressed_kv_sparse_amd as hca
 import oracle
-from hca_workloads import CONFIGS, prefill_inputs
+from hca_workloads import CONFIGS, decode_inputs, prefill_inputs, ring_from_raw
 from parity_util import assert_close, params_for
 
 pytestmark = pytest.mark.gpu
@@ -88,3 +88,50 @@ def test_zero_mixing_is_plain_prefill():
                                      inp["v"], kc, vc)
     torch.cuda.synchronize()
     assert torch.equal(o_mix.view(torch.int16), o_plain.view(torch.int16))
+
+
+@pytest.mark.parametrize("lens,rank,with_gate", [
+    ([131072] * 4 + [1, 200, 5000], 16, True),    # several splits per sequence, short ones with one
+    ([70000, 3000], 32, False),
+    ([777], 1, True),
+])
+def test_decode_gated_vha(lens, rank, with_gate):
+    c = dataclasses.replace(CONFIGS["decode_64x128k"], decode_batch=len(lens))
+    inp = decode_inputs(c, DEV, lens=lens, seed=431)
+    p = params_for(c)
+    u, v = _factors(1, rank, seed=432)
+    gate = None
+    if with_gate:
+        g = torch.Generator(device=DEV).manual_seed(433)
+        gate = torch.randn((len(lens), 64), generator=g, device=DEV) * 2
+    o = hca.hca_attend_decode_gated_vha(p, inp["seqlens"], inp["cu_blocks"], inp["max_blocks"], inp["q"], inp["kc"],
+                                        inp["vc"], inp["kw"], inp["vw"], gate=gate, vha_u=u, vha_v=v)
+    torch.cuda.synchronize()
+    ref = oracle.attend_decode(inp["q"].cpu(), inp["kc"].cpu(), inp["vc"].cpu(), inp["kw"].cpu(), inp["vw"].cpu(),
+                               lens, inp["cu_blocks_host"], c.window)
+    ref = oracle.head_mix_and_gate(ref, u.cpu(), v.cpu(), None if gate is None else gate.cpu())
+    # a 1-token sequence's output is one value row, mixed: |O| passes 4, where
+    # bf16 rounding alone reaches 0.0156
+    assert_close(o, ref, torch.bfloat16, f"decode gated VHA lens={lens[:3]} rank={rank} gate={with_gate}",
+                 beyond_rounding=True)
+
+
+def test_chunk_gated_vha():
+    """A chunk at position 1500 of a 2600-token sequence with the epilogue:
+    rows 1500.. of the oracle's whole-sequence prefill, mixed and gated."""
+    c, inp, p, kc, vc = _case([2600], 1, seed=441)
+    p0, n, R = 1500, 1100, 128
+    u, v = _factors(1, 16, seed=442)
+    g = torch.Generator(device=DEV).manual_seed(443)
+    gate = torch.randn((n, 64), generator=g, device=DEV) * 2
+    kw = ring_from_raw(inp["k"], p0, R)[None].contiguous()
+    vw = ring_from_raw(inp["v"], p0, R)[None].contiguous()
+    i32 = lambda x: torch.tensor(x, dtype=torch.int32, device=DEV)  # noqa: E731
+    sl = slice(p0, p0 + n)
+    o = hca.hca_attend_prefill_chunk_gated_vha(p, i32([0, n]), i32([p0]), inp["cu_blocks"], n,
+                                               inp["q"][sl].contiguous(), inp["k"][sl].contiguous(),
+                                               inp["v"][sl].contiguous(), kc, vc, kw, vw, gate=gate, vha_u=u, vha_v=v)
+    torch.cuda.synchronize()
+    full = _oracle(c, inp)
+    ref = oracle.head_mix_and_gate(full[p0:p0 + n], u.cpu(), v.cpu(), gate.cpu())
+    assert_close(o, ref, torch.bfloat16, "chunk gated VHA")

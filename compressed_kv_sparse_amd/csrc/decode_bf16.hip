@@ -9,9 +9,9 @@
 //
 // Design (gfx950): one workgroup of 4 wavefronts x 16 heads per (sequence,
 // KV head, key split) streams its key range through LDS (tiles of 32 keys,
-// double buffered) and writes fp32 partials (m, l, O/l) to the workspace; a
-// second, fully parallel kernel merges them in split order, so the result
-// is deterministic.  Scores use the transposed product S^T = K Q^T and the
+// double buffered) and writes partials (m, l in fp32, O/l in bf16) to the
+// workspace; a second, fully parallel kernel merges them in split order, so
+// the result is deterministic.  Scores use the transposed product S^T = K Q^T and the
 // output O^T += V^T P^T as in prefill, with the softmax schedule of
 // bf16_tiles.h (no accumulator rescaling).
 #include <algorithm>

@@ -510,7 +510,7 @@ __device__ __forceinline__ void store_output(const Ctx& c, PState& st, float* li
       typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
       const u32x2 v0 = *(const u32x2 HCA_LDS*)src, v1 = *(const u32x2 HCA_LDS*)(src + 8);
       const u32x4 v = {v0[0], v0[1], v1[0], v1[1]};
-      *(u32x4*)(obase + (size_t)row * D + cw) = v;
+      __builtin_nontemporal_store(v, (u32x4*)(obase + (size_t)row * D + cw));
     }
     return;
   }
@@ -530,10 +530,12 @@ __device__ __forceinline__ void store_output(const Ctx& c, PState& st, float* li
       }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's LDS writes are done
     bf16* og = obase + (size_t)(32 * (hg ^ g)) * D;
+    // streaming stores: each output row is written once and not read here
 #pragma unroll 4
     for (int i = 0; i < 16; ++i) {
       const int row = 2 * i + hr;
-      *(bf16x8*)(og + (size_t)row * D + cw) = *(const bf16x8 HCA_LDS*)(stg + row * OSTR + cw * 2);
+      __builtin_nontemporal_store(*(const bf16x8 HCA_LDS*)(stg + row * OSTR + cw * 2),
+                                  (bf16x8*)(og + (size_t)row * D + cw));
     }
   }
 }

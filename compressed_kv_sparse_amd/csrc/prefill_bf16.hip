@@ -623,11 +623,9 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, int pair0, in
   c.sc2 = a.scale * kLog2e;
 
   // the empty parts of the first pipeline stages read the K and V buffers:
-  // make them finite
-  for (int o = threadIdx.x * 16; !LO && o < KTILE; o += 256 * 16) {
-    *(u32x4 HCA_LDS*)(c.kb[0] + o) = u32x4{};
-    *(u32x4 HCA_LDS*)(c.kb[1] + o) = u32x4{};
-  }
+  // make them finite.  Not kb[0]: the pass's K(0) load fills all of it, and
+  // other waves may issue that load before this wave's stores land.
+  for (int o = threadIdx.x * 16; !LO && o < KTILE; o += 256 * 16) *(u32x4 HCA_LDS*)(c.kb[1] + o) = u32x4{};
   for (int o = threadIdx.x * 16; !LO && o < VTILE; o += 256 * 16) {
     *(u32x4 HCA_LDS*)(c.vb[0] + o) = u32x4{};
     *(u32x4 HCA_LDS*)(c.vb[1] + o) = u32x4{};

@@ -386,28 +386,37 @@ __device__ __forceinline__ void attend_pair(const Ctx& c, const bf16x8 (&qf)[DST
 // matrix-core products:
 //   Z [ranks x cols] = V^T O: A = V^T (constant), B = O read back transposed
 //     from bf16 rows (one per head) staged in the wave's own LDS buffer;
-//   y^T = acc^T + Z^T (U^T diag(l)): A = Z^T straight from Z's accumulators
-//     (lane = column), B = U scaled by each head's l, C = the tile of acc
-//     (read, never written back), so that y / l = O + U Z.
+//   M^T = Z^T U^T: A = Z^T straight from Z's accumulators (lane = column),
+//     B = U^T, from zero; then y = sigmoid(g) (acc / l + M) elementwise
+//     (the accumulators are only read).
 // The ranks run in the k-slot order Z's accumulator layout gives (lane
 // group h: ranks 4h..4h+3, 8+4h..8+4h+3 of each 16), and V^T follows the
-// head order of the transposed reads.  y is scaled, rounded and written over
-// the tile's staged columns (already read), then all 64 rows are stored.
+// head order of the transposed reads.  V^T, U^T and the gate come from LDS,
+// loaded at the start of the pass.  y is rounded and written over the
+// tile's staged columns (already read), then all 64 rows are stored.
 constexpr int MSTR = 520;  // LDS bytes per staged head row (64 rows fill a K buffer)
 
 __device__ __forceinline__ int kslot_index(int h, int j) { return j < 4 ? 4 * h + j : 8 + 4 * h + (j - 4); }
 
 __device__ __forceinline__ float sigmoid(float x) { return 1.f / (1.f + __expf(-x)); }
 
+// Epilogue inputs in LDS, written at the start of the pass (the epilogue's
+// global loads would otherwise stall every workgroup's tail): the mixing
+// factors as bf16 MFMA fragments and the gate's sigmoid of both positions.
+constexpr int kEpiV = 0;        // V^T: [rank 32][k-step 4][lane half 2][8 heads] bf16
+constexpr int kEpiU = 4096;     // U^T: [head 64][k-step 2][lane half 2][8 ranks] bf16
+constexpr int kEpiGate = 8192;  // [position 2][head 64] fp32
+constexpr int kEpiBytes = 8704;
+
 // O = acc / l for all 64 heads of the wave's position over its column half,
 // rounded to bf16.  1/l of the partner's rows comes through LDS.  The
 // half-rows are staged in the wave's own buffer, one head group (32 rows x
 // OSTR bytes) at a time, and stored two per instruction (lanes 0-31 row 2i,
 // lanes 32-63 row 2i+1; 512 contiguous bytes each).  EPI: the head mixing
-// and the per-head gate first (output row qrow of the query tensor).
+// and the per-head gate first, with their inputs from `epi`.
 template <bool EPI>
 __device__ __forceinline__ void store_output(const Ctx& c, PState& st, float* linv, bf16* obase,
-                                             bool row_ok, const PrefillArgs& a, int kvh, int qrow) {
+                                             bool row_ok, const PrefillArgs& a, const char HCA_LDS* epi) {
   const int lane = c.lane, wave = c.wave, hg = wave & 1;
   const float lt = st.l + __shfl_xor(st.l, 32);
   const float inv_own = 1.f / lt;
@@ -420,11 +429,11 @@ __device__ __forceinline__ void store_output(const Ctx& c, PState& st, float* li
     const int h = lane >> 5, r = lane & 31;
     const bool mix = a.mix_u != nullptr;
     const int rank = a.mix_rank;
-    float sc[2] = {inv_own, inv_par};  // output scale of head group g: 1/l, times the gate
+    float gs[2] = {1.f, 1.f};  // gate of head group g (own, partner)
     if (a.gate) {
-      const float* gr = a.gate + (size_t)qrow * a.hq + kvh * G + r;
-      sc[0] *= sigmoid(gr[32 * hg]);
-      sc[1] *= sigmoid(gr[32 * (hg ^ 1)]);
+      const float HCA_LDS* gr = (const float HCA_LDS*)(epi + kEpiGate) + 64 * (wave >> 1) + r;
+      gs[0] = gr[32 * hg];
+      gs[1] = gr[32 * (hg ^ 1)];
     }
     bf16x8 vt[4], ut[2][2];
     if (mix) {
@@ -443,24 +452,14 @@ __device__ __forceinline__ void store_output(const Ctx& c, PState& st, float* li
             *(bf16x4 HCA_LDS*)(rowp + (32 * ct + 8 * q4) * 2) = v;
           }
       }
-      const float* vg = a.mix_v + (size_t)kvh * G * rank;
-      const float* ug = a.mix_u + (size_t)kvh * G * rank;
 #pragma unroll
-      for (int s = 0; s < 4; ++s)  // A = V^T, k-step s: heads 16s + kslot_index(h, j)
+      for (int s = 0; s < 4; ++s)  // A = V^T, k-step s
+        vt[s] = *(const bf16x8 HCA_LDS*)(epi + kEpiV + ((r * 4 + s) * 2 + h) * 16);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) vt[s][j] = (bf16)(r < rank ? vg[(16 * s + kslot_index(h, j)) * rank + r] : 0.f);
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {  // B = U^T diag(l) of head group g, k-step s2: ranks 16 s2 + kslot_index(h, j)
-        const int hd = 32 * (hg ^ g) + r;
-        const float l = 1.f / (g ? inv_par : inv_own);
+      for (int g = 0; g < 2; ++g)  // B = U^T of head group g, k-step s2
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int rr = 16 * s2 + kslot_index(h, j);
-            ut[g][s2][j] = (bf16)(rr < rank ? ug[hd * rank + rr] * l : 0.f);
-          }
-      }
+          ut[g][s2] = *(const bf16x8 HCA_LDS*)(epi + kEpiU + (((32 * (hg ^ g) + r) * 2 + s2) * 2 + h) * 16);
     }
     const int off = (4 * h + ((lane & 15) >> 2)) * MSTR + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
     __builtin_amdgcn_sched_barrier(0);
@@ -484,17 +483,18 @@ __device__ __forceinline__ void store_output(const Ctx& c, PState& st, float* li
       }
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        f32x16 y = st.o[g][ct];
+        f32x16 y = {};  // the mixing term of these 32 heads x 32 columns
         if (mix) {
           y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za[0], ut[g][0], y, 0, 0, 0);
           if (rank > 16) y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za[1], ut[g][1], y, 0, 0, 0);
         }
+        const float inv = g ? inv_par : inv_own;
         char HCA_LDS* rowp = stg + (32 * (hg ^ g) + r) * MSTR + h * 8 + 64 * ct;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           bf16x4 v;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = (bf16)(y[4 * q4 + i] * sc[g]);
+          for (int i = 0; i < 4; ++i) v[i] = (bf16)((st.o[g][ct][4 * q4 + i] * inv + y[4 * q4 + i]) * gs[g]);
           *(bf16x4 HCA_LDS*)(rowp + 16 * q4) = v;
         }
       }
@@ -540,6 +540,39 @@ __device__ __forceinline__ void store_output(const Ctx& c, PState& st, float* li
   }
 }
 
+// The epilogue's inputs into LDS, once per workgroup: V^T and U^T of KV head
+// kvh as bf16 fragments (rank rows past `mix_rank` zero) and the gate's
+// sigmoid for the pair's positions (rows row0, row0 + 1; the second only if
+// it exists).  All loads are in bounds and issued before the first wait.
+__device__ __forceinline__ void load_epilogue_inputs(const PrefillArgs& a, char HCA_LDS* epi, int kvh, int row0,
+                                                     bool t1_ok) {
+  const int i8 = threadIdx.x, gh = i8 & 1;
+  bf16x8 fv = {}, fu = {};
+  float gv = 0.f;
+  if (a.mix_u) {
+    const int rank = a.mix_rank;
+    const float* vg = a.mix_v + (size_t)kvh * G * rank;
+    const float* ug = a.mix_u + (size_t)kvh * G * rank;
+    const int rv = i8 >> 3, sv = (i8 >> 1) & 3;  // V^T chunk: rank rv, heads 16 sv + kslot_index(gh, j)
+    const int hu = i8 >> 2, su = (i8 >> 1) & 1;  // U^T chunk: head hu, ranks 16 su + kslot_index(gh, j)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int ru = 16 * su + kslot_index(gh, j);
+      const float x = vg[(16 * sv + kslot_index(gh, j)) * rank + min(rv, rank - 1)];
+      const float y = ug[hu * rank + min(ru, rank - 1)];
+      fv[j] = (bf16)(rv < rank ? x : 0.f);
+      fu[j] = (bf16)(ru < rank ? y : 0.f);
+    }
+  }
+  const int pos = t1_ok ? (i8 >> 6) & 1 : 0;
+  if (a.gate) gv = a.gate[(size_t)(row0 + pos) * a.hq + kvh * G + (i8 & 63)];
+  if (a.mix_u) {
+    *(bf16x8 HCA_LDS*)(epi + kEpiV + 16 * i8) = fv;
+    *(bf16x8 HCA_LDS*)(epi + kEpiU + 16 * i8) = fu;
+  }
+  if (a.gate && i8 < 128) ((float HCA_LDS*)(epi + kEpiGate))[i8] = sigmoid(gv);
+}
+
 // Keys of position pair (t0, t_last): the later position's complete entries
 // plus the raw rows from the earlier position's window start to t_last.
 __host__ __device__ inline int pair_keys(int t0, int t_last, int window) {
@@ -556,7 +589,8 @@ __host__ __device__ inline int pair_keys(int t0, int t_last, int window) {
 template <bool LO, bool EPI>
 __device__ __forceinline__ void prefill_body(const PrefillArgs& a, int pair0, int bx, char HCA_LDS* k0_s,
                                              char HCA_LDS* k1_s, char HCA_LDS* v0_s, char HCA_LDS* v1_s,
-                                             char HCA_LDS* w0_s, char HCA_LDS* w1_s, int* flag_s, float* linv_s) {
+                                             char HCA_LDS* w0_s, char HCA_LDS* w1_s, int* flag_s, float* linv_s,
+                                             char HCA_LDS* epi_s) {
   const int b = blockIdx.y, kvh = blockIdx.z;
 
   const int start = a.cu_seqlens[b];
@@ -640,10 +674,13 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, int pair0, in
 #pragma unroll
     for (int k = 0; k < DSTEPS; ++k) qf[k] = *(const bf16x8*)(qrow + 16 * k);
   }
+  // the epilogue's inputs: their latency overlaps the Q loads, and the
+  // pass's barriers order the LDS writes before their use
+  if constexpr (EPI) load_epilogue_inputs(a, epi_s, kvh, start + (t0 - p0), t1_ok);
   PState st;
   attend_pair<LO>(c, qf, st);
   bf16* obase = (bf16*)a.o + ((size_t)qrow * a.hq + kvh * G) * D + hg * 256;
-  store_output<EPI>(c, st, linv_s, obase, row_ok, a, kvh, qrow);
+  store_output<EPI>(c, st, linv_s, obase, row_ok, a, epi_s);
 }
 
 // Grid (lo_n + npairs - hi_begin, batch, Hkv), 256 threads: workgroup x <
@@ -661,8 +698,9 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_kernel(PrefillArgs a, int
   __shared__ __attribute__((aligned(16))) char w1_s[4 * WSLOT];
   __shared__ int flag_s[2];
   __shared__ float linv_s[4 * 32];
+  __shared__ __attribute__((aligned(16))) char epi_s[EPI ? kEpiBytes : 16];
 #define HCA_LDS_ARGS (char HCA_LDS*)k0_s, (char HCA_LDS*)k1_s, (char HCA_LDS*)v0_s, (char HCA_LDS*)v1_s, \
-    (char HCA_LDS*)w0_s, (char HCA_LDS*)w1_s, flag_s, linv_s
+    (char HCA_LDS*)w0_s, (char HCA_LDS*)w1_s, flag_s, linv_s, (char HCA_LDS*)epi_s
   if ((int)blockIdx.x < lo_n)
     prefill_body<true, EPI>(a, 0, blockIdx.x, HCA_LDS_ARGS);
   else

@@ -16,3 +16,4 @@ from .hca_oracle import (  # noqa: F401
     pooling_weights,
     visible_sets,
 )
+from .hca_backward import attend_prefill_backward, loss_for_gradcheck  # noqa: F401,E402

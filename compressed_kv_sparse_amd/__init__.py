@@ -1,4 +1,4 @@
-"""HCA (Heavily Compressed Attention) layer forward for AMD MI355X.
+"""HCA (Heavily Compressed Attention) layer forward and backward for AMD MI355X.
 
 The computation lives in libhca.so (hand-written HIP kernels for gfx950 behind
 the C ABI of include/hca.h); this package is its Python binding.  Build the
@@ -14,7 +14,10 @@ from .hca import (  # noqa: F401
     hca_attend_decode,
     hca_attend_decode_gated_vha,
     hca_attend_prefill,
+    hca_attend_prefill_backward,
+    hca_attend_prefill_backward_workspace_bytes,
     hca_attend_prefill_gated_vha,
+    hca_attend_prefill_lse,
     hca_attend_prefill_chunk,
     hca_attend_prefill_chunk_gated_vha,
     hca_compress,
@@ -26,6 +29,7 @@ from .hca import (  # noqa: F401
     hca_version,
     library,
     make_params,
+    new_backward_workspace,
     new_decode_workspace,
     new_prefill_chunk_workspace,
 )

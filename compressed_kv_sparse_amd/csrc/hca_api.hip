@@ -118,11 +118,38 @@ hca_status hca_attend_prefill(const hca_params* params, int32_t batch, int32_t m
                                       nullptr, nullptr, nullptr, 0, o, stream);
 }
 
+static hca_status prefill_common(const hca_params* params, int32_t batch, int32_t max_seqlen,
+                                 const int32_t* cu_seqlens, const int32_t* cu_blocks, const void* q, const void* k,
+                                 const void* v, const void* kc, const void* vc, const float* gate,
+                                 const float* vha_u, const float* vha_v, int32_t vha_rank, void* o, float* lse,
+                                 void* stream);
+
 hca_status hca_attend_prefill_gated_vha(const hca_params* params, int32_t batch, int32_t max_seqlen,
                                         const int32_t* cu_seqlens, const int32_t* cu_blocks, const void* q,
                                         const void* k, const void* v, const void* kc, const void* vc,
                                         const float* gate, const float* vha_u, const float* vha_v,
                                         int32_t vha_rank, void* o, void* stream) {
+  return prefill_common(params, batch, max_seqlen, cu_seqlens, cu_blocks, q, k, v, kc, vc, gate, vha_u, vha_v,
+                        vha_rank, o, nullptr, stream);
+}
+
+hca_status hca_attend_prefill_lse(const hca_params* params, int32_t batch, int32_t max_seqlen,
+                                  const int32_t* cu_seqlens, const int32_t* cu_blocks, const void* q, const void* k,
+                                  const void* v, const void* kc, const void* vc, void* o, float* lse,
+                                  void* stream) {
+  const hca_status st = check_params(params);
+  if (st != HCA_OK) return st;
+  if (params->dtype != HCA_BF16) return HCA_ERR_UNSUPPORTED;  // saved for the matrix-core backward
+  if (batch > 0 && max_seqlen > 0 && !lse) return HCA_ERR_NULL;
+  return prefill_common(params, batch, max_seqlen, cu_seqlens, cu_blocks, q, k, v, kc, vc, nullptr, nullptr, nullptr,
+                        0, o, lse, stream);
+}
+
+static hca_status prefill_common(const hca_params* params, int32_t batch, int32_t max_seqlen,
+                                 const int32_t* cu_seqlens, const int32_t* cu_blocks, const void* q, const void* k,
+                                 const void* v, const void* kc, const void* vc, const float* gate,
+                                 const float* vha_u, const float* vha_v, int32_t vha_rank, void* o, float* lse,
+                                 void* stream) {
   hca_status st = check_params(params);
   if (st != HCA_OK) return st;
   if (batch < 0 || max_seqlen < 0 || batch > 65535) return HCA_ERR_SHAPE;
@@ -155,9 +182,68 @@ hca_status hca_attend_prefill_gated_vha(const hca_params* params, int32_t batch,
   a.mix_u = vha_u;
   a.mix_v = vha_v;
   a.mix_rank = vha_u ? vha_rank : 0;
+  a.lse = lse;
   hipStream_t s = (hipStream_t)stream;
   return from_hip(params->dtype == HCA_BF16 ? hca::launch_prefill_bf16(a, s)
                                             : hca::launch_prefill_f32(a, s));
+}
+
+size_t hca_attend_prefill_backward_workspace_bytes(const hca_params* params, int32_t batch, int32_t total_tokens,
+                                                   int32_t total_blocks, int32_t max_seqlen) {
+  if (check_params(params) != HCA_OK || batch < 0 || total_tokens < 0 || total_blocks < 0 || max_seqlen < 0) return 0;
+  if (params->dtype != HCA_BF16 || !mfma_shape(params)) return 0;
+  return hca::backward_workspace_bytes(batch, params->num_q_heads, params->num_kv_heads, total_tokens, total_blocks,
+                                       max_seqlen, params->window);
+}
+
+hca_status hca_attend_prefill_backward(const hca_params* params, int32_t batch, int32_t max_seqlen,
+                                       int32_t total_tokens, int32_t total_blocks, const int32_t* cu_seqlens,
+                                       const int32_t* cu_blocks, const void* q, const void* k, const void* v,
+                                       const float* w, const void* kc, const void* vc, const void* o,
+                                       const float* lse, const void* dout, void* dq, void* dk, void* dv, float* dw,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  hca_status st = check_params(params);
+  if (st != HCA_OK) return st;
+  if (batch < 0 || max_seqlen < 0 || batch > 65535 || total_tokens < 0 || total_blocks < 0) return HCA_ERR_SHAPE;
+  if (params->dtype != HCA_BF16 || !mfma_shape(params)) return HCA_ERR_UNSUPPORTED;
+  if (!mfma_rows_fit(params, max_seqlen)) return HCA_ERR_SHAPE;
+  if ((long)total_tokens < (long)max_seqlen || (long)total_blocks * hca::kBlock > (long)total_tokens)
+    return HCA_ERR_SHAPE;
+  if (!w || !dw) return HCA_ERR_NULL;  // dw [Hkv, 128] is written even without tokens
+  const size_t need = hca::backward_workspace_bytes(batch, params->num_q_heads, params->num_kv_heads, total_tokens,
+                                                    total_blocks, max_seqlen, params->window);
+  if (!workspace || workspace_bytes < need) return HCA_ERR_WORKSPACE;
+  const bool rows = batch > 0 && max_seqlen > 0;
+  if (rows && (!cu_seqlens || !cu_blocks || !q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv))
+    return HCA_ERR_NULL;
+  if (rows && max_seqlen >= hca::kBlock && (!kc || !vc)) return HCA_ERR_NULL;
+  hca::BackwardArgs a{};
+  a.batch = rows ? batch : 0;
+  a.max_seqlen = rows ? max_seqlen : 0;
+  a.total_tokens = total_tokens;
+  a.total_blocks = rows ? total_blocks : 0;
+  a.hq = params->num_q_heads;
+  a.hkv = params->num_kv_heads;
+  a.d = params->head_dim;
+  a.window = params->window;
+  a.scale = scale_of(params);
+  a.cu_seqlens = cu_seqlens;
+  a.cu_blocks = cu_blocks;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.kc = kc;
+  a.vc = vc;
+  a.o = o;
+  a.dout = dout;
+  a.w = w;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dw = dw;
+  a.ws = workspace;
+  return from_hip(hca::launch_backward_bf16(a, (hipStream_t)stream));
 }
 
 size_t hca_decode_workspace_bytes(const hca_params* params, int32_t batch, int32_t max_blocks) {

@@ -81,6 +81,9 @@ struct PrefillArgs {
   const float* mix_u;
   const float* mix_v;
   int mix_rank;
+  // Optional (bf16 path): per-row log-sum-exp of the scaled scores [N, Hq]
+  // fp32, natural log, for the backward (NULL: not written).
+  float* lse;
 };
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
@@ -132,5 +135,48 @@ struct DecodePlan {
 };
 DecodePlan decode_plan(int batch, int hkv, int max_blocks, int window);
 size_t decode_workspace_bytes_bf16(int batch, int hkv, int max_blocks, int window);
+
+// Backward of the bf16 prefill (backward_bf16.hip).  Inputs as in the
+// forward plus the pooling logits w [Hkv, 128], the forward output o, its
+// lse [N, Hq] and dout [N, Hq, d]; outputs dq [N, Hq, d], dk, dv [N, Hkv, d]
+// (bf16) and dw [Hkv, 128] (fp32).  The workspace pointers below ws are
+// carved by the launcher.
+struct BackwardArgs {
+  int batch, max_seqlen, total_tokens, total_blocks, hq, hkv, d, window;
+  float scale;
+  const int* cu_seqlens;
+  const int* cu_blocks;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* kc;
+  const void* vc;
+  const void* o;
+  const void* dout;
+  const float* w;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dw;
+  void* ws;
+  // set by the launcher
+  int comp_tiles;
+  float* delta;    // dO . O per row [N, Hq]
+  float* dk_rows;  // raw-row gradients from the window keys [N, Hkv, d]
+  float* dv_rows;
+  float* part_k;   // compressed-entry partials [B, Hkv, comp_tiles, nsplit, 32, d]
+  float* part_v;
+  float* gbuf;     // per entry terms of the pooling-logit gradient [total_blocks, Hkv, 128]
+};
+// Work split of the dK/dV kernel: raw tiles of 32 rows; compressed tiles of
+// 32 entries, each over nsplit runs of pch positions.
+struct BackwardPlan {
+  int raw_tiles, comp_tiles, nsplit, pch;
+};
+BackwardPlan backward_plan(int batch, int hkv, int max_seqlen, int window);
+size_t backward_workspace_bytes(int batch, int hq, int hkv, int total_tokens, int total_blocks, int max_seqlen,
+                                int window);
+hipError_t launch_backward_bf16(BackwardArgs a, hipStream_t s);
 
 }  // namespace hca

@@ -394,6 +394,7 @@ __device__ __forceinline__ void attend_pair(const Ctx& c, const bf16x8 (&qf)[DST
 // head order of the transposed reads.  V^T, U^T and the gate come from LDS,
 // loaded at the start of the pass.  y is rounded and written over the
 // tile's staged columns (already read), then all 64 rows are stored.
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr int MSTR = 520;  // LDS bytes per staged head row (64 rows fill a K buffer)
 
 __device__ __forceinline__ int kslot_index(int h, int j) { return j < 4 ? 4 * h + j : 8 + 4 * h + (j - 4); }
@@ -416,7 +417,8 @@ constexpr int kEpiBytes = 8704;
 // and the per-head gate first, with their inputs from `epi`.
 template <bool EPI>
 __device__ __forceinline__ void store_output(const Ctx& c, PState& st, float* linv, bf16* obase,
-                                             bool row_ok, const PrefillArgs& a, const char HCA_LDS* epi) {
+                                             bool row_ok, const PrefillArgs& a, const char HCA_LDS* epi,
+                                             float* lse_row) {
   const int lane = c.lane, wave = c.wave, hg = wave & 1;
   const float lt = st.l + __shfl_xor(st.l, 32);
   const float inv_own = 1.f / lt;
@@ -424,6 +426,9 @@ __device__ __forceinline__ void store_output(const Ctx& c, PState& st, float* li
   __syncthreads();  // every wave is past its last tile: K/V buffers are free
   const float inv_par = linv[(wave ^ 1) * 32 + (lane & 31)];
   if (!row_ok) return;
+  // log-sum-exp of the row's scaled scores (natural log): the weights are
+  // exp2(s sc2 - m), so sum exp(scale s) = 2^m lt
+  if (lse_row && lane < 32) lse_row[lane] = (st.m + __log2f(lt)) * kLn2;
   char HCA_LDS* stg = wave == 0 ? c.kb[0] : wave == 1 ? c.kb[1] : wave == 2 ? c.vb[0] : c.vb[1];
   if constexpr (EPI) {
     const int h = lane >> 5, r = lane & 31;
@@ -680,7 +685,8 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, int pair0, in
   PState st;
   attend_pair<LO>(c, qf, st);
   bf16* obase = (bf16*)a.o + ((size_t)qrow * a.hq + kvh * G) * D + hg * 256;
-  store_output<EPI>(c, st, linv_s, obase, row_ok, a, epi_s);
+  float* lse_row = a.lse ? a.lse + (size_t)qrow * a.hq + kvh * G + 32 * hg : nullptr;
+  store_output<EPI>(c, st, linv_s, obase, row_ok, a, epi_s, lse_row);
 }
 
 // Grid (lo_n + npairs - hi_begin, batch, Hkv), 256 threads: workgroup x <

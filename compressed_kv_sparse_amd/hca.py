@@ -24,6 +24,7 @@ EXPORTS = ("hca_compress", "hca_attend_prefill", "hca_decode_workspace_bytes",
            "hca_attend_decode", "hca_compress_chunk", "hca_ring_append",
            "hca_prefill_chunk_workspace_bytes", "hca_attend_prefill_chunk", "hca_attend_prefill_gated_vha",
            "hca_attend_decode_gated_vha", "hca_attend_prefill_chunk_gated_vha",
+           "hca_attend_prefill_lse", "hca_attend_prefill_backward_workspace_bytes", "hca_attend_prefill_backward",
            "hca_status_string", "hca_version")
 
 
@@ -97,6 +98,13 @@ def library() -> ctypes.CDLL:
     lib.hca_attend_prefill_chunk.argtypes = [P, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                              i32, vp, vp, sz, vp]
     lib.hca_attend_prefill_chunk.restype = ctypes.c_int
+    lib.hca_attend_prefill_lse.argtypes = [P, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.hca_attend_prefill_lse.restype = ctypes.c_int
+    lib.hca_attend_prefill_backward_workspace_bytes.argtypes = [P, i32, i32, i32, i32]
+    lib.hca_attend_prefill_backward_workspace_bytes.restype = sz
+    lib.hca_attend_prefill_backward.argtypes = [P, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hca_attend_prefill_backward.restype = ctypes.c_int
     lib.hca_status_string.argtypes = [ctypes.c_int]
     lib.hca_status_string.restype = ctypes.c_char_p
     lib.hca_version.argtypes = []
@@ -176,6 +184,57 @@ def hca_attend_prefill_gated_vha(params: HcaParams, cu_seqlens, cu_blocks, max_s
                                                 _stream(stream))
     _check("hca_attend_prefill_gated_vha", st)
     return o
+
+
+def hca_attend_prefill_lse(params: HcaParams, cu_seqlens, cu_blocks, max_seqlen: int, q, k, v, kc, vc,
+                           o=None, lse=None, stream=None):
+    """hca_attend_prefill that also saves the per-row log-sum-exp of the
+    scaled scores (fp32 [N_tok, Hq], natural log).  Returns (o, lse)."""
+    batch = cu_seqlens.numel() - 1
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    st = library().hca_attend_prefill_lse(ctypes.byref(params), batch, int(max_seqlen), _ptr(cu_seqlens),
+                                          _ptr(cu_blocks), _ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc),
+                                          _ptr(o), _ptr(lse), _stream(stream))
+    _check("hca_attend_prefill_lse", st)
+    return o, lse
+
+
+def hca_attend_prefill_backward_workspace_bytes(params: HcaParams, batch: int, total_tokens: int,
+                                                total_blocks: int, max_seqlen: int) -> int:
+    return int(library().hca_attend_prefill_backward_workspace_bytes(
+        ctypes.byref(params), int(batch), int(total_tokens), int(total_blocks), int(max_seqlen)))
+
+
+def new_backward_workspace(params: HcaParams, batch: int, total_tokens: int, total_blocks: int, max_seqlen: int,
+                           device=None):
+    """Workspace of the size hca_attend_prefill_backward needs."""
+    n = hca_attend_prefill_backward_workspace_bytes(params, batch, total_tokens, total_blocks, max_seqlen)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device or torch.cuda.current_device())
+
+
+def hca_attend_prefill_backward(params: HcaParams, cu_seqlens, cu_blocks, max_seqlen: int, total_blocks: int,
+                                q, k, v, w, kc, vc, o, lse, dout, workspace=None, dq=None, dk=None, dv=None,
+                                dw=None, stream=None):
+    """Gradients (dq, dk, dv, dw) of a loss through pooling + prefill
+    attention, given dout = dL/dO.  Returns (dq, dk, dv, dw)."""
+    batch = cu_seqlens.numel() - 1
+    ntok = q.shape[0]
+    if workspace is None:
+        workspace = new_backward_workspace(params, batch, ntok, total_blocks, max_seqlen, device=q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    dw = torch.empty(w.shape, dtype=torch.float32, device=q.device) if dw is None else dw
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = library().hca_attend_prefill_backward(
+        ctypes.byref(params), batch, int(max_seqlen), int(ntok), int(total_blocks), _ptr(cu_seqlens),
+        _ptr(cu_blocks), _ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(kc), _ptr(vc), _ptr(o), _ptr(lse), _ptr(dout),
+        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dw), _ptr(workspace), ws_bytes, _stream(stream))
+    _check("hca_attend_prefill_backward", st)
+    return dq, dk, dv, dw
 
 
 def hca_decode_workspace_bytes(params: HcaParams, batch: int, max_blocks: int) -> int:

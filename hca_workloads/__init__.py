@@ -14,6 +14,7 @@ from .gen import (  # noqa: F401
     cu_from_lengths,
     decode_inputs,
     draw_lengths,
+    backward_inputs,
     prefill_inputs,
     ring_from_raw,
 )

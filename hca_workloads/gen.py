@@ -81,6 +81,17 @@ def prefill_inputs(cfg, device="cpu", lens=None, seed=None, kc_random: bool = Fa
     return d
 
 
+def backward_inputs(cfg, device="cpu", lens=None, seed=None):
+    """prefill_inputs plus the output gradient dout [N_tok, Hq, d], drawn
+    like the queries (a synthetic dL/dO of the layer's output)."""
+    seed = cfg.seed if seed is None else seed
+    d = prefill_inputs(cfg, device, lens=lens, seed=seed)
+    g = _gen(seed + 7919, device)
+    ntok = d["q"].shape[0]
+    d["dout"] = _normal((ntok, cfg.hq, cfg.d), g, device, cfg.rms, _DT[cfg.dtype])
+    return d
+
+
 def decode_inputs(cfg, device="cpu", lens=None, seed=None, ring=None):
     """Decode batch: one query per sequence plus a filled cache.
 

@@ -292,6 +292,79 @@ HCA_API hca_status hca_attend_prefill_chunk_gated_vha(
     int32_t ring_cap, const float* gate, const float* vha_u, const float* vha_v, int32_t vha_rank,
     void* o, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Training: the gradient of hca_attend_prefill.  The pages train the model at
+ * long context (release blog "ERNIE 5.5 Flash Base", section 2.1; the model
+ * card gives the 128K training context) and print no backward: these calls
+ * compute the exact derivative of the forward above, HCA_BF16 with 512-dim
+ * heads and 64 query heads per KV head only (HCA_ERR_UNSUPPORTED otherwise).
+ *
+ * hca_attend_prefill_lse - hca_attend_prefill that also writes, per query row,
+ * the log-sum-exp of its scaled scores over its visible keys:
+ *
+ *   lse             device fp32 [N_tok, Hq], natural log,
+ *                   lse[t, h] = log sum_j exp(scale q[t,h] . key_j)
+ *
+ * Same other arguments, errors and ownership as hca_attend_prefill.
+ */
+HCA_API hca_status hca_attend_prefill_lse(const hca_params* params, int32_t batch, int32_t max_seqlen,
+                                          const int32_t* cu_seqlens, const int32_t* cu_blocks,
+                                          const void* q, const void* k, const void* v,
+                                          const void* kc, const void* vc, void* o, float* lse,
+                                          void* stream);
+
+/*
+ * hca_attend_prefill_backward_workspace_bytes - scratch bytes that
+ * hca_attend_prefill_backward needs (0 for invalid or unsupported params):
+ * 4 N_tok Hq (dO . O per row) + 8 N_tok Hkv d (fp32 raw-row gradients)
+ * + 8 B Hkv ceil(max_blocks / 32) S 32 d (fp32 partials of the compressed
+ * entries, S <= 256 runs of max(64, ceil(max_seqlen / 256)) positions,
+ * max_blocks = floor(max_seqlen / 128)) + 512 total_blocks Hkv, each part
+ * rounded up to 256 bytes.
+ */
+HCA_API size_t hca_attend_prefill_backward_workspace_bytes(const hca_params* params, int32_t batch,
+                                                           int32_t total_tokens, int32_t total_blocks,
+                                                           int32_t max_seqlen);
+
+/*
+ * hca_attend_prefill_backward - gradients of a loss L through
+ * hca_compress (K and V pooled with softmax(w)) followed by
+ * hca_attend_prefill, given dL/dO:
+ *
+ *   batch, max_seqlen, cu_seqlens, cu_blocks   as for hca_attend_prefill
+ *   total_tokens    host: N_tok = cu_seqlens[B]
+ *   total_blocks    host: cu_blocks[B]
+ *   q, k, v         device bf16 inputs of the forward
+ *   w               device fp32 [Hkv, 128] pooling logits
+ *   kc, vc          device bf16 [total_blocks, Hkv, d] the forward's entries
+ *   o, lse          device: the forward's output and hca_attend_prefill_lse's
+ *                   lse
+ *   dout            device bf16 [N_tok, Hq, d] dL/dO
+ *   dq              device bf16 [N_tok, Hq, d] dL/dq (written)
+ *   dk, dv          device bf16 [N_tok, Hkv, d] dL/dk, dL/dv through both the
+ *                   raw window and the pooled entries (written)
+ *   dw              device fp32 [Hkv, 128] dL/dw (written; zero without a
+ *                   complete block)
+ *   workspace       device scratch of at least
+ *                   hca_attend_prefill_backward_workspace_bytes bytes
+ *                   (HCA_ERR_WORKSPACE when NULL or smaller)
+ *
+ * Per query row and visible key j: P_j = exp(scale q.k_j - lse),
+ * dS_j = P_j (dO.v_j - dO.O); dq = scale sum dS_j k_j, a key gets
+ * scale dS_j q and its value P_j dO; an entry's gradients reach its block's
+ * rows weighted by softmax(w), and dw = p (g - sum p g) with
+ * g_i = sum over entries of (dKc . K_i + dVc . V_i).  Deterministic (no
+ * atomics).  Outputs must not alias inputs or the workspace.
+ */
+HCA_API hca_status hca_attend_prefill_backward(const hca_params* params, int32_t batch, int32_t max_seqlen,
+                                               int32_t total_tokens, int32_t total_blocks,
+                                               const int32_t* cu_seqlens, const int32_t* cu_blocks,
+                                               const void* q, const void* k, const void* v, const float* w,
+                                               const void* kc, const void* vc, const void* o,
+                                               const float* lse, const void* dout, void* dq, void* dk,
+                                               void* dv, float* dw, void* workspace, size_t workspace_bytes,
+                                               void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 HCA_API const char* hca_status_string(hca_status status);
 

@@ -47,6 +47,7 @@ KERNEL_SOURCES = {
     "compress_chunk": (_CS + "compress.hip",),
     "ring_append": (_CS + "chunk.hip",),
     "decode_maintenance": (_CS + "compress.hip", _CS + "chunk.hip"),
+    "backward": (_CS + "backward_bf16.hip", _CS + "bf16_tiles.h"),
 }
 
 
@@ -77,6 +78,18 @@ def prefill_work(c, lens, e):
         raw = (min(W, L) * (min(W, L) + 1)) // 2 + max(0, L - W) * W
         pairs += comp + raw
     return byt, 4 * c.d * c.hq * pairs
+
+
+def backward_work(c, lens, e):
+    """(bytes, flops) of one hca_attend_prefill_backward call: q, o, dout
+    read and dq written; raw K, V read and dK, dV written; the entries read;
+    10*d*Hq flops per visible (query, key) pair (the scores S and dP, and
+    the products for dQ, dK and dV, each 2*d per pair and head)."""
+    pb, pf = prefill_work(c, lens, e)
+    ntok = sum(lens)
+    nblk = sum(l // c.block for l in lens)
+    byt = ntok * (4 * c.hq * c.d * e + 4 * c.hkv * c.d * e + 4 * c.hq) + nblk * 2 * c.hkv * c.d * e
+    return byt, pf // 4 * 10
 
 
 def compress_work(c, lens, e):
@@ -304,6 +317,29 @@ def run_prefill(torch, hca, c, steps, warmup, clock, min_warm_s, lens=None):
                 p, inp["cu_seqlens"], inp["cu_blocks"], inp["max_seqlen"], inp["q"], inp["k"], inp["v"], kc, vc,
                 gate=gate, vha_u=u, vha_v=v, o=o))
         torch.cuda.synchronize()
+        # the backward: gradients of the pooling + attention for a synthetic
+        # dL/dO, from the forward's o and lse
+        dout = (torch.randn(inp["q"].shape, generator=g, device="cuda")).to(dt)
+        o2, lse = hca.hca_attend_prefill_lse(p, inp["cu_seqlens"], inp["cu_blocks"], inp["max_seqlen"], inp["q"],
+                                             inp["k"], inp["v"], kc, vc)
+        ntok = inp["q"].shape[0]
+        ws = hca.new_backward_workspace(p, len(inp["lens"]), ntok, inp["total_blocks"], inp["max_seqlen"])
+        dq, dk, dv = torch.empty_like(inp["q"]), torch.empty_like(inp["k"]), torch.empty_like(inp["v"])
+        dw = torch.empty((c.hkv, c.block), dtype=torch.float32, device="cuda")
+
+        def bwd():
+            return hca.hca_attend_prefill_backward(p, inp["cu_seqlens"], inp["cu_blocks"], inp["max_seqlen"],
+                                                   inp["total_blocks"], inp["q"], inp["k"], inp["v"], inp["w"], kc,
+                                                   vc, o2, lse, dout, workspace=ws, dq=dq, dk=dk, dv=dv, dw=dw)
+        for _ in range(2):
+            bwd()
+        for _ in range(steps):
+            clock.run("prefill_lse", lambda: hca.hca_attend_prefill_lse(
+                p, inp["cu_seqlens"], inp["cu_blocks"], inp["max_seqlen"], inp["q"], inp["k"], inp["v"], kc, vc,
+                o=o2, lse=lse))
+            clock.run("backward", bwd)
+        torch.cuda.synchronize()
+        del dout, o2, lse, ws, dq, dk, dv, dw
     return inp, wall, nwarm
 
 
@@ -555,6 +591,16 @@ def main():
             ef = pf + ntok_of(lens) * c.d * 4 * c.hq * EPILOGUE_RANK
             kernels["prefill_gated_vha"] = roofline("prefill_gated_vha", c.name, eb, ef, t_epi, bound)
             kernels["prefill_gated_vha"]["overhead_vs_prefill"] = round(t_epi / t_pre - 1.0, 4)
+        if clock.pairs.get("backward"):
+            bb, bf = backward_work(c, lens, e)
+            t_bwd, t_lse = clock.mean_ms("backward"), clock.mean_ms("prefill_lse")
+            bbound = "hbm" if bf / bb < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "mfma"
+            kernels["backward"] = roofline("backward", c.name, bb, bf, t_bwd, bbound)
+            kernels["backward"]["mfma_frac"] = round(bf / (t_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+            kernels["backward"]["hbm_frac"] = round(bb / (t_bwd * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+            kernels["backward"]["ratio_to_forward"] = round(t_bwd / t_pre, 3)
+            kernels["prefill_lse"] = roofline("prefill_lse", c.name, pb + ntok_of(lens) * c.hq * 4, pf, t_lse, bound)
+            kernels["prefill_lse"]["overhead_vs_prefill"] = round(t_lse / t_pre - 1.0, 4)
         result.update({"value": round(ntok / (ms_step * 1e-3), 1), "unit": "tokens/s",
                        "ms_per_step": round(ms_step, 4)})
         result["config"] = {"workload": c.name, "batch": len(lens), "seq_len": max(lens),

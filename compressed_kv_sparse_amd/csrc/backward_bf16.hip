@@ -44,6 +44,7 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+
 // Transposed A (or B) fragment of a 16x16x32 product from row-major bf16
 // rows in LDS (row stride `stride` bytes): lane l gets column l%16 of rows
 // 4g + j (j < 4) and 16 + 4g + j, g = l/16; `base` already holds the lane
@@ -90,14 +91,26 @@ __device__ __forceinline__ void dq_tile(const char HCA_LDS* kbuf, const char HCA
   f32x4 s0 = {}, s1 = {}, p0 = {}, p1 = {};
   const char HCA_LDS* ka = kbuf + r * KSTR + g * 16;
   const char HCA_LDS* va = vbuf + r * VSTR + g * 16;
+  // K and V row fragments one k-step ahead (a deeper prefetch spills)
+  bf16x8 f[2][4];
+  f[0][0] = lds_k_frag(ka);
+  f[0][1] = lds_k_frag(ka + 16 * KSTR);
+  f[0][2] = lds_k_frag(va);
+  f[0][3] = lds_k_frag(va + 16 * VSTR);
 #pragma unroll
   for (int k = 0; k < KSTEPS; ++k) {
-    const bf16x8 k0 = lds_k_frag(ka + k * 64), k1 = lds_k_frag(ka + 16 * KSTR + k * 64);
-    const bf16x8 v0 = lds_k_frag(va + k * 64), v1 = lds_k_frag(va + 16 * VSTR + k * 64);
-    s0 = mfma16(k0, qf[k], s0);
-    s1 = mfma16(k1, qf[k], s1);
-    p0 = mfma16(v0, df[k], p0);
-    p1 = mfma16(v1, df[k], p1);
+    const int c = k & 1, n = c ^ 1;
+    if (k + 1 < KSTEPS) {
+      f[n][0] = lds_k_frag(ka + (k + 1) * 64);
+      f[n][1] = lds_k_frag(ka + 16 * KSTR + (k + 1) * 64);
+      f[n][2] = lds_k_frag(va + (k + 1) * 64);
+      f[n][3] = lds_k_frag(va + 16 * VSTR + (k + 1) * 64);
+    }
+    s0 = mfma16(f[c][0], qf[k], s0);
+    s1 = mfma16(f[c][1], qf[k], s1);
+    p0 = mfma16(f[c][2], df[k], p0);
+    p1 = mfma16(f[c][3], df[k], p1);
+    __builtin_amdgcn_sched_barrier(0);
   }
   bf16x8 bds;
   const int kk0 = tile * NT + 4 * g;
@@ -109,8 +122,14 @@ __device__ __forceinline__ void dq_tile(const char HCA_LDS* kbuf, const char HCA
     bds[4 + i] = (bf16)(pb * (p1[i] - dd));
   }
   const char HCA_LDS* kt = kbuf + (4 * g + (r >> 2)) * KSTR + 8 * (lane & 3);
+  bf16x8 a[2];
+  a[0] = lds_tr_frag(kt, KSTR);
 #pragma unroll
-  for (int ct = 0; ct < DQ_TILES; ++ct) st.acc[ct] = mfma16(lds_tr_frag(kt + 32 * ct, KSTR), bds, st.acc[ct]);
+  for (int ct = 0; ct < DQ_TILES; ++ct) {
+    if (ct + 1 < DQ_TILES) a[(ct + 1) & 1] = lds_tr_frag(kt + 32 * (ct + 1), KSTR);
+    st.acc[ct] = mfma16(a[ct & 1], bds, st.acc[ct]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BackwardArgs a) {
@@ -187,222 +206,180 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BackwardArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: grid (raw_tiles + comp_tiles * nsplit, batch, Hkv), 256 threads.
-// Workgroup x < raw_tiles owns raw rows 32x .. 32x+31 of the sequence and
-// the positions that see them (x*32 .. x*32+31+W-1); the others own
-// compressed entries 32c .. 32c+31 (c = (x - raw_tiles) / nsplit) and split
-// s of the positions that see entry 32c (those from 128 (32c+1) - 1 on, in
-// runs of `pch`).  Per position and half of the 64 heads (a "step"):
-//   stage the 32 Q rows and 32 dO rows in LDS;
-//   waves 0, 1: S^T [32 keys x 16 rows] = K Q^T; waves 2, 3: dP^T = V dO^T
-//     (rows 16 (w&1) ..); both to LDS as fp32;
-//   all threads: P = exp2(S sc2 - lse2) on visible (key, position) pairs,
-//     dS = P (dP - D), both as bf16 A operands [key][rows in k-slot order];
-//   wave w, columns 128w .. 128w+127: dV += P^T dO, dK += dS^T Q
-//     (B = the staged rows read transposed).
+// dK, dV: grid (items, batch, Hkv), 256 threads.  An item is a tile of 64
+// keys and a run of the positions that see them: raw tiles (rows 64x ..
+// 64x+63 of the sequence; positions 64x .. 64x+63+W-1, in nsr runs of prr)
+// first, then compressed tiles (entries 64c .. 64c+63; positions from
+// 128 (64c+1) - 1 on, in nsc runs of pch).  Every item writes its own fp32
+// partial [64 keys][d] for K and V; bwd_pool_kernel sums them in run order
+// (deterministic).
+//
+// Wave w owns keys 16w .. 16w+15 of the tile and keeps K^T and V^T of them
+// in registers (the B operands: lane l = key l%16, d = 32k + 8g .. +7).  A
+// "step" is one position and 32 of its heads (rows), staged in LDS (Q and
+// dO rows, lse and D; double buffered, filled by direct buffer->LDS loads
+// during the previous step):
+//   S = Q K^T, dP = dO V^T   [32 rows x 16 keys]: A = staged rows
+//   P = exp2(S sc2 - lse2) on visible (row, key) pairs, dS = P (dP - D):
+//     in the accumulator layout lane l holds key l%16 and rows 4g + i,
+//     16 + 4g + i, which is the A layout of P^T / dS^T with the rows in the
+//     k-slot order of the transposed reads below - no exchange needed;
+//   dV += P^T dO, dK += dS^T Q   [16 keys x 512]: B = staged rows read
+//     transposed; the accumulators (2 x 128 registers) are pinned to AGPRs.
 // ---------------------------------------------------------------------------
-struct DkvLds {
-  char HCA_LDS* kt;   // 32 K rows (KSTR)
-  char HCA_LDS* vt;   // 32 V rows (VSTR)
-  char HCA_LDS* qs;   // 32 staged Q rows (BSTR)
-  char HCA_LDS* ds;   // 32 staged dO rows (BSTR)
-  float HCA_LDS* sx;  // S  [32 keys][SSTR]
-  float HCA_LDS* px;  // dP [32 keys][SSTR]
-  char HCA_LDS* pa;   // P^T  bf16 [32 keys][32 rows, k-slot order]
-  char HCA_LDS* sa;   // dS^T bf16 [32 keys][32 rows, k-slot order]
-  float HCA_LDS* rs;  // lse2 [32], D [32] of the staged rows
-};
+constexpr int KT = 64;              // keys per item
+constexpr int QSTAGE = 32 * BSTR;   // one staged half position of Q (or dO)
 
-// Byte offset of (key, row) in the P^T / dS^T operand buffers: lane l of an
-// A fragment reads key 16m + l%16, rows 4g + j and 16 + 4g + j (g = l/16),
-// the k-slot order of the transposed reads of the staged rows.
-__device__ __forceinline__ int kslot_off(int key, int row) {
-  return key * 64 + ((row & 15) >> 2) * 16 + ((row >> 4) * 4 + (row & 3)) * 2;
+__device__ __forceinline__ void stage_rows(const BackwardArgs& a, size_t tok, int kvh, int hh,
+                                           char HCA_LDS* buf, float HCA_LDS* rs, int wave, int lane) {
+  const size_t row0 = tok * a.hq + kvh * G + 32 * hh;  // first of the 32 rows
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const bf16*)a.q + row0 * D, 32 * D * sizeof(bf16));
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc((const bf16*)a.dout + row0 * D, 32 * D * sizeof(bf16));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = wave * 8 + i;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (void HCA_LDS*)(buf + row * BSTR), 16,
+                                             row * D * (int)sizeof(bf16) + lane * 16, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (void HCA_LDS*)(buf + QSTAGE + row * BSTR), 16,
+                                             row * D * (int)sizeof(bf16) + lane * 16, 0, 0, 0);
+  }
+  if (wave == 0) {  // lse and D of the 32 rows: lanes 32.. read past the range (zeros)
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.lse + row0, 32 * sizeof(float));
+    const __amdgpu_buffer_rsrc_t rdl = make_rsrc(a.delta + row0, 32 * sizeof(float));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (void HCA_LDS*)rs, 4, lane * 4, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rdl, (void HCA_LDS*)(rs + 64), 4, lane * 4, 0, 0, 0);
+  }
 }
 
-__global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BackwardArgs a, int raw_tiles, int nsplit, int pch) {
-  __shared__ __attribute__((aligned(16))) char kt_s[NT * KSTR];
-  __shared__ __attribute__((aligned(16))) char vt_s[NT * VSTR];
-  __shared__ __attribute__((aligned(16))) char qs_s[32 * BSTR];
-  __shared__ __attribute__((aligned(16))) char ds_s[32 * BSTR];
-  __shared__ __attribute__((aligned(16))) float sx_s[NT * SSTR];
-  __shared__ __attribute__((aligned(16))) float px_s[NT * SSTR];
-  __shared__ __attribute__((aligned(16))) char pa_s[NT * 64];
-  __shared__ __attribute__((aligned(16))) char sa_s[NT * 64];
-  __shared__ __attribute__((aligned(16))) float rs_s[64];
+__global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BackwardArgs a, BackwardPlan pl) {
+  __shared__ __attribute__((aligned(16))) char st_s[2][2 * QSTAGE];
+  __shared__ __attribute__((aligned(16))) float rs_s[2][128];
 
   const int b = blockIdx.y, kvh = blockIdx.z;
   const int start = a.cu_seqlens[b];
   const int len = a.cu_seqlens[b + 1] - start;
   const int nb = a.cu_blocks[b + 1] - a.cu_blocks[b];
-  const int x = blockIdx.x;
-  const bool comp = x >= raw_tiles;
-  int key0, t_begin, t_end, ctile = 0, split = 0;
+  const int x = blockIdx.x;  // the item
+  const int raw_items = pl.raw_tiles * pl.nsr;
+  const bool comp = x >= raw_items;
+  int key0, t_begin, t_end;
   if (!comp) {
-    key0 = x * NT;
+    key0 = (x / pl.nsr) * KT;
     if (key0 >= len) return;
-    t_begin = key0;
-    t_end = min(len, key0 + NT - 1 + a.window);
+    const int t_last = min(len, key0 + KT - 1 + a.window);  // end of the positions that see the tile
+    t_begin = key0 + (x % pl.nsr) * pl.prr;
+    if (t_begin >= t_last) return;
+    t_end = min(t_last, t_begin + pl.prr);
   } else {
-    ctile = (x - raw_tiles) / nsplit;
-    split = (x - raw_tiles) % nsplit;
-    key0 = ctile * NT;
+    const int y = x - raw_items;
+    key0 = (y / pl.nsc) * KT;
     if (key0 >= nb) return;
-    const int first = kBlock * (key0 + 1) - 1;  // first position that sees entry key0
-    t_begin = first + split * pch;
+    t_begin = kBlock * (key0 + 1) - 1 + (y % pl.nsc) * pl.pch;
     if (t_begin >= len) return;
-    t_end = min(len, t_begin + pch);
+    t_end = min(len, t_begin + pl.pch);
   }
-  const int nkey = min(NT, (comp ? nb : len) - key0);  // keys of the tile that exist
+  const int nkey = min(KT, (comp ? nb : len) - key0);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, r = lane & 15;
-  DkvLds L;
-  L.kt = (char HCA_LDS*)kt_s;
-  L.vt = (char HCA_LDS*)vt_s;
-  L.qs = (char HCA_LDS*)qs_s;
-  L.ds = (char HCA_LDS*)ds_s;
-  L.sx = (float HCA_LDS*)sx_s;
-  L.px = (float HCA_LDS*)px_s;
-  L.pa = (char HCA_LDS*)pa_s;
-  L.sa = (char HCA_LDS*)sa_s;
-  L.rs = (float HCA_LDS*)rs_s;
+  const int kl = 16 * wave + r;      // the lane's key within the tile
+  const int kk = key0 + kl;           // ... within the sequence (entry or raw position)
 
-  // the 32 keys: slots of a key list that is all compressed or all raw
-  KeySource ks;
-  seq_sources(a, b, kvh, start, len, ks);
-  ks.nc = comp ? nb : 0;
-  ks.nkeys = comp ? nb : len;
-  ks.raw0 = 0;
-  issue_tile<4>(ks, key0 / NT, L.kt, L.vt, wave, lane);
-
-  const float sc2 = a.scale * kLog2e;
-  f32x4 acc_v[2][8], acc_k[2][8];  // [key half m][16-column tile u]: keys 16m + 4g + i, d = 128w + 16u + l%16
+  // K^T and V^T fragments of the lane's key (past the end: the last key,
+  // masked below)
+  bf16x8 kf[KSTEPS], vf[KSTEPS];
+  {
+    const size_t row = comp ? (size_t)(a.cu_blocks[b] + min(kk, nb - 1)) : (size_t)start + min(kk, len - 1);
+    const bf16* kr = (const bf16*)(comp ? a.kc : a.k) + (row * a.hkv + kvh) * D + 8 * g;
+    const bf16* vr = (const bf16*)(comp ? a.vc : a.v) + (row * a.hkv + kvh) * D + 8 * g;
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int u = 0; u < 8; ++u) acc_v[m][u] = acc_k[m][u] = f32x4{};
-
-  const size_t rstride = (size_t)a.hq * D * sizeof(bf16);
-  for (int t = t_begin; t < t_end; ++t) {
-    const size_t tok = (size_t)start + t;
-    for (int hh = 0; hh < 2; ++hh) {
-      // stage the 32 Q and dO rows (heads 32hh .. of the group) of position t
-      {
-        const size_t off = tok * rstride + (size_t)(kvh * G + 32 * hh) * D * sizeof(bf16);
-        const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char*)a.q + off, 32 * D * sizeof(bf16));
-        const __amdgpu_buffer_rsrc_t rd = make_rsrc((const char*)a.dout + off, 32 * D * sizeof(bf16));
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int row = wave * 8 + i;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (void HCA_LDS*)(L.qs + row * BSTR), 16,
-                                                   row * D * (int)sizeof(bf16) + lane * 16, 0, 0, 0);
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (void HCA_LDS*)(L.ds + row * BSTR), 16,
-                                                   row * D * (int)sizeof(bf16) + lane * 16, 0, 0, 0);
-        }
-        if (threadIdx.x < 32) {
-          const size_t ri = tok * a.hq + kvh * G + 32 * hh + threadIdx.x;
-          L.rs[threadIdx.x] = a.lse[ri] * kLog2e;
-          L.rs[32 + threadIdx.x] = a.delta[ri];
-        }
-      }
-      wait_vm_all();
-      __syncthreads();
-      // S^T (waves 0, 1) or dP^T (waves 2, 3) of rows 16 (w & 1) .. +15
-      {
-        const bool is_dp = wave >= 2;
-        const int rh = wave & 1;
-        const char HCA_LDS* A = (is_dp ? L.vt : L.kt) + r * (is_dp ? VSTR : KSTR) + g * 16;
-        const int astr16 = 16 * (is_dp ? VSTR : KSTR);
-        const char HCA_LDS* B = (is_dp ? L.ds : L.qs) + (16 * rh + r) * BSTR + g * 16;
-        f32x4 c0 = {}, c1 = {};
-#pragma unroll
-        for (int k = 0; k < KSTEPS; ++k) {
-          const bf16x8 bq = lds_k_frag(B + k * 64);
-          c0 = mfma16(lds_k_frag(A + k * 64), bq, c0);
-          c1 = mfma16(lds_k_frag(A + astr16 + k * 64), bq, c1);
-        }
-        float HCA_LDS* dst = is_dp ? L.px : L.sx;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          dst[(4 * g + i) * SSTR + 16 * rh + r] = c0[i];
-          dst[(16 + 4 * g + i) * SSTR + 16 * rh + r] = c1[i];
-        }
-      }
-      __syncthreads();
-      // P and dS of the 32 x 32 (key, row) pairs, 4 per thread
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = threadIdx.x * 4 + u;
-        const int key = e >> 5, row = e & 31;
-        const int kk = key0 + key;
-        const bool vis = key < nkey && (comp ? kBlock * (kk + 1) <= t + 1 : (kk <= t && t - kk < a.window));
-        const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(L.sx[key * SSTR + row], sc2, -L.rs[row])) : 0.f;
-        const float dsv = p * (L.px[key * SSTR + row] - L.rs[32 + row]);
-        const int o = kslot_off(key, row);
-        *(bf16 HCA_LDS*)(L.pa + o) = (bf16)p;
-        *(bf16 HCA_LDS*)(L.sa + o) = (bf16)dsv;
-      }
-      __syncthreads();
-      // dV += P^T dO, dK += dS^T Q over the wave's 128 columns
-      {
-        const int tro = (4 * g + (r >> 2)) * BSTR + 8 * (lane & 3) + wave * 256;
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const bf16x8 ap = *(const bf16x8 HCA_LDS*)(L.pa + (16 * m + r) * 64 + g * 16);
-          const bf16x8 as = *(const bf16x8 HCA_LDS*)(L.sa + (16 * m + r) * 64 + g * 16);
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            acc_v[m][u] = mfma16(ap, lds_tr_frag(L.ds + tro + 32 * u, BSTR), acc_v[m][u]);
-            acc_k[m][u] = mfma16(as, lds_tr_frag(L.qs + tro + 32 * u, BSTR), acc_k[m][u]);
-          }
-        }
-      }
-      __syncthreads();
+    for (int k = 0; k < KSTEPS; ++k) {
+      kf[k] = *(const bf16x8*)(kr + 32 * k);
+      vf[k] = *(const bf16x8*)(vr + 32 * k);
     }
   }
+  f32x4 accv[D / 16], acck[D / 16];  // lane l: keys 16w + 4g + i, d = 16u + l%16
+#pragma unroll
+  for (int u = 0; u < D / 16; ++u) accv[u] = acck[u] = f32x4{};
 
-  // results: raw rows to the fp32 row gradients, compressed entries to this
-  // split's partial
-  float* dst_k;
-  float* dst_v;
-  size_t rstr;  // floats between consecutive keys
-  if (!comp) {
-    const size_t base = ((size_t)start + key0) * a.hkv + kvh;
-    dst_k = a.dk_rows + base * D;
-    dst_v = a.dv_rows + base * D;
-    rstr = (size_t)a.hkv * D;
-  } else {
-    const size_t slot = ((((size_t)b * a.hkv + kvh) * a.comp_tiles + ctile) * nsplit + split) * NT;
-    dst_k = a.part_k + slot * D;
-    dst_v = a.part_v + slot * D;
-    rstr = D;
-  }
+  const float sc2 = a.scale * kLog2e;
+  const int nsteps = 2 * (t_end - t_begin);
+  char HCA_LDS* const buf0 = (char HCA_LDS*)&st_s[0][0];
+  float HCA_LDS* const rs0 = (float HCA_LDS*)&rs_s[0][0];
+  stage_rows(a, (size_t)start + t_begin, kvh, 0, buf0, rs0, wave, lane);
+  wait_vm_all();
+  __syncthreads();
+  const int tro = (4 * g + (r >> 2)) * BSTR + 8 * (lane & 3);
+  for (int i = 0; i < nsteps; ++i) {
+    const int t = t_begin + (i >> 1), hh = i & 1;
+    if (i + 1 < nsteps)
+      stage_rows(a, (size_t)start + t_begin + ((i + 1) >> 1), kvh, (i + 1) & 1, buf0 + ((i + 1) & 1) * 2 * QSTAGE,
+                 rs0 + ((i + 1) & 1) * 128, wave, lane);
+    const char HCA_LDS* qs = buf0 + (i & 1) * 2 * QSTAGE;
+    const char HCA_LDS* ds = qs + QSTAGE;
+    const float HCA_LDS* rs = rs0 + (i & 1) * 128;
+    // S, dP of the 32 rows and the wave's 16 keys
+    f32x4 sx[2] = {}, px[2] = {};
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
+    for (int k = 0; k < KSTEPS; ++k) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = 16 * m + 4 * g + i;
-      if (key >= nkey) continue;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int col = wave * 128 + 16 * u + r;
-        dst_k[key * rstr + col] = acc_k[m][u][i] * a.scale;
-        dst_v[key * rstr + col] = acc_v[m][u][i];
+      for (int m = 0; m < 2; ++m) {
+        const int o = (16 * m + r) * BSTR + 64 * k + 16 * g;
+        sx[m] = mfma16(lds_k_frag(qs + o), kf[k], sx[m]);
+        px[m] = mfma16(lds_k_frag(ds + o), vf[k], px[m]);
       }
+    }
+    const bool vis = kl < nkey && (comp ? kBlock * (kk + 1) <= t + 1 : (kk <= t && t - kk < a.window));
+    bf16x8 ap, as;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = 16 * m + 4 * g + j;
+        const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sx[m][j], sc2, -rs[row] * kLog2e)) : 0.f;
+        ap[4 * m + j] = (bf16)p;
+        as[4 * m + j] = (bf16)(p * (px[m][j] - rs[64 + row]));
+      }
+    bf16x8 bo[2], bq[2];
+    bo[0] = lds_tr_frag(ds + tro, BSTR);
+    bq[0] = lds_tr_frag(qs + tro, BSTR);
+#pragma unroll
+    for (int u = 0; u < D / 16; ++u) {
+      if (u + 1 < D / 16) {
+        bo[(u + 1) & 1] = lds_tr_frag(ds + tro + 32 * (u + 1), BSTR);
+        bq[(u + 1) & 1] = lds_tr_frag(qs + tro + 32 * (u + 1), BSTR);
+      }
+      accv[u] = mfma16(ap, bo[u & 1], accv[u]);
+      acck[u] = mfma16(as, bq[u & 1], acck[u]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_vm_all();
+    __syncthreads();
+  }
+
+  // this item's partial: keys 16w + 4g + i, columns 16u + l%16
+  const size_t slot = (((size_t)b * a.hkv + kvh) * pl.items + x) * KT;
+  float* pk = a.part_k + slot * D;
+  float* pv = a.part_v + slot * D;
+#pragma unroll
+  for (int u = 0; u < D / 16; ++u)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const size_t o = (size_t)(16 * wave + 4 * g + j) * D + 16 * u + r;
+      pk[o] = acck[u][j] * a.scale;
+      pv[o] = accv[u][j];
     }
 }
 
 // ---------------------------------------------------------------------------
 // Pooling backward: grid (ceil(max_seqlen / 128), batch, Hkv), 256 threads.
-// Block j of a sequence: when complete, dKc / dVc of entry j = the sum of
-// its tile's partials over the splits that exist for this sequence; every
-// row i of the block gets dK = dK_rows + p_i dKc (rounded to bf16), dV
-// likewise, and g_i = dKc . K_i + dVc . V_i is stored for the dw kernel.
-// A trailing partial block only rounds its rows.
+// Row r of block j gets dK = sum of its raw tile's partials over the runs
+// that exist, plus p_i dKc of entry j when the block is complete (dKc = the
+// sum of the entry's partials), rounded to bf16; dV likewise; and the
+// block's terms g_i = dKc . K_i + dVc . V_i for the dw kernel.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void bwd_pool_kernel(BackwardArgs a, int nsplit, int pch) {
+__global__ __launch_bounds__(256) void bwd_pool_kernel(BackwardArgs a, BackwardPlan pl) {
   __shared__ float dkc_s[D];
   __shared__ float dvc_s[D];
   __shared__ float p_s[kBlock];
@@ -413,6 +390,7 @@ __global__ __launch_bounds__(256) void bwd_pool_kernel(BackwardArgs a, int nspli
   const int nb = a.cu_blocks[b + 1] - a.cu_blocks[b];
   const bool full = j < nb;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const size_t unit = ((size_t)b * a.hkv + kvh) * pl.items;
   if (full) {
     // p = softmax(w_kvh), one wave
     if (wave == 0) {
@@ -420,19 +398,19 @@ __global__ __launch_bounds__(256) void bwd_pool_kernel(BackwardArgs a, int nspli
       float mx = fmaxf(w0, w1);
       for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
       const float e0 = __expf(w0 - mx), e1 = __expf(w1 - mx);
-      float s = e0 + e1;
-      for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
-      p_s[lane] = e0 / s;
-      p_s[64 + lane] = e1 / s;
+      float sm = e0 + e1;
+      for (int o = 32; o > 0; o >>= 1) sm += __shfl_xor(sm, o);
+      p_s[lane] = e0 / sm;
+      p_s[64 + lane] = e1 / sm;
     }
-    const int ctile = j / NT, kk = j % NT;
-    const int first = kBlock * (ctile * NT + 1) - 1;
-    const int ns = (len - first + pch - 1) / pch;
-    const size_t slot0 = (((size_t)b * a.hkv + kvh) * a.comp_tiles + ctile) * nsplit;
+    const int ctile = j / KT, key = j % KT;
+    const int first = kBlock * (ctile * KT + 1) - 1;
+    const int ns = (len - first + pl.pch - 1) / pl.pch;
+    const size_t item0 = unit + (size_t)pl.raw_tiles * pl.nsr + (size_t)ctile * pl.nsc;
     for (int c = threadIdx.x; c < D; c += 256) {
       float sk = 0.f, sv = 0.f;
-      for (int s = 0; s < ns; ++s) {
-        const size_t o = ((slot0 + s) * NT + kk) * D + c;
+      for (int sp = 0; sp < ns; ++sp) {
+        const size_t o = ((item0 + sp) * KT + key) * D + c;
         sk += a.part_k[o];
         sv += a.part_v[o];
       }
@@ -444,9 +422,24 @@ __global__ __launch_bounds__(256) void bwd_pool_kernel(BackwardArgs a, int nspli
   // rows: wave w takes rows w, w+4, ...; lane l columns 8l .. 8l+7
   const int rows = min(kBlock, len - j * kBlock);
   for (int i = wave; i < rows; i += 4) {
-    const size_t row = ((size_t)start + j * kBlock + i) * a.hkv + kvh;
-    const float* rk = a.dk_rows + row * D + 8 * lane;
-    const float* rv = a.dv_rows + row * D + 8 * lane;
+    const int rpos = j * kBlock + i;  // position in the sequence
+    const int rtile = rpos / KT;
+    const int t_last = min(len, rtile * KT + KT - 1 + a.window);
+    const size_t item0 = unit + (size_t)rtile * pl.nsr;
+    float dk8[8] = {}, dv8[8] = {};
+    for (int sp = 0; sp < pl.nsr && rtile * KT + sp * pl.prr < t_last; ++sp) {
+      const size_t o = ((item0 + sp) * KT + rpos % KT) * D + 8 * lane;
+      const f32x4 k0 = *(const f32x4*)(a.part_k + o), k1 = *(const f32x4*)(a.part_k + o + 4);
+      const f32x4 v0 = *(const f32x4*)(a.part_v + o), v1 = *(const f32x4*)(a.part_v + o + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dk8[e] += k0[e];
+        dk8[4 + e] += k1[e];
+        dv8[e] += v0[e];
+        dv8[4 + e] += v1[e];
+      }
+    }
+    const size_t row = ((size_t)start + rpos) * a.hkv + kvh;
     bf16x8 ok, ov;
     float gi = 0.f;
     const float pi = full ? p_s[i] : 0.f;
@@ -455,8 +448,8 @@ __global__ __launch_bounds__(256) void bwd_pool_kernel(BackwardArgs a, int nspli
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float ck = full ? dkc_s[8 * lane + e] : 0.f, cv = full ? dvc_s[8 * lane + e] : 0.f;
-      ok[e] = (bf16)(rk[e] + pi * ck);
-      ov[e] = (bf16)(rv[e] + pi * cv);
+      ok[e] = (bf16)(dk8[e] + pi * ck);
+      ov[e] = (bf16)(dv8[e] + pi * cv);
       gi = __builtin_fmaf(ck, (float)kx[e], __builtin_fmaf(cv, (float)vx[e], gi));
     }
     *(bf16x8*)((bf16*)a.dk + row * D + 8 * lane) = ok;
@@ -503,13 +496,15 @@ __global__ __launch_bounds__(128) void bwd_dw_kernel(BackwardArgs a) {
 BackwardPlan backward_plan(int batch, int hkv, int max_seqlen, int window) {
   BackwardPlan p;
   const int max_blocks = max_seqlen / kBlock;
-  p.raw_tiles = (max_seqlen + NT - 1) / NT;
-  p.comp_tiles = (max_blocks + NT - 1) / NT;
+  p.raw_tiles = (max_seqlen + KT - 1) / KT;
+  p.nsr = 2;  // runs of the positions that see a raw tile (64 + W - 1 of them)
+  p.prr = (KT - 1 + window + p.nsr - 1) / p.nsr;
+  p.comp_tiles = (max_blocks + KT - 1) / KT;
   p.pch = std::max(64, (max_seqlen + 255) / 256);
-  p.nsplit = std::max(1, (max_seqlen + p.pch - 1) / p.pch);
+  p.nsc = std::max(1, (max_seqlen + p.pch - 1) / p.pch);
+  p.items = p.raw_tiles * p.nsr + p.comp_tiles * p.nsc;
   (void)batch;
   (void)hkv;
-  (void)window;
   return p;
 }
 
@@ -519,24 +514,18 @@ size_t backward_workspace_bytes(int batch, int hq, int hkv, int total_tokens, in
                                 int window) {
   const BackwardPlan p = backward_plan(batch, hkv, max_seqlen, window);
   size_t n = 0;
-  n += align256((size_t)total_tokens * hq * sizeof(float));                          // delta
-  n += 2 * align256((size_t)total_tokens * hkv * D * sizeof(float));                 // dk_rows, dv_rows
-  n += 2 * align256((size_t)batch * hkv * p.comp_tiles * p.nsplit * NT * D * sizeof(float));  // partials
-  n += align256((size_t)std::max(total_blocks, 1) * hkv * kBlock * sizeof(float));  // g
+  n += align256((size_t)total_tokens * hq * sizeof(float));                                    // delta
+  n += 2 * align256((size_t)batch * hkv * p.items * KT * D * sizeof(float));                   // partials
+  n += align256((size_t)std::max(total_blocks, 1) * hkv * kBlock * sizeof(float));            // g
   return n;
 }
 
 hipError_t launch_backward_bf16(BackwardArgs a, hipStream_t s) {
   const BackwardPlan p = backward_plan(a.batch, a.hkv, a.max_seqlen, a.window);
-  a.comp_tiles = p.comp_tiles;
   char* w = (char*)a.ws;
   a.delta = (float*)w;
   w += align256((size_t)a.total_tokens * a.hq * sizeof(float));
-  a.dk_rows = (float*)w;
-  w += align256((size_t)a.total_tokens * a.hkv * D * sizeof(float));
-  a.dv_rows = (float*)w;
-  w += align256((size_t)a.total_tokens * a.hkv * D * sizeof(float));
-  const size_t part = align256((size_t)a.batch * a.hkv * p.comp_tiles * p.nsplit * NT * D * sizeof(float));
+  const size_t part = align256((size_t)a.batch * a.hkv * p.items * KT * D * sizeof(float));
   a.part_k = (float*)w;
   w += part;
   a.part_v = (float*)w;
@@ -545,9 +534,8 @@ hipError_t launch_backward_bf16(BackwardArgs a, hipStream_t s) {
 
   if (a.batch > 0 && a.max_seqlen > 0) {
     bwd_dq_kernel<<<dim3(a.max_seqlen, a.batch, a.hkv), 256, 0, s>>>(a);
-    const int items = p.raw_tiles + p.comp_tiles * p.nsplit;
-    bwd_dkv_kernel<<<dim3(items, a.batch, a.hkv), 256, 0, s>>>(a, p.raw_tiles, p.nsplit, p.pch);
-    bwd_pool_kernel<<<dim3((a.max_seqlen + kBlock - 1) / kBlock, a.batch, a.hkv), 256, 0, s>>>(a, p.nsplit, p.pch);
+    bwd_dkv_kernel<<<dim3(p.items, a.batch, a.hkv), 256, 0, s>>>(a, p);
+    bwd_pool_kernel<<<dim3((a.max_seqlen + kBlock - 1) / kBlock, a.batch, a.hkv), 256, 0, s>>>(a, p);
   }
   bwd_dw_kernel<<<a.hkv, 128, 0, s>>>(a);  // no complete block: g = 0, dw = 0
   return hipGetLastError();

@@ -161,18 +161,16 @@ struct BackwardArgs {
   float* dw;
   void* ws;
   // set by the launcher
-  int comp_tiles;
   float* delta;    // dO . O per row [N, Hq]
-  float* dk_rows;  // raw-row gradients from the window keys [N, Hkv, d]
-  float* dv_rows;
-  float* part_k;   // compressed-entry partials [B, Hkv, comp_tiles, nsplit, 32, d]
+  float* part_k;   // per-item partials of the key gradients [B, Hkv, items, 64, d]
   float* part_v;
   float* gbuf;     // per entry terms of the pooling-logit gradient [total_blocks, Hkv, 128]
 };
-// Work split of the dK/dV kernel: raw tiles of 32 rows; compressed tiles of
-// 32 entries, each over nsplit runs of pch positions.
+// Work split of the dK/dV kernel: raw tiles of 64 rows, each over nsr runs
+// of prr positions; compressed tiles of 64 entries, each over nsc runs of
+// pch positions; items = raw_tiles * nsr + comp_tiles * nsc.
 struct BackwardPlan {
-  int raw_tiles, comp_tiles, nsplit, pch;
+  int raw_tiles, nsr, prr, comp_tiles, nsc, pch, items;
 };
 BackwardPlan backward_plan(int batch, int hkv, int max_seqlen, int window);
 size_t backward_workspace_bytes(int batch, int hq, int hkv, int total_tokens, int total_blocks, int max_seqlen,

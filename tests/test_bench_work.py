@@ -58,3 +58,17 @@ def test_decode_and_compress_work():
     nblk = 64 + 2
     assert cb == nblk * c8.hkv * (2 * 128 * c8.d * 2 + 2 * c8.d * 2)  # K, V rows read; Kc, Vc written
     assert cf == nblk * c8.hkv * 4 * 128 * c8.d
+
+
+@pytest.mark.parametrize("lens,window", [([8192], 128), ([1, 127, 129, 3000], 64)])
+def test_backward_work(lens, window):
+    c = dataclasses.replace(CONFIGS["prefill_8k"], window=window)
+    byt, flops = bench.backward_work(c, lens, 2)
+    # scores S and dP, and the products for dQ, dK and dV: 2*d flops each per
+    # visible (query row, key) pair
+    assert flops == 5 * 2 * c.d * c.hq * _pairs(lens, window)
+    ntok = sum(lens)
+    entries = sum(L // 128 for L in lens)
+    # q, o, dout read and dq written (Hq rows); k, v read and dk, dv written
+    # (Hkv rows); the fp32 lse read; the entries read
+    assert byt == ntok * (4 * c.hq * c.d * 2 + 4 * c.hkv * c.d * 2 + 4 * c.hq) + entries * 2 * c.hkv * c.d * 2

@@ -103,3 +103,16 @@ def test_forward_lse():
     print(f"lse max abs error {err:.3e}", flush=True)
     # the forward's row sum adds the bf16-rounded weights: relative 2^-9 at most
     assert err <= 4e-3
+
+
+def test_backward_prefill_8k_full():
+    """The benchmarked workload at full size (one 8192-token sequence, Hq 64,
+    d 512, W 128), in the launch configuration bench.py times: every row of
+    dq, dk, dv and all of dw against the oracle (about 15 s of CPU)."""
+    c0 = CONFIGS["prefill_8k"]
+    c, inp, kc, vc, o, lse, (dq, dk, dv, dw) = _run(list(c0.prefill_lens), c0.hkv, c0.window, seed=c0.seed)
+    rdq, rdk, rdv, rdw, st = _oracle(c, inp)
+    _check("dq", dq, rdq)
+    _check("dk", dk, rdk)
+    _check("dv", dv, rdv)
+    _check("dw", dw, rdw)

@@ -17,3 +17,4 @@ from .hca_oracle import (  # noqa: F401
     visible_sets,
 )
 from .hca_backward import attend_prefill_backward, loss_for_gradcheck  # noqa: F401,E402
+from .dsa_oracle import attend_selected, dsa_decode, index_scores, select_topk  # noqa: F401,E402

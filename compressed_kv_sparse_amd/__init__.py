@@ -23,6 +23,8 @@ from .hca import (  # noqa: F401
     hca_compress,
     hca_compress_chunk,
     hca_decode_workspace_bytes,
+    hca_dsa_decode,
+    hca_dsa_decode_workspace_bytes,
     hca_prefill_chunk_workspace_bytes,
     hca_ring_append,
     hca_status_string,

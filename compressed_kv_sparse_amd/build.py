@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libhca.so")
 
 SOURCES = ["compress.hip", "attend_f32.hip", "prefill_bf16.hip", "decode_bf16.hip", "chunk.hip", "backward_bf16.hip",
-           "hca_api.hip"]
+           "dsa.hip", "hca_api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -246,6 +246,40 @@ hca_status hca_attend_prefill_backward(const hca_params* params, int32_t batch, 
   return from_hip(hca::launch_backward_bf16(a, (hipStream_t)stream));
 }
 
+size_t hca_dsa_decode_workspace_bytes(int32_t batch, int32_t max_seqlen, int32_t topk) {
+  if (batch < 0 || max_seqlen < 0 || topk < 1) return 0;
+  return hca::dsa_workspace_bytes(batch, max_seqlen, topk);
+}
+
+hca_status hca_dsa_decode(int32_t batch, int32_t max_seqlen, int32_t topk, float softmax_scale,
+                          const int32_t* seqlens, const int32_t* cu_rows, const void* q, const int8_t* qi,
+                          const void* k, const void* v, const int8_t* ki, void* o, int32_t* sel, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (batch < 0 || batch > 65535 || max_seqlen < 0 || topk < 1) return HCA_ERR_SHAPE;
+  if (!(softmax_scale == softmax_scale)) return HCA_ERR_SHAPE;  // NaN
+  if ((long)batch * max_seqlen > 0x7fffffffL) return HCA_ERR_SHAPE;
+  if (batch == 0 || max_seqlen == 0) return HCA_OK;
+  if (!seqlens || !cu_rows || !q || !qi || !k || !v || !ki || !o || !sel) return HCA_ERR_NULL;
+  const size_t need = hca::dsa_workspace_bytes(batch, max_seqlen, topk);
+  if (!workspace || workspace_bytes < need) return HCA_ERR_WORKSPACE;
+  hca::DsaArgs a{};
+  a.batch = batch;
+  a.max_seqlen = max_seqlen;
+  a.topk = topk;
+  a.scale = softmax_scale > 0.f ? softmax_scale : 1.f / 16.f;  // 1/sqrt(256)
+  a.seqlens = seqlens;
+  a.cu_rows = cu_rows;
+  a.q = q;
+  a.qi = (const signed char*)qi;
+  a.k = k;
+  a.v = v;
+  a.ki = (const signed char*)ki;
+  a.o = o;
+  a.sel = sel;
+  a.ws = workspace;
+  return from_hip(hca::launch_dsa_decode(a, (hipStream_t)stream));
+}
+
 size_t hca_decode_workspace_bytes(const hca_params* params, int32_t batch, int32_t max_blocks) {
   if (check_params(params) != HCA_OK || batch < 0 || max_blocks < 0) return 0;
   if (params->dtype == HCA_F32) return 0;

@@ -177,4 +177,32 @@ size_t backward_workspace_bytes(int batch, int hq, int hkv, int total_tokens, in
                                 int window);
 hipError_t launch_backward_bf16(BackwardArgs a, hipStream_t s);
 
+// Sparse-attention decode of the full-context layers (dsa.hip): 64 query
+// heads and one shared key/value head of width 256, an int8 indexer of
+// width 128.  Sequence b has seqlens[b] cached rows starting at row
+// cu_rows[b] of k, v [rows, 256] and ki [rows, 128]; its query sits at the
+// last position.  The workspace pointers below ws are carved by the launcher.
+struct DsaArgs {
+  int batch, max_seqlen, topk;
+  float scale;
+  const int* seqlens;
+  const int* cu_rows;
+  const void* q;           // [B, 64, 256] bf16
+  const signed char* qi;   // [B, 128]
+  const void* k;
+  const void* v;
+  const signed char* ki;
+  void* o;                 // [B, 64, 256] bf16
+  int* sel;                // [B, topk] selected positions, increasing, -1 padded
+  void* ws;
+  // set by the launcher
+  unsigned* keys;          // [B, max_seqlen] score + 2^21
+  unsigned* hist;          // [B, 2049] histogram of key >> 11
+  float* part_m;           // [B, nsplit, 64]
+  float* part_l;
+  bf16* part_o;            // [B, nsplit, 64, 256]
+};
+size_t dsa_workspace_bytes(int batch, int max_seqlen, int topk);
+hipError_t launch_dsa_decode(DsaArgs a, hipStream_t s);
+
 }  // namespace hca

@@ -25,6 +25,7 @@ EXPORTS = ("hca_compress", "hca_attend_prefill", "hca_decode_workspace_bytes",
            "hca_prefill_chunk_workspace_bytes", "hca_attend_prefill_chunk", "hca_attend_prefill_gated_vha",
            "hca_attend_decode_gated_vha", "hca_attend_prefill_chunk_gated_vha",
            "hca_attend_prefill_lse", "hca_attend_prefill_backward_workspace_bytes", "hca_attend_prefill_backward",
+           "hca_dsa_decode_workspace_bytes", "hca_dsa_decode",
            "hca_status_string", "hca_version")
 
 
@@ -105,6 +106,10 @@ def library() -> ctypes.CDLL:
     lib.hca_attend_prefill_backward.argtypes = [P, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                                 vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hca_attend_prefill_backward.restype = ctypes.c_int
+    lib.hca_dsa_decode_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.hca_dsa_decode_workspace_bytes.restype = sz
+    lib.hca_dsa_decode.argtypes = [i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hca_dsa_decode.restype = ctypes.c_int
     lib.hca_status_string.argtypes = [ctypes.c_int]
     lib.hca_status_string.restype = ctypes.c_char_p
     lib.hca_version.argtypes = []
@@ -235,6 +240,29 @@ def hca_attend_prefill_backward(params: HcaParams, cu_seqlens, cu_blocks, max_se
         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dw), _ptr(workspace), ws_bytes, _stream(stream))
     _check("hca_attend_prefill_backward", st)
     return dq, dk, dv, dw
+
+
+def hca_dsa_decode_workspace_bytes(batch: int, max_seqlen: int, topk: int) -> int:
+    return int(library().hca_dsa_decode_workspace_bytes(int(batch), int(max_seqlen), int(topk)))
+
+
+def hca_dsa_decode(seqlens, cu_rows, max_seqlen: int, topk: int, q, qi, k, v, ki, workspace=None, o=None,
+                   sel=None, softmax_scale: float = 0.0, stream=None):
+    """Sparse-attention decode of the full-context layers: indexer scores,
+    top-k selection and attention over the selection.  q bf16 [B, 64, 256],
+    qi int8 [B, 128], k, v bf16 [rows, 256], ki int8 [rows, 128].
+    Returns (o [B, 64, 256], sel int32 [B, topk])."""
+    batch = seqlens.numel()
+    if workspace is None:
+        n = hca_dsa_decode_workspace_bytes(batch, max_seqlen, topk)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q) if o is None else o
+    sel = torch.empty((batch, int(topk)), dtype=torch.int32, device=q.device) if sel is None else sel
+    st = library().hca_dsa_decode(int(batch), int(max_seqlen), int(topk), float(softmax_scale), _ptr(seqlens),
+                                  _ptr(cu_rows), _ptr(q), _ptr(qi), _ptr(k), _ptr(v), _ptr(ki), _ptr(o), _ptr(sel),
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("hca_dsa_decode", st)
+    return o, sel
 
 
 def hca_decode_workspace_bytes(params: HcaParams, batch: int, max_blocks: int) -> int:

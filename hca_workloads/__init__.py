@@ -13,6 +13,7 @@ from .gen import (  # noqa: F401
     chunk_inputs,
     cu_from_lengths,
     decode_inputs,
+    dsa_inputs,
     draw_lengths,
     backward_inputs,
     prefill_inputs,

@@ -92,6 +92,31 @@ def backward_inputs(cfg, device="cpu", lens=None, seed=None):
     return d
 
 
+def dsa_inputs(lens, seed, device="cpu", ties: bool = False, hq: int = 64, d: int = 256, di: int = 128):
+    """Sparse-attention decode batch of the full-context layers: sequence b
+    has lens[b] cached rows (packed, first row cu_rows[b]) and one query at
+    its last position.  q, k, v: RMS-normalised N(0, 1) in bf16; qi, ki:
+    uniform int8 in [-127, 127] (ties: in {-1, 0, 1}, so many scores are
+    equal)."""
+    g = _gen(seed, device)
+    lens = [int(x) for x in lens]
+    rows = int(sum(lens))
+    cu = cu_from_lengths(lens)
+    lo, hi = (-1, 2) if ties else (-127, 128)
+    return {
+        "lens": lens,
+        "cu_rows_host": cu[:-1],
+        "max_seqlen": max(lens),
+        "seqlens": torch.tensor(lens, dtype=torch.int32, device=device),
+        "cu_rows": torch.tensor(cu[:-1], dtype=torch.int32, device=device),
+        "q": _normal((len(lens), hq, d), g, device, True, torch.bfloat16),
+        "k": _normal((rows, d), g, device, True, torch.bfloat16),
+        "v": _normal((rows, d), g, device, True, torch.bfloat16),
+        "qi": torch.randint(lo, hi, (len(lens), di), generator=g, device=device, dtype=torch.int8),
+        "ki": torch.randint(lo, hi, (rows, di), generator=g, device=device, dtype=torch.int8),
+    }
+
+
 def decode_inputs(cfg, device="cpu", lens=None, seed=None, ring=None):
     """Decode batch: one query per sequence plus a filled cache.
 

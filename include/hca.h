@@ -365,6 +365,53 @@ HCA_API hca_status hca_attend_prefill_backward(const hca_params* params, int32_t
                                                void* dv, float* dw, void* workspace, size_t workspace_bytes,
                                                void* stream);
 
+/*
+ * Sparse attention of the full-context (MLA) layers, decode step.  The pages
+ * (release blog "ERNIE 5.5 Flash Base", section 2.1; Zhidx article, section
+ * 1; model card) describe it in outline only: a lightweight indexer scores
+ * the past positions of each query, core attention runs over the top-k
+ * highest-scoring positions, and these layers use 256-dim heads.  Fixed here
+ * (the pages give no indexer form and no k):
+ *
+ *   score(s) = qi . ki[s]   one int8 indexer head of width 128, exact integer
+ *   selection               the topk highest scores among positions 0 .. L-1
+ *                           (the query sits at L-1), equal scores to the
+ *                           smaller position; all positions when L <= topk
+ *   attention               64 query heads of width 256 attend under one
+ *                           softmax to the shared key / value rows (one KV
+ *                           head, width 256) of the selected positions
+ *
+ * hca_dsa_decode_workspace_bytes - scratch bytes hca_dsa_decode needs (0 for
+ * invalid sizes).
+ */
+HCA_API size_t hca_dsa_decode_workspace_bytes(int32_t batch, int32_t max_seqlen, int32_t topk);
+
+/*
+ * hca_dsa_decode - one query per sequence.
+ *
+ *   batch, max_seqlen, topk  host: B, max_b L_b (L_b >= 1), k >= 1
+ *   softmax_scale   <= 0: 1/16 (1/sqrt(256))
+ *   seqlens         device int32 [B]: L_b
+ *   cu_rows         device int32 [B]: first cache row of sequence b; its rows
+ *                   cu_rows[b] .. cu_rows[b] + L_b - 1 hold positions 0 .. L_b-1
+ *   q               device bf16 [B, 64, 256] queries
+ *   qi              device int8 [B, 128] indexer queries
+ *   k, v            device bf16 [rows, 256] key / value cache
+ *   ki              device int8 [rows, 128] indexer keys
+ *   o               device bf16 [B, 64, 256] output (written)
+ *   sel             device int32 [B, topk] selected positions in increasing
+ *                   order, -1 after the first min(topk, L_b) (written)
+ *   workspace       device scratch of hca_dsa_decode_workspace_bytes bytes
+ *                   (HCA_ERR_WORKSPACE when NULL or smaller)
+ *
+ * The selection is exact (integer scores), so it is the same on every device.
+ * Outputs must not alias inputs.
+ */
+HCA_API hca_status hca_dsa_decode(int32_t batch, int32_t max_seqlen, int32_t topk, float softmax_scale,
+                                  const int32_t* seqlens, const int32_t* cu_rows, const void* q,
+                                  const int8_t* qi, const void* k, const void* v, const int8_t* ki, void* o,
+                                  int32_t* sel, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 HCA_API const char* hca_status_string(hca_status status);
 

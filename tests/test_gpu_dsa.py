@@ -1,0 +1,55 @@
+"""GPU parity of the sparse-attention decode of the full-context layers
+(hca_dsa_decode) against the oracle: the selected positions bit for bit
+(integer scores decide them on both sides), the output within the bf16 bound
+(max-abs <= 1e-2, rel-L2 <= 5e-3)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import compressed_kv_sparse_amd as hca
+import oracle
+from hca_workloads import dsa_inputs
+from parity_util import assert_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _check(lens, topk, seed, ties=False):
+    print(f"case lens={lens[:6]} k={topk} ties={ties}", flush=True)
+    inp = dsa_inputs(lens, seed, DEV, ties=ties)
+    o, sel = hca.hca_dsa_decode(inp["seqlens"], inp["cu_rows"], inp["max_seqlen"], topk, inp["q"], inp["qi"],
+                                inp["k"], inp["v"], inp["ki"])
+    torch.cuda.synchronize()
+    ref, rsel = oracle.dsa_decode(inp["q"].cpu(), inp["qi"].cpu(), inp["k"].cpu(), inp["v"].cpu(), inp["ki"].cpu(),
+                                  lens, inp["cu_rows_host"], topk)
+    got = sel.cpu().numpy()
+    for b, L in enumerate(lens):
+        n = min(L, topk)
+        assert np.array_equal(got[b, :n], rsel[b]), f"selection of sequence {b} (L={L})"
+        assert np.all(got[b, n:] == -1)
+    assert_close(o, torch.tensor(ref), torch.bfloat16, f"dsa lens={lens[:4]} k={topk}")
+
+
+@pytest.mark.parametrize("lens,topk", [
+    ([1, 100, 2047, 2048, 2049, 5000], 2048),   # around k: all selected, exactly k, one dropped
+    ([3000, 17, 9000], 64),
+    ([4000], 1),
+    ([513, 257], 3),
+])
+def test_dsa_decode(lens, topk):
+    _check(lens, topk, seed=601)
+
+
+def test_dsa_decode_ties():
+    """Indexer values in {-1, 0, 1}: most scores are shared, so the tie rule
+    (smaller position first) decides most of the selection."""
+    _check([3000, 700], 64, seed=611, ties=True)
+    _check([5000], 2048, seed=612, ties=True)
+
+
+def test_dsa_decode_128k():
+    """One sequence at the workload's context length (131072) and k = 2048."""
+    _check([131072, 5], 2048, seed=621)

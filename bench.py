@@ -36,7 +36,9 @@ METRIC = "HCA prefill tokens/s (%MFMA peak) + decode queries/s (%HBM peak), 1 GP
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3
-WORKLOADS = ("prefill_8k", "prefill_128k", "decode_64x128k", "mixed_1m", "tiny_f32", "chunk_32k_at_224k")
+WORKLOADS = ("prefill_8k", "prefill_128k", "decode_64x128k", "mixed_1m", "tiny_f32", "chunk_32k_at_224k",
+             "dsa_decode_64x128k")
+DSA_BATCH, DSA_LEN, DSA_TOPK, DSA_SEED = 64, 131072, 2048, 1011
 EPILOGUE_RANK = 16  # head-mixing rank of the fused-epilogue measurement (the pages give none)
 _CS = "compressed_kv_sparse_amd/csrc/"
 KERNEL_SOURCES = {
@@ -48,6 +50,7 @@ KERNEL_SOURCES = {
     "ring_append": (_CS + "chunk.hip",),
     "decode_maintenance": (_CS + "compress.hip", _CS + "chunk.hip"),
     "backward": (_CS + "backward_bf16.hip", _CS + "bf16_tiles.h"),
+    "dsa_decode": (_CS + "dsa.hip",),
 }
 
 
@@ -90,6 +93,19 @@ def backward_work(c, lens, e):
     nblk = sum(l // c.block for l in lens)
     byt = ntok * (4 * c.hq * c.d * e + 4 * c.hkv * c.d * e + 4 * c.hq) + nblk * 2 * c.hkv * c.d * e
     return byt, pf // 4 * 10
+
+
+def dsa_work(lens, topk, hq=64, d=256, di=128):
+    """(bytes, flops) of one hca_dsa_decode call: every cached indexer key
+    read once (di int8 bytes per position), the selected K and V rows read
+    once, q read, o written, the selection written; 2*di integer ops per
+    scored position and 4*d*Hq flops per selected key."""
+    byt, flops = 0, 0
+    for L in lens:
+        n = min(L, topk)
+        byt += L * di + n * 2 * d * 2 + 2 * hq * d * 2 + di + topk * 4
+        flops += 2 * di * L + 4 * d * hq * n
+    return byt, flops
 
 
 def compress_work(c, lens, e):
@@ -426,6 +442,51 @@ def cpu_baseline_chunk(c, ci, seconds):
                       f"of the chunk's {L // c.block - p0 // c.block} blocks in {t_pool:.1f} s, prorated per token"}
 
 
+def run_dsa(torch, hca, args, clock):
+    """The sparse-attention decode step of the full-context layers: 64
+    sequences of 131072 cached positions, k = 2048 (1.2 GB of HBM traffic
+    per call, so the 256 MB last-level cache cannot serve repeats)."""
+    from hca_workloads import dsa_inputs
+
+    lens = [DSA_LEN] * DSA_BATCH
+    inp = dsa_inputs(lens, DSA_SEED, "cuda")
+    ws = torch.empty(hca.hca_dsa_decode_workspace_bytes(DSA_BATCH, DSA_LEN, DSA_TOPK), dtype=torch.uint8,
+                     device="cuda")
+    o = torch.empty_like(inp["q"])
+    sel = torch.empty((DSA_BATCH, DSA_TOPK), dtype=torch.int32, device="cuda")
+
+    def step(i=0):
+        clock.run("dsa_decode", lambda: hca.hca_dsa_decode(inp["seqlens"], inp["cu_rows"], DSA_LEN, DSA_TOPK, inp["q"],
+                                                           inp["qi"], inp["k"], inp["v"], inp["ki"], workspace=ws,
+                                                           o=o, sel=sel))
+
+    nwarm = warm_up(torch, step, args.warmup, args.min_warmup_s)
+    clock.reset()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return inp, wall, nwarm
+
+
+def cpu_baseline_dsa(inp, seconds):
+    """The oracle on as many of the sequences as fit in `seconds`."""
+    import oracle
+
+    t0 = time.perf_counter()
+    done = 0
+    while done < len(inp["lens"]) and (time.perf_counter() - t0 < seconds or done == 0):
+        b = done
+        oracle.dsa_decode(inp["q"][b:b + 1].cpu(), inp["qi"][b:b + 1].cpu(),
+                          inp["k"][b * DSA_LEN:(b + 1) * DSA_LEN].cpu(), inp["v"][b * DSA_LEN:(b + 1) * DSA_LEN].cpu(),
+                          inp["ki"][b * DSA_LEN:(b + 1) * DSA_LEN].cpu(), [DSA_LEN], [0], DSA_TOPK)
+        done += 1
+    el = time.perf_counter() - t0
+    return {"value": round(done / el, 3), "unit": "queries/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{done} of {len(inp['lens'])} sequences (131072 positions, k = 2048) in {el:.1f} s"}
+
+
 def run_decode(torch, hca, c, steps, warmup, clock, min_warm_s, n_sets=4):
     """Rotates n_sets independent caches so repeats do not hit in the 256 MiB
     last-level cache."""
@@ -533,6 +594,24 @@ def main():
         return
 
     clock = KernelClock(torch)
+    if args.workload == "dsa_decode_64x128k":
+        log(f"[bench] dsa_decode_64x128k: {DSA_BATCH} x {DSA_LEN} positions, k={DSA_TOPK}, steps={args.steps}")
+        inp, wall, nwarm = run_dsa(torch, hca, args, clock)
+        db, df = dsa_work(inp["lens"], DSA_TOPK)
+        t = clock.mean_ms("dsa_decode")
+        rl = roofline("dsa_decode", "dsa_decode_64x128k", db, df, t, "hbm")
+        out = {"metric": METRIC, "value": round(DSA_BATCH / (t * 1e-3), 1), "unit": "queries/s", "n_gpus": 1,
+               "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16 (int8 indexer)",
+               "data": "synthetic (seeded random tensors of the workload's shapes)",
+               "config": {"workload": "dsa_decode_64x128k", "batch": DSA_BATCH, "context": DSA_LEN, "topk": DSA_TOPK,
+                          "q_heads": 64, "head_dim": 256, "indexer_dim": 128, "parallelism": "none (1 GPU)"},
+               "roofline": rl, "warmup_steps_run": nwarm, "kernels": {"dsa_decode": rl}}
+        if not args.no_cpu_baseline:
+            log(f"[bench] cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")
+            out["cpu_baseline"] = cpu_baseline_dsa(inp, args.cpu_seconds)
+        print(json.dumps(out), flush=True)
+        return
     c = CONFIGS[args.workload]
     e = 2 if c.dtype == "bf16" else 4
     result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

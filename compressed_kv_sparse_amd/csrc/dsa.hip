@@ -15,14 +15,15 @@
 // Kernels, in launch order:
 //   dsa_zero_kernel    clears the per-sequence histogram of the score keys
 //   dsa_score_kernel   (chunk of 4096 positions, sequence): integer scores
-//                      with v_dot4 (sdot4), stored as keys u = score + 2^21
+//                      with v_dot4 (sdot4), 8 lanes per indexer row so that
+//                      the loads are contiguous, stored as keys u = score + 2^21
 //                      in [0, 2^22]; adds its histogram of u >> 11 to the
 //                      sequence's (global atomics on the non-empty bins)
 //   dsa_select_kernel  (sequence): the exact threshold key by a two-level
 //                      radix select (u >> 11 from the histogram, then u & 2047
 //                      by one pass over the keys), then the selected
-//                      positions in order: each thread counts its contiguous
-//                      range, one block scan, each thread writes its range
+//                      positions in order: each wave counts its contiguous
+//                      segment, then writes it with lane prefix sums
 //   dsa_attend_kernel  (split of 256 selected keys, sequence): 4 waves x 16
 //                      heads on v_mfma_f32_16x16x32_bf16, gathered K and V
 //                      rows double buffered in LDS, online softmax; writes
@@ -46,6 +47,9 @@ constexpr int SPLIT = 256;     // selected keys per attention workgroup
 constexpr int TK = 32;         // keys per attention tile
 constexpr int RS = 528;        // LDS bytes per staged key / value row (512 + 16)
 
+// keys per sequence row of the key buffer: max_seqlen rounded up to 256
+__host__ __device__ inline int key_stride(int max_seqlen) { return (max_seqlen + 255) / 256 * 256; }
+
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -67,9 +71,12 @@ __global__ __launch_bounds__(256) void dsa_zero_kernel(unsigned* hist, int n) {
 }
 
 // ---------------------------------------------------------------------------
-// Scores of positions [c CH, (c+1) CH) of sequence b: thread t takes
-// positions c CH + t + 256 j.  The keys go to keys[b][position] (row stride
-// max_seqlen), the histogram of u >> 11 to hist[b][HBINS].
+// Scores of positions [c CH, (c+1) CH) of sequence b.  Eight lanes share one
+// indexer row (lane l reads bytes 16 (l%8) .. +15 of row l/8 of its group),
+// so each wave load moves 8 whole rows (1 KiB, contiguous); three shuffles
+// add the 8 partial dot products.  Wave w takes rows 32 i + 8 w + l/8 of the
+// chunk, four groups per step in flight.  The keys go to keys[b][position],
+// the histogram of u >> 11 to hist[b][HBINS].
 __global__ __launch_bounds__(256) void dsa_score_kernel(DsaArgs a) {
   __shared__ unsigned hs[HBINS];
   const int c = blockIdx.x, b = blockIdx.y;
@@ -77,27 +84,35 @@ __global__ __launch_bounds__(256) void dsa_score_kernel(DsaArgs a) {
   const int p0 = c * CH;
   if (p0 >= L) return;
   for (int i = threadIdx.x; i < HBINS; i += 256) hs[i] = 0;
-  // the query's 32 dwords of int8 (the same for every thread)
-  const int* qw = (const int*)(a.qi + (size_t)b * DI);
-  int q[DI / 4];
-#pragma unroll
-  for (int j = 0; j < DI / 4; ++j) q[j] = qw[j];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, part = lane & 7;
+  // this lane's 16 bytes of the indexer query
+  const i32x4 q = *(const i32x4*)(a.qi + (size_t)b * DI + 16 * part);
   __syncthreads();
   const size_t r0 = (size_t)a.cu_rows[b];
-  unsigned* keys = a.keys + (size_t)b * a.max_seqlen;
+  unsigned* keys = a.keys + (size_t)b * key_stride(a.max_seqlen);
   const int p1 = min(L, p0 + CH);
-  for (int p = p0 + threadIdx.x; p < p1; p += 256) {
-    const i32x4* kr = (const i32x4*)(a.ki + (r0 + p) * DI);
-    int acc = 0;
+  for (int pb = p0 + 8 * wave + (lane >> 3); pb < p1; pb += 4 * 32) {
+    i32x4 kv[4];
 #pragma unroll
-    for (int j = 0; j < DI / 16; ++j) {
-      const i32x4 kv = kr[j];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_sdot4(q[4 * j + e], kv[e], acc, false);
+    for (int x = 0; x < 4; ++x) {
+      const int p = min(pb + 32 * x, p1 - 1);  // past the end: the last row again (not stored)
+      kv[x] = *(const i32x4*)(a.ki + (r0 + p) * DI + 16 * part);
     }
-    const unsigned u = (unsigned)(acc + KEY_OFF);
-    keys[p] = u;
-    atomicAdd(&hs[u >> 11], 1u);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      int acc = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_sdot4(q[e], kv[x][e], acc, false);
+      acc += __shfl_xor(acc, 1);
+      acc += __shfl_xor(acc, 2);
+      acc += __shfl_xor(acc, 4);
+      const int p = pb + 32 * x;
+      if (part == 0 && p < p1) {
+        const unsigned u = (unsigned)(acc + KEY_OFF);
+        keys[p] = u;
+        atomicAdd(&hs[u >> 11], 1u);
+      }
+    }
   }
   __syncthreads();
   unsigned* gh = a.hist + (size_t)b * HBINS;
@@ -106,116 +121,210 @@ __global__ __launch_bounds__(256) void dsa_score_kernel(DsaArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Block-wide exclusive scan of one value per thread (256 threads), in thread
-// order; returns the exclusive prefix and writes the total to *total.
-__device__ __forceinline__ unsigned block_scan(unsigned v, unsigned* ws, unsigned* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  unsigned x = v;  // inclusive scan within the wave
+// Keys are read four per lane (16 bytes): a "chunk" is 256 consecutive
+// positions, lane l holding 4l .. 4l+3.  Rows of the key buffer are padded
+// to a multiple of 256 positions; positions >= L are masked by index.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// exclusive prefix sum over the 64 lanes of a wave
+__device__ __forceinline__ unsigned wave_excl(unsigned v) {
+  const int lane = threadIdx.x & 63;
+  unsigned x = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const unsigned y = __shfl_up(x, o);
     if (lane >= o) x += y;
   }
-  if (lane == 63) ws[wave] = x;
-  __syncthreads();
-  unsigned before = 0, tot = 0;
+  return x - v;
+}
+__device__ __forceinline__ unsigned wave_sum(unsigned v) {
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    if (w < wave) before += ws[w];
-    tot += ws[w];
-  }
-  __syncthreads();
-  *total = tot;
-  return before + x - v;
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
 }
 
 // Sequence b: the selected positions, increasing, into sel[b][0 .. k) (-1
-// after the first min(k, L)).
-__global__ __launch_bounds__(256) void dsa_select_kernel(DsaArgs a) {
-  __shared__ unsigned lh[LBINS];
-  __shared__ unsigned wsum[4];
-  __shared__ unsigned pick[4];  // hi bin, count above it, threshold key, ties to take
+// after the first min(k, L)).  256 threads = 4 waves; wave w owns the
+// contiguous segment of chunks [w C, (w+1) C).
+//  1. the hi bin (u >> 11) that holds the k-th largest key, from the
+//     histogram summed from the top;
+//  2. one pass over the keys: each wave counts its keys above the hi bin
+//     and builds its own histogram of the low bits inside the bin; their
+//     sum gives the exact threshold key and the ties at it to take, and each
+//     wave's counts follow from its own histogram;
+//  3. each wave writes its segment in order (ballot prefix counts per chunk),
+//     after the keys of the waves before it, taking ties while its budget
+//     lasts.
+constexpr int SEL_BATCH = 8;  // chunks of keys in flight per wave
+
+__global__ __launch_bounds__(256) void dsa_select_kernel(DsaArgs a, int kstride) {
+  __shared__ unsigned lh[4][LBINS];  // per wave
+  __shared__ unsigned cnt_s[256];
+  __shared__ unsigned seg[2][4];     // per wave: keys above the threshold, ties at it
+  __shared__ unsigned above_s[4];    // per wave: keys above the hi bin
+  __shared__ unsigned pick[4];       // hi bin, count above it, threshold key, ties to take
   const int b = blockIdx.x;
   const int L = a.seqlens[b];
   const int k = a.topk;
   int* sel = a.sel + (size_t)b * k;
-  const unsigned* keys = a.keys + (size_t)b * a.max_seqlen;
-  const int tid = threadIdx.x;
+  const u32x4* keys4 = (const u32x4*)(a.keys + (size_t)b * kstride);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (L <= k) {  // every position
     for (int i = tid; i < k; i += 256) sel[i] = i < L ? i : -1;
     return;
   }
-  // 1. hi bin from the histogram, counted from the top: thread t owns bins
-  // HBINS-1-8t .. HBINS-8-8t (9 for the last thread)
+  // 1. hi bin
   const unsigned* gh = a.hist + (size_t)b * HBINS;
-  const int top = HBINS - 1 - 8 * tid;
-  const int nb = tid == 255 ? HBINS - 8 * 255 : 8;
-  unsigned cnt = 0;
-  for (int i = 0; i < nb; ++i) cnt += gh[top - i];
-  unsigned tot;
-  const unsigned above = block_scan(cnt, wsum, &tot);  // keys in bins above this thread's
-  if (above < (unsigned)k && above + cnt >= (unsigned)k) {
-    unsigned acc = above;
-    for (int i = 0; i < nb; ++i) {
-      const unsigned h = gh[top - i];
-      if (acc + h >= (unsigned)k) {
-        pick[0] = top - i;
-        pick[1] = acc;
-        break;
-      }
-      acc += h;
-    }
-  }
-  for (int i = tid; i < LBINS; i += 256) lh[i] = 0;
-  __syncthreads();
-  const unsigned hbin = pick[0], n_above = pick[1];
-  // 2. low bits of the keys in the hi bin
-  for (int p = tid; p < L; p += 256) {
-    const unsigned u = keys[p];
-    if ((u >> 11) == hbin) atomicAdd(&lh[u & 2047], 1u);
-  }
-  __syncthreads();
   {
-    const int ltop = LBINS - 1 - 8 * tid;
-    unsigned c2 = 0;
-    for (int i = 0; i < 8; ++i) c2 += lh[ltop - i];
-    unsigned t2;
-    const unsigned ab = n_above + block_scan(c2, wsum, &t2);
-    if (ab < (unsigned)k && ab + c2 >= (unsigned)k) {
-      unsigned acc = ab;
-      for (int i = 0; i < 8; ++i) {
-        const unsigned h = lh[ltop - i];
+    const int top = HBINS - 1 - 8 * tid;
+    const int nb = tid == 255 ? HBINS - 8 * 255 : 8;
+    unsigned c = 0;
+    for (int i = 0; i < nb; ++i) c += gh[top - i];
+    cnt_s[tid] = c;
+    for (int i = lane; i < LBINS; i += 64) lh[wave][i] = 0;
+    __syncthreads();
+    if (tid == 0) {  // 256 partial sums, top down
+      unsigned acc = 0;
+      int t = 0;
+      while (acc + cnt_s[t] < (unsigned)k) acc += cnt_s[t++];
+      const int tp = HBINS - 1 - 8 * t;
+      const int nbt = t == 255 ? HBINS - 8 * 255 : 8;
+      for (int i = 0; i < nbt; ++i) {
+        const unsigned h = gh[tp - i];
         if (acc + h >= (unsigned)k) {
-          pick[2] = (hbin << 11) | (unsigned)(ltop - i);
-          pick[3] = (unsigned)k - acc;  // ties at the threshold to take, in position order
+          pick[0] = tp - i;
+          pick[1] = acc;
           break;
         }
         acc += h;
       }
     }
+    __syncthreads();
+  }
+  const unsigned hbin = pick[0], n_above = pick[1];
+  const int nch = (L + 255) / 256;  // chunks of 256 positions
+  const int C = (nch + 3) / 4;
+  const int cb = wave * C, ce = min(nch, cb + C);
+  // 2. the wave's keys above the hi bin and its histogram of the low bits in it
+  unsigned above = 0;
+  for (int c0 = cb; c0 < ce; c0 += SEL_BATCH) {
+    u32x4 kv[SEL_BATCH];
+#pragma unroll
+    for (int j = 0; j < SEL_BATCH; ++j) kv[j] = c0 + j < ce ? keys4[(c0 + j) * 64 + lane] : u32x4{};
+#pragma unroll
+    for (int j = 0; j < SEL_BATCH; ++j) {
+      const int p0 = (c0 + j) * 256 + 4 * lane;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const unsigned u = kv[j][e];
+        if (c0 + j < ce && p0 + e < L) {
+          above += (u >> 11) > hbin;
+          if ((u >> 11) == hbin) atomicAdd(&lh[wave][u & 2047], 1u);
+        }
+      }
+    }
+  }
+  above = wave_sum(above);
+  if (lane == 0) above_s[wave] = above;
+  __syncthreads();
+  {
+    const int ltop = LBINS - 1 - 8 * tid;
+    unsigned c = 0;
+    for (int i = 0; i < 8; ++i) c += lh[0][ltop - i] + lh[1][ltop - i] + lh[2][ltop - i] + lh[3][ltop - i];
+    cnt_s[tid] = c;
+    __syncthreads();
+    if (tid == 0) {
+      unsigned acc = n_above;
+      int t = 0;
+      while (acc + cnt_s[t] < (unsigned)k) acc += cnt_s[t++];
+      const int lt = LBINS - 1 - 8 * t;
+      for (int i = 0; i < 8; ++i) {
+        const int bin = lt - i;
+        const unsigned h = lh[0][bin] + lh[1][bin] + lh[2][bin] + lh[3][bin];
+        if (acc + h >= (unsigned)k) {
+          pick[2] = (hbin << 11) | (unsigned)bin;
+          pick[3] = (unsigned)k - acc;  // ties at the threshold, taken in position order
+          break;
+        }
+        acc += h;
+      }
+    }
+    __syncthreads();
+  }
+  const unsigned thr = pick[2], n_eq = pick[3];
+  {  // this wave's keys above the threshold and ties at it, from its histogram
+    const unsigned lo = thr & 2047;
+    unsigned g = 0;
+    for (int i = lo + 1 + lane; i < LBINS; i += 64) g += lh[wave][i];
+    g = wave_sum(g);
+    if (lane == 0) {
+      seg[0][wave] = above_s[wave] + g;
+      seg[1][wave] = lh[wave][lo];
+    }
   }
   __syncthreads();
-  const unsigned thr = pick[2], n_eq = pick[3];
-  // 3. thread t scans positions [t R, (t+1) R): counts, scans, then writes
-  const int R = (L + 255) / 256;
-  const int q0 = min(L, tid * R), q1 = min(L, q0 + R);
-  unsigned gt = 0, eq = 0;
-  for (int p = q0; p < q1; ++p) {
-    const unsigned u = keys[p];
-    gt += u > thr;
-    eq += u == thr;
+  unsigned out = 0, eq_before = 0;
+  for (int w = 0; w < wave; ++w) {
+    const unsigned take = eq_before >= n_eq ? 0u : min(seg[1][w], n_eq - eq_before);
+    out += seg[0][w] + take;
+    eq_before += seg[1][w];
   }
-  unsigned t_gt, t_eq;
-  const unsigned eq_before = block_scan(eq, wsum, &t_eq);
-  const unsigned eq_take = eq_before >= n_eq ? 0u : min(eq, n_eq - eq_before);
-  const unsigned out_before = block_scan(gt + eq_take, wsum, &t_gt);
-  unsigned o = out_before, taken = 0;
-  for (int p = q0; p < q1; ++p) {
-    const unsigned u = keys[p];
-    if (u > thr || (u == thr && taken < eq_take)) {
-      if (u == thr) ++taken;
-      if (o < (unsigned)k) sel[o] = p;  // the counts above make o < k; the guard keeps writes in the row
-      ++o;
+  const unsigned budget = eq_before >= n_eq ? 0u : min(seg[1][wave], n_eq - eq_before);  // ties this wave takes
+  // 3. ordered output of the segment
+  const unsigned long long below = (1ull << lane) - 1ull;  // lanes before this one
+  unsigned ties_seen = 0;
+  for (int c0 = cb; c0 < ce; c0 += SEL_BATCH) {
+    u32x4 kv[SEL_BATCH];
+#pragma unroll
+    for (int j = 0; j < SEL_BATCH; ++j) kv[j] = c0 + j < ce ? keys4[(c0 + j) * 64 + lane] : u32x4{};
+#pragma unroll
+    for (int j = 0; j < SEL_BATCH; ++j) {
+      if (c0 + j >= ce) break;
+      const int p0 = (c0 + j) * 256 + 4 * lane;
+      bool g4[4], e4[4];
+      unsigned ng = 0, ne = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool in = p0 + e < L;
+        g4[e] = in && kv[j][e] > thr;
+        e4[e] = in && kv[j][e] == thr;
+        ng += g4[e];
+        ne += e4[e];
+      }
+      const unsigned long long any = __ballot(ng + ne > 0);
+      if (any == 0) continue;  // nothing selected in this chunk
+      // ties of the lanes before this one, then this lane's ties in the budget
+      unsigned te = 0, tt = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const unsigned long long m = __ballot(e4[e]);
+        te += __popcll(m & below);
+        tt += __popcll(m);
+      }
+      const unsigned tb = ties_seen + te;
+      const unsigned nt = tb >= budget ? 0u : min(ne, budget - tb);
+      unsigned oe = 0, ot = 0;
+      const unsigned long long mt = __ballot(nt > 0);
+      (void)mt;
+      // output slots of the lanes before this one: their keys above plus their ties taken
+      unsigned mine = ng + nt;
+#pragma unroll
+      for (int bit = 0; bit < 3; ++bit) {  // mine <= 4: three ballots of its bits
+        const unsigned long long m = __ballot((mine >> bit) & 1u);
+        oe += (unsigned)__popcll(m & below) << bit;
+        ot += (unsigned)__popcll(m) << bit;
+      }
+      unsigned o = out + oe, taken = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (g4[e] || (e4[e] && taken < nt)) {
+          if (e4[e]) ++taken;
+          if (o < (unsigned)k) sel[o] = p0 + e;  // the counts make o < k; the guard keeps writes in the row
+          ++o;
+        }
+      }
+      out += ot;
+      ties_seen += tt;
     }
   }
 }
@@ -390,7 +499,7 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 size_t dsa_workspace_bytes(int batch, int max_seqlen, int topk) {
   const int nsplit = (std::min(max_seqlen, topk) + SPLIT - 1) / SPLIT;
   size_t n = 0;
-  n += align256((size_t)batch * max_seqlen * sizeof(unsigned));   // keys
+  n += align256((size_t)batch * key_stride(max_seqlen) * sizeof(unsigned));  // keys
   n += align256((size_t)batch * HBINS * sizeof(unsigned));        // histogram
   n += 2 * align256((size_t)batch * nsplit * HQ * sizeof(float)); // m, l
   n += align256((size_t)batch * nsplit * HQ * DD * sizeof(bf16)); // O / l
@@ -401,7 +510,7 @@ hipError_t launch_dsa_decode(DsaArgs a, hipStream_t s) {
   const int nsplit = (std::min(a.max_seqlen, a.topk) + SPLIT - 1) / SPLIT;
   char* w = (char*)a.ws;
   a.keys = (unsigned*)w;
-  w += align256((size_t)a.batch * a.max_seqlen * sizeof(unsigned));
+  w += align256((size_t)a.batch * key_stride(a.max_seqlen) * sizeof(unsigned));
   a.hist = (unsigned*)w;
   w += align256((size_t)a.batch * HBINS * sizeof(unsigned));
   a.part_m = (float*)w;
@@ -412,7 +521,7 @@ hipError_t launch_dsa_decode(DsaArgs a, hipStream_t s) {
   const int nh = a.batch * HBINS;
   dsa_zero_kernel<<<(nh + 255) / 256, 256, 0, s>>>(a.hist, nh);
   dsa_score_kernel<<<dim3((a.max_seqlen + CH - 1) / CH, a.batch), 256, 0, s>>>(a);
-  dsa_select_kernel<<<a.batch, 256, 0, s>>>(a);
+  dsa_select_kernel<<<a.batch, 256, 0, s>>>(a, key_stride(a.max_seqlen));
   dsa_attend_kernel<<<dim3(nsplit, a.batch), 256, 0, s>>>(a, nsplit);
   dsa_merge_kernel<<<a.batch, 256, 0, s>>>(a, nsplit);
   return hipGetLastError();

@@ -72,3 +72,13 @@ def test_backward_work(lens, window):
     # q, o, dout read and dq written (Hq rows); k, v read and dk, dv written
     # (Hkv rows); the fp32 lse read; the entries read
     assert byt == ntok * (4 * c.hq * c.d * 2 + 4 * c.hkv * c.d * 2 + 4 * c.hq) + entries * 2 * c.hkv * c.d * 2
+
+
+def test_dsa_work():
+    lens, k = [1, 2048, 131072], 2048
+    byt, flops = bench.dsa_work(lens, k)
+    sel = [min(L, k) for L in lens]
+    # indexer keys (128 int8 per position), selected K and V rows (256 bf16
+    # each), q and o (64 x 256 bf16), the indexer query, the selection
+    assert byt == sum(L * 128 + n * 2 * 256 * 2 + 2 * 64 * 256 * 2 + 128 + k * 4 for L, n in zip(lens, sel))
+    assert flops == sum(2 * 128 * L + 4 * 256 * 64 * n for L, n in zip(lens, sel))

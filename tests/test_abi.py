@@ -253,3 +253,58 @@ def test_decode_and_chunk_epilogue_validation(lib):
     assert chk(_p(), rank=0) == ERR_SHAPE
     assert chk(_p(dtype=hca.HCA_F32, num_q_heads=4, head_dim=64, window=64)) == ERR_UNSUPPORTED
     assert chk(_p(), batch=0) == OK
+
+
+def test_backward_validation(lib):
+    """hca_attend_prefill_lse / hca_attend_prefill_backward reject bad
+    arguments on the host (and the workspace size query agrees)."""
+    p = _p()
+    n_ws = lib.hca_attend_prefill_backward_workspace_bytes(ctypes.byref(p), 1, 8192, 64, 8192)
+    assert n_ws > 8 * 8192 * 512  # at least the fp32 row partials
+    assert lib.hca_attend_prefill_backward_workspace_bytes(ctypes.byref(_p(dtype=hca.HCA_F32)), 1, 8192, 64, 8192) == 0
+    assert lib.hca_attend_prefill_backward_workspace_bytes(ctypes.byref(_p(head_dim=128)), 1, 8192, 64, 8192) == 0
+
+    def bwd(params=p, batch=1, max_seqlen=300, ntok=300, nblk=2, w=DUMMY, dw=DUMMY, ws=DUMMY, ws_bytes=1 << 40,
+            ptr=DUMMY):
+        pp = ctypes.byref(params) if params is not None else None
+        return lib.hca_attend_prefill_backward(pp, batch, max_seqlen, ntok, nblk, ptr, ptr, ptr, ptr, ptr, w, ptr,
+                                               ptr, ptr, ptr, ptr, ptr, ptr, ptr, dw, ws, ws_bytes, None)
+
+    assert bwd(params=None) == ERR_NULL
+    assert bwd(params=_p(dtype=hca.HCA_F32)) == ERR_UNSUPPORTED
+    assert bwd(params=_p(num_q_heads=32)) == ERR_UNSUPPORTED
+    assert bwd(batch=-1) == ERR_SHAPE
+    assert bwd(ntok=100) == ERR_SHAPE          # fewer tokens than the longest sequence
+    assert bwd(nblk=3) == ERR_SHAPE            # more entries than complete blocks
+    assert bwd(w=NULL) == ERR_NULL
+    assert bwd(dw=NULL) == ERR_NULL
+    assert bwd(ws=NULL) == ERR_WORKSPACE
+    assert bwd(ws_bytes=16) == ERR_WORKSPACE
+    assert bwd(ptr=NULL) == ERR_NULL
+    # the lse forward: bf16 only, lse required
+    args = [ctypes.byref(p), 1, 300] + [DUMMY] * 8
+    assert lib.hca_attend_prefill_lse(*args, NULL, None) == ERR_NULL
+    pf = _p(dtype=hca.HCA_F32)
+    assert lib.hca_attend_prefill_lse(ctypes.byref(pf), 1, 300, *([DUMMY] * 8), DUMMY, None) == ERR_UNSUPPORTED
+
+
+def test_dsa_validation(lib):
+    """hca_dsa_decode rejects bad sizes, missing pointers and a short
+    workspace on the host; empty batches are a no-op."""
+    need = lib.hca_dsa_decode_workspace_bytes(4, 131072, 2048)
+    assert need >= 4 * 131072 * 4  # the keys alone
+    assert lib.hca_dsa_decode_workspace_bytes(4, 131072, 0) == 0
+
+    def dsa(batch=2, max_seqlen=1000, topk=64, scale=0.0, ptr=DUMMY, ws=DUMMY, ws_bytes=1 << 40):
+        return lib.hca_dsa_decode(batch, max_seqlen, topk, scale, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ws,
+                                  ws_bytes, None)
+
+    assert dsa(topk=0) == ERR_SHAPE
+    assert dsa(batch=-1) == ERR_SHAPE
+    assert dsa(batch=70000) == ERR_SHAPE
+    assert dsa(scale=float("nan")) == ERR_SHAPE
+    assert dsa(batch=0) == OK
+    assert dsa(max_seqlen=0) == OK
+    assert dsa(ptr=NULL) == ERR_NULL
+    assert dsa(ws=NULL) == ERR_WORKSPACE
+    assert dsa(ws_bytes=100) == ERR_WORKSPACE

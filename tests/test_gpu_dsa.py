@@ -53,3 +53,29 @@ def test_dsa_decode_ties():
 def test_dsa_decode_128k():
     """One sequence at the workload's context length (131072) and k = 2048."""
     _check([131072, 5], 2048, seed=621)
+
+
+@pytest.mark.parametrize("lens,topk", [
+    ([256, 4096, 4097, 8192], 2048),   # chunk and row-padding boundaries
+    ([1, 1, 1], 2048),                 # single-token sequences: the query sees only itself
+    ([2049, 4095], 2048),
+])
+def test_dsa_decode_boundaries(lens, topk):
+    _check(lens, topk, seed=631)
+
+
+def test_dsa_decode_rows_with_gaps():
+    """cu_rows is each sequence's first cache row, not a prefix sum: rows of
+    other data (here, random rows) may sit between the sequences."""
+    lens, gap, topk = [3000, 700, 5000], 37, 512
+    inp = dsa_inputs([L + gap for L in lens], 641, DEV)
+    starts = [int(c) + gap for c in inp["cu_rows_host"]]
+    cu = torch.tensor(starts, dtype=torch.int32, device=DEV)
+    sl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    o, sel = hca.hca_dsa_decode(sl, cu, max(lens), topk, inp["q"], inp["qi"], inp["k"], inp["v"], inp["ki"])
+    torch.cuda.synchronize()
+    ref, rsel = oracle.dsa_decode(inp["q"].cpu(), inp["qi"].cpu(), inp["k"].cpu(), inp["v"].cpu(), inp["ki"].cpu(),
+                                  lens, starts, topk)
+    for b in range(len(lens)):
+        assert np.array_equal(sel.cpu().numpy()[b, :min(lens[b], topk)], rsel[b])
+    assert_close(o, torch.tensor(ref), torch.bfloat16, "dsa rows with gaps")

@@ -19,11 +19,11 @@
 //                      the loads are contiguous, stored as keys u = score + 2^21
 //                      in [0, 2^22]; adds its histogram of u >> 11 to the
 //                      sequence's (global atomics on the non-empty bins)
-//   dsa_select_kernel  (sequence): the exact threshold key by a two-level
+//   dsa_lohist_kernel, dsa_count_kernel, dsa_emit_kernel  (chunk,
+//                      sequence): the exact threshold key by a two-level
 //                      radix select (u >> 11 from the histogram, then u & 2047
-//                      by one pass over the keys), then the selected
-//                      positions in order: each wave counts its contiguous
-//                      segment, then writes it with lane prefix sums
+//                      from a histogram of the keys in that bin), each
+//                      chunk's counts, then the selected positions in order
 //   dsa_attend_kernel  (split of 256 selected keys, sequence): 4 waves x 16
 //                      heads on v_mfma_f32_16x16x32_bf16, gathered K and V
 //                      rows double buffered in LDS, online softmax; writes
@@ -47,8 +47,9 @@ constexpr int SPLIT = 256;     // selected keys per attention workgroup
 constexpr int TK = 32;         // keys per attention tile
 constexpr int RS = 528;        // LDS bytes per staged key / value row (512 + 16)
 
-// keys per sequence row of the key buffer: max_seqlen rounded up to 256
-__host__ __device__ inline int key_stride(int max_seqlen) { return (max_seqlen + 255) / 256 * 256; }
+// keys per sequence row of the key buffer: max_seqlen rounded up to a whole
+// chunk, so a chunk's 4096 keys are always inside its row
+__host__ __device__ inline int key_stride(int max_seqlen) { return (max_seqlen + CH - 1) / CH * CH; }
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -121,211 +122,283 @@ __global__ __launch_bounds__(256) void dsa_score_kernel(DsaArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Keys are read four per lane (16 bytes): a "chunk" is 256 consecutive
-// positions, lane l holding 4l .. 4l+3.  Rows of the key buffer are padded
-// to a multiple of 256 positions; positions >= L are masked by index.
+// Keys are read four per lane (16 bytes): a group of 256 consecutive
+// positions has lane l holding 4l .. 4l+3.  Rows of the key buffer are padded
+// to whole chunks of CH positions; positions >= L are masked by index.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-// exclusive prefix sum over the 64 lanes of a wave
-__device__ __forceinline__ unsigned wave_excl(unsigned v) {
-  const int lane = threadIdx.x & 63;
-  unsigned x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const unsigned y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  return x - v;
-}
 __device__ __forceinline__ unsigned wave_sum(unsigned v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   return v;
 }
 
-// Sequence b: the selected positions, increasing, into sel[b][0 .. k) (-1
-// after the first min(k, L)).  256 threads = 4 waves; wave w owns the
-// contiguous segment of chunks [w C, (w+1) C).
-//  1. the hi bin (u >> 11) that holds the k-th largest key, from the
-//     histogram summed from the top;
-//  2. one pass over the keys: each wave counts its keys above the hi bin
-//     and builds its own histogram of the low bits inside the bin; their
-//     sum gives the exact threshold key and the ties at it to take, and each
-//     wave's counts follow from its own histogram;
-//  3. each wave writes its segment in order (ballot prefix counts per chunk),
-//     after the keys of the waves before it, taking ties while its budget
-//     lasts.
-constexpr int SEL_BATCH = 8;  // chunks of keys in flight per wave
+// The selection runs on chunks of CH positions (the scoring's), in three
+// kernels; each recomputes the same thresholds from the histograms, so all
+// workgroups agree:
+//   dsa_lohist_kernel  the hi bin (u >> 11) holding the k-th largest key,
+//                      from the histogram; the chunk's histogram of the low
+//                      bits of the keys in that bin, added to the sequence's;
+//   dsa_count_kernel   the exact threshold key and the ties at it to take
+//                      (from both histograms); the chunk's keys above the
+//                      threshold and at it;
+//   dsa_emit_kernel    the chunk's output offset and tie budget from the
+//                      counts of the chunks before it; its selected
+//                      positions in order (per wave: 1024 positions, ballot
+//                      prefix counts).
 
-__global__ __launch_bounds__(256) void dsa_select_kernel(DsaArgs a, int kstride) {
-  __shared__ unsigned lh[4][LBINS];  // per wave
-  __shared__ unsigned cnt_s[256];
-  __shared__ unsigned seg[2][4];     // per wave: keys above the threshold, ties at it
-  __shared__ unsigned above_s[4];    // per wave: keys above the hi bin
-  __shared__ unsigned pick[4];       // hi bin, count above it, threshold key, ties to take
-  const int b = blockIdx.x;
+// Wave 0: the first t in the 256 partial counts cnt[] (ordered from the top
+// bin down) at which acc0 plus the running sum reaches k; res[0] = t,
+// res[1] = acc0 plus the counts before t.  Lane l scans cnt[4l .. 4l+3].
+__device__ __forceinline__ void first_reach(const unsigned* cnt, unsigned acc0, unsigned k, unsigned* res) {
+  const int lane = threadIdx.x & 63;
+  unsigned c[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) c[e] = cnt[4 * lane + e];
+  const unsigned tot = c[0] + c[1] + c[2] + c[3];
+  unsigned incl = tot;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const unsigned y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  const unsigned long long m = __ballot(acc0 + incl >= k);
+  const int first = m ? __builtin_ctzll(m) : 63;  // (every count reaches k: the bound keeps t < 256)
+  if (lane == first) {
+    unsigned acc = acc0 + incl - tot;
+    int t = 4 * lane;
+#pragma unroll
+    for (int e = 0; e < 3; ++e) {
+      if (acc + c[e] >= k) break;
+      acc += c[e];
+      ++t;
+    }
+    res[0] = (unsigned)t;
+    res[1] = acc;
+  }
+}
+
+// Bin selection shared by the selection kernels.  Thread t holds bins
+// top - 8t .. top - 8t - 7 of a histogram in registers (thread 255 of the
+// hi histogram also bin 0); `cnt` is 256 words of LDS, `res` 2, `pick` 4.
+//   find_hi:        pick[0] = the hi bin holding the k-th largest key,
+//                   pick[1] = keys in bins above it;
+//   find_threshold: pick[2] = the k-th largest key, pick[3] = the keys equal
+//                   to it that are selected (the first ones by position).
+__device__ __forceinline__ void find_hi(const unsigned* gh, int k, unsigned* cnt, unsigned* res, unsigned* pick) {
+  const int tid = threadIdx.x;
+  const int top = HBINS - 1 - 8 * tid;
+  unsigned h[9];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h[i] = gh[top - i];
+  h[8] = tid == 255 ? gh[0] : 0u;
+  unsigned c = 0;
+#pragma unroll
+  for (int i = 0; i < 9; ++i) c += h[i];
+  cnt[tid] = c;
+  __syncthreads();
+  if (tid < 64) first_reach(cnt, 0u, (unsigned)k, res);
+  __syncthreads();
+  if (tid == (int)res[0]) {
+    unsigned acc = res[1];
+    int i = 0;
+    while (i < 8 && acc + h[i] < (unsigned)k) acc += h[i++];
+    pick[0] = (unsigned)(top - i);
+    pick[1] = acc;
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ void find_threshold(const unsigned* lo, int k, unsigned* cnt, unsigned* res,
+                                               unsigned* pick) {
+  const int tid = threadIdx.x;
+  const int ltop = LBINS - 1 - 8 * tid;
+  unsigned h[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h[i] = lo[ltop - i];
+  unsigned c = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c += h[i];
+  cnt[tid] = c;
+  __syncthreads();
+  if (tid < 64) first_reach(cnt, pick[1], (unsigned)k, res);
+  __syncthreads();
+  if (tid == (int)res[0]) {
+    unsigned acc = res[1];
+    int i = 0;
+    while (i < 7 && acc + h[i] < (unsigned)k) acc += h[i++];
+    pick[2] = (pick[0] << 11) | (unsigned)(ltop - i);
+    pick[3] = (unsigned)k - acc;
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void dsa_lohist_kernel(DsaArgs a, int kstride) {
+  __shared__ unsigned lh[LBINS];
+  __shared__ unsigned cnt[256];
+  __shared__ unsigned res[2], pick[4];
+  const int c = blockIdx.x, b = blockIdx.y;
+  const int L = a.seqlens[b];
+  if (L <= a.topk || c * CH >= L) return;
+  for (int i = threadIdx.x; i < LBINS; i += 256) lh[i] = 0;
+  find_hi(a.hist + (size_t)b * HBINS, a.topk, cnt, res, pick);
+  const unsigned hbin = pick[0];
+  const u32x4* keys4 = (const u32x4*)(a.keys + (size_t)b * kstride + (size_t)c * CH);
+  const int n = min(CH, L - c * CH);
+  for (int i = threadIdx.x; 4 * i < n; i += 256) {
+    const u32x4 kv = keys4[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (4 * i + e < n && (kv[e] >> 11) == hbin) atomicAdd(&lh[kv[e] & 2047], 1u);
+  }
+  __syncthreads();
+  unsigned* gl = a.lohist + (size_t)b * LBINS;
+  for (int i = threadIdx.x; i < LBINS; i += 256)
+    if (lh[i]) atomicAdd(&gl[i], lh[i]);
+}
+
+__global__ __launch_bounds__(256) void dsa_count_kernel(DsaArgs a, int kstride, int nchunk) {
+  __shared__ unsigned cnt[256];
+  __shared__ unsigned res[2], pick[4];
+  __shared__ unsigned red[2][4];
+  const int c = blockIdx.x, b = blockIdx.y;
+  const int L = a.seqlens[b];
+  if (L <= a.topk || c * CH >= L) return;
+  find_hi(a.hist + (size_t)b * HBINS, a.topk, cnt, res, pick);
+  find_threshold(a.lohist + (size_t)b * LBINS, a.topk, cnt, res, pick);
+  const unsigned thr = pick[2];
+  const u32x4* keys4 = (const u32x4*)(a.keys + (size_t)b * kstride + (size_t)c * CH);
+  const int n = min(CH, L - c * CH);
+  unsigned gt = 0, eq = 0;
+  for (int i = threadIdx.x; 4 * i < n; i += 256) {
+    const u32x4 kv = keys4[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool in = 4 * i + e < n;
+      gt += in && kv[e] > thr;
+      eq += in && kv[e] == thr;
+    }
+  }
+  gt = wave_sum(gt);
+  eq = wave_sum(eq);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    red[0][wave] = gt;
+    red[1][wave] = eq;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned* out = a.chunk_cnt + ((size_t)b * nchunk + c) * 2;
+    out[0] = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+    out[1] = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+    if (c == 0) {
+      a.thr[2 * b] = thr;
+      a.thr[2 * b + 1] = pick[3];
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void dsa_emit_kernel(DsaArgs a, int kstride, int nchunk) {
+  __shared__ unsigned seg[2][4];  // per wave: keys above the threshold, ties at it
+  __shared__ unsigned base[2];    // output offset and ties before this chunk
+  const int c = blockIdx.x, b = blockIdx.y;
   const int L = a.seqlens[b];
   const int k = a.topk;
   int* sel = a.sel + (size_t)b * k;
-  const u32x4* keys4 = (const u32x4*)(a.keys + (size_t)b * kstride);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (L <= k) {  // every position
-    for (int i = tid; i < k; i += 256) sel[i] = i < L ? i : -1;
+  if (L <= k) {  // every position; chunk c writes slots [c CH, (c+1) CH) of the row
+    for (int i = c * CH + tid; i < min(k, (c + 1) * CH); i += 256) sel[i] = i < L ? i : -1;
     return;
   }
-  // 1. hi bin
-  const unsigned* gh = a.hist + (size_t)b * HBINS;
-  {
-    const int top = HBINS - 1 - 8 * tid;
-    const int nb = tid == 255 ? HBINS - 8 * 255 : 8;
-    unsigned c = 0;
-    for (int i = 0; i < nb; ++i) c += gh[top - i];
-    cnt_s[tid] = c;
-    for (int i = lane; i < LBINS; i += 64) lh[wave][i] = 0;
-    __syncthreads();
-    if (tid == 0) {  // 256 partial sums, top down
-      unsigned acc = 0;
-      int t = 0;
-      while (acc + cnt_s[t] < (unsigned)k) acc += cnt_s[t++];
-      const int tp = HBINS - 1 - 8 * t;
-      const int nbt = t == 255 ? HBINS - 8 * 255 : 8;
-      for (int i = 0; i < nbt; ++i) {
-        const unsigned h = gh[tp - i];
-        if (acc + h >= (unsigned)k) {
-          pick[0] = tp - i;
-          pick[1] = acc;
-          break;
-        }
-        acc += h;
-      }
+  if (c * CH >= L) return;
+  const unsigned thr = a.thr[2 * b], n_eq = a.thr[2 * b + 1];
+  if (wave == 0) {  // the chunks before this one: keys above, ties seen; of those ties the first n_eq are taken
+    unsigned gtb = 0, eqb = 0;
+    const unsigned* cc = a.chunk_cnt + (size_t)b * nchunk * 2;
+    for (int j = lane; j < c; j += 64) {
+      gtb += cc[2 * j];
+      eqb += cc[2 * j + 1];
     }
-    __syncthreads();
-  }
-  const unsigned hbin = pick[0], n_above = pick[1];
-  const int nch = (L + 255) / 256;  // chunks of 256 positions
-  const int C = (nch + 3) / 4;
-  const int cb = wave * C, ce = min(nch, cb + C);
-  // 2. the wave's keys above the hi bin and its histogram of the low bits in it
-  unsigned above = 0;
-  for (int c0 = cb; c0 < ce; c0 += SEL_BATCH) {
-    u32x4 kv[SEL_BATCH];
-#pragma unroll
-    for (int j = 0; j < SEL_BATCH; ++j) kv[j] = c0 + j < ce ? keys4[(c0 + j) * 64 + lane] : u32x4{};
-#pragma unroll
-    for (int j = 0; j < SEL_BATCH; ++j) {
-      const int p0 = (c0 + j) * 256 + 4 * lane;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const unsigned u = kv[j][e];
-        if (c0 + j < ce && p0 + e < L) {
-          above += (u >> 11) > hbin;
-          if ((u >> 11) == hbin) atomicAdd(&lh[wave][u & 2047], 1u);
-        }
-      }
-    }
-  }
-  above = wave_sum(above);
-  if (lane == 0) above_s[wave] = above;
-  __syncthreads();
-  {
-    const int ltop = LBINS - 1 - 8 * tid;
-    unsigned c = 0;
-    for (int i = 0; i < 8; ++i) c += lh[0][ltop - i] + lh[1][ltop - i] + lh[2][ltop - i] + lh[3][ltop - i];
-    cnt_s[tid] = c;
-    __syncthreads();
-    if (tid == 0) {
-      unsigned acc = n_above;
-      int t = 0;
-      while (acc + cnt_s[t] < (unsigned)k) acc += cnt_s[t++];
-      const int lt = LBINS - 1 - 8 * t;
-      for (int i = 0; i < 8; ++i) {
-        const int bin = lt - i;
-        const unsigned h = lh[0][bin] + lh[1][bin] + lh[2][bin] + lh[3][bin];
-        if (acc + h >= (unsigned)k) {
-          pick[2] = (hbin << 11) | (unsigned)bin;
-          pick[3] = (unsigned)k - acc;  // ties at the threshold, taken in position order
-          break;
-        }
-        acc += h;
-      }
-    }
-    __syncthreads();
-  }
-  const unsigned thr = pick[2], n_eq = pick[3];
-  {  // this wave's keys above the threshold and ties at it, from its histogram
-    const unsigned lo = thr & 2047;
-    unsigned g = 0;
-    for (int i = lo + 1 + lane; i < LBINS; i += 64) g += lh[wave][i];
-    g = wave_sum(g);
+    gtb = wave_sum(gtb);
+    eqb = wave_sum(eqb);
     if (lane == 0) {
-      seg[0][wave] = above_s[wave] + g;
-      seg[1][wave] = lh[wave][lo];
+      base[0] = gtb + min(eqb, n_eq);
+      base[1] = eqb;
     }
+  }
+  const int n = min(CH, L - c * CH);
+  const int p0c = c * CH;
+  // wave w: positions [1024 w, 1024 (w+1)) of the chunk, four groups of 256
+  const u32x4* keys4 = (const u32x4*)(a.keys + (size_t)b * kstride + (size_t)p0c);
+  u32x4 kv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) kv[j] = keys4[(4 * wave + j) * 64 + lane];  // inside the padded row
+  unsigned gt = 0, eq = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int q = (4 * wave + j) * 256 + 4 * lane + e;
+      gt += q < n && kv[j][e] > thr;
+      eq += q < n && kv[j][e] == thr;
+    }
+  gt = wave_sum(gt);
+  eq = wave_sum(eq);
+  if (lane == 0) {
+    seg[0][wave] = gt;
+    seg[1][wave] = eq;
   }
   __syncthreads();
-  unsigned out = 0, eq_before = 0;
+  unsigned out = base[0], eqb = base[1];
   for (int w = 0; w < wave; ++w) {
-    const unsigned take = eq_before >= n_eq ? 0u : min(seg[1][w], n_eq - eq_before);
+    const unsigned take = eqb >= n_eq ? 0u : min(seg[1][w], n_eq - eqb);
     out += seg[0][w] + take;
-    eq_before += seg[1][w];
+    eqb += seg[1][w];
   }
-  const unsigned budget = eq_before >= n_eq ? 0u : min(seg[1][wave], n_eq - eq_before);  // ties this wave takes
-  // 3. ordered output of the segment
-  const unsigned long long below = (1ull << lane) - 1ull;  // lanes before this one
+  const unsigned budget = eqb >= n_eq ? 0u : min(seg[1][wave], n_eq - eqb);  // ties this wave takes
+  const unsigned long long below = (1ull << lane) - 1ull;
   unsigned ties_seen = 0;
-  for (int c0 = cb; c0 < ce; c0 += SEL_BATCH) {
-    u32x4 kv[SEL_BATCH];
 #pragma unroll
-    for (int j = 0; j < SEL_BATCH; ++j) kv[j] = c0 + j < ce ? keys4[(c0 + j) * 64 + lane] : u32x4{};
+  for (int j = 0; j < 4; ++j) {
+    const int q0 = (4 * wave + j) * 256 + 4 * lane;
+    bool g4[4], e4[4];
+    unsigned ng = 0, ne = 0;
 #pragma unroll
-    for (int j = 0; j < SEL_BATCH; ++j) {
-      if (c0 + j >= ce) break;
-      const int p0 = (c0 + j) * 256 + 4 * lane;
-      bool g4[4], e4[4];
-      unsigned ng = 0, ne = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool in = p0 + e < L;
-        g4[e] = in && kv[j][e] > thr;
-        e4[e] = in && kv[j][e] == thr;
-        ng += g4[e];
-        ne += e4[e];
-      }
-      const unsigned long long any = __ballot(ng + ne > 0);
-      if (any == 0) continue;  // nothing selected in this chunk
-      // ties of the lanes before this one, then this lane's ties in the budget
-      unsigned te = 0, tt = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const unsigned long long m = __ballot(e4[e]);
-        te += __popcll(m & below);
-        tt += __popcll(m);
-      }
-      const unsigned tb = ties_seen + te;
-      const unsigned nt = tb >= budget ? 0u : min(ne, budget - tb);
-      unsigned oe = 0, ot = 0;
-      const unsigned long long mt = __ballot(nt > 0);
-      (void)mt;
-      // output slots of the lanes before this one: their keys above plus their ties taken
-      unsigned mine = ng + nt;
-#pragma unroll
-      for (int bit = 0; bit < 3; ++bit) {  // mine <= 4: three ballots of its bits
-        const unsigned long long m = __ballot((mine >> bit) & 1u);
-        oe += (unsigned)__popcll(m & below) << bit;
-        ot += (unsigned)__popcll(m) << bit;
-      }
-      unsigned o = out + oe, taken = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (g4[e] || (e4[e] && taken < nt)) {
-          if (e4[e]) ++taken;
-          if (o < (unsigned)k) sel[o] = p0 + e;  // the counts make o < k; the guard keeps writes in the row
-          ++o;
-        }
-      }
-      out += ot;
-      ties_seen += tt;
+    for (int e = 0; e < 4; ++e) {
+      g4[e] = q0 + e < n && kv[j][e] > thr;
+      e4[e] = q0 + e < n && kv[j][e] == thr;
+      ng += g4[e];
+      ne += e4[e];
     }
+    if (__ballot(ng + ne > 0) == 0) continue;
+    unsigned te = 0, tt = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const unsigned long long m = __ballot(e4[e]);
+      te += __popcll(m & below);
+      tt += __popcll(m);
+    }
+    const unsigned tb = ties_seen + te;
+    const unsigned nt = tb >= budget ? 0u : min(ne, budget - tb);
+    const unsigned mine = ng + nt;
+    unsigned oe = 0, ot = 0;
+#pragma unroll
+    for (int bit = 0; bit < 3; ++bit) {  // mine <= 4
+      const unsigned long long m = __ballot((mine >> bit) & 1u);
+      oe += (unsigned)__popcll(m & below) << bit;
+      ot += (unsigned)__popcll(m) << bit;
+    }
+    unsigned o = out + oe, taken = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (g4[e] || (e4[e] && taken < nt)) {
+        if (e4[e]) ++taken;
+        if (o < (unsigned)k) sel[o] = p0c + q0 + e;  // the counts make o < k; the guard keeps writes in the row
+        ++o;
+      }
+    }
+    out += ot;
+    ties_seen += tt;
   }
 }
 
@@ -501,6 +574,9 @@ size_t dsa_workspace_bytes(int batch, int max_seqlen, int topk) {
   size_t n = 0;
   n += align256((size_t)batch * key_stride(max_seqlen) * sizeof(unsigned));  // keys
   n += align256((size_t)batch * HBINS * sizeof(unsigned));        // histogram
+  n += align256((size_t)batch * LBINS * sizeof(unsigned));        // low-bit histogram in the hi bin
+  n += align256((size_t)batch * ((max_seqlen + CH - 1) / CH) * 2 * sizeof(unsigned));  // chunk counts
+  n += align256((size_t)batch * 2 * sizeof(unsigned));            // threshold, ties
   n += 2 * align256((size_t)batch * nsplit * HQ * sizeof(float)); // m, l
   n += align256((size_t)batch * nsplit * HQ * DD * sizeof(bf16)); // O / l
   return n;
@@ -511,17 +587,29 @@ hipError_t launch_dsa_decode(DsaArgs a, hipStream_t s) {
   char* w = (char*)a.ws;
   a.keys = (unsigned*)w;
   w += align256((size_t)a.batch * key_stride(a.max_seqlen) * sizeof(unsigned));
+  const int nchunk = (a.max_seqlen + CH - 1) / CH;
   a.hist = (unsigned*)w;
   w += align256((size_t)a.batch * HBINS * sizeof(unsigned));
+  a.lohist = (unsigned*)w;
+  w += align256((size_t)a.batch * LBINS * sizeof(unsigned));
+  a.chunk_cnt = (unsigned*)w;
+  w += align256((size_t)a.batch * nchunk * 2 * sizeof(unsigned));
+  a.thr = (unsigned*)w;
+  w += align256((size_t)a.batch * 2 * sizeof(unsigned));
   a.part_m = (float*)w;
   w += align256((size_t)a.batch * nsplit * HQ * sizeof(float));
   a.part_l = (float*)w;
   w += align256((size_t)a.batch * nsplit * HQ * sizeof(float));
   a.part_o = (bf16*)w;
-  const int nh = a.batch * HBINS;
+  // the two histograms are contiguous (HBINS + LBINS words per sequence, each part 256-byte aligned)
+  const int nh = (int)(((char*)a.chunk_cnt - (char*)a.hist) / sizeof(unsigned));
   dsa_zero_kernel<<<(nh + 255) / 256, 256, 0, s>>>(a.hist, nh);
-  dsa_score_kernel<<<dim3((a.max_seqlen + CH - 1) / CH, a.batch), 256, 0, s>>>(a);
-  dsa_select_kernel<<<a.batch, 256, 0, s>>>(a, key_stride(a.max_seqlen));
+  const dim3 chunks(nchunk, a.batch);
+  const int ks = key_stride(a.max_seqlen);
+  dsa_score_kernel<<<chunks, 256, 0, s>>>(a);
+  dsa_lohist_kernel<<<chunks, 256, 0, s>>>(a, ks);
+  dsa_count_kernel<<<chunks, 256, 0, s>>>(a, ks, nchunk);
+  dsa_emit_kernel<<<dim3(std::max(nchunk, (a.topk + CH - 1) / CH), a.batch), 256, 0, s>>>(a, ks, nchunk);
   dsa_attend_kernel<<<dim3(nsplit, a.batch), 256, 0, s>>>(a, nsplit);
   dsa_merge_kernel<<<a.batch, 256, 0, s>>>(a, nsplit);
   return hipGetLastError();

@@ -198,6 +198,9 @@ struct DsaArgs {
   // set by the launcher
   unsigned* keys;          // [B, max_seqlen] score + 2^21
   unsigned* hist;          // [B, 2049] histogram of key >> 11
+  unsigned* lohist;        // [B, 2048] histogram of key & 2047 inside the selected hi bin
+  unsigned* chunk_cnt;     // [B, chunks, 2] keys above the threshold, ties at it
+  unsigned* thr;           // [B, 2] threshold key, ties to take
   float* part_m;           // [B, nsplit, 64]
   float* part_l;
   bf16* part_o;            // [B, nsplit, 64, 256]

@@ -28,7 +28,7 @@
 //                      heads on v_mfma_f32_16x16x32_bf16, gathered K and V
 //                      rows double buffered in LDS, online softmax; writes
 //                      m, l and O / l per split
-//   dsa_merge_kernel   (sequence): combines the splits in order.
+//   dsa_merge_kernel   (8 heads, sequence): combines the splits in order.
 #include <algorithm>
 
 #include "hca_internal.h"
@@ -415,8 +415,9 @@ __device__ __forceinline__ bf16x8 lds_tr(const char HCA_LDS* base) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-__global__ __launch_bounds__(256) void dsa_attend_kernel(DsaArgs a, int nsplit) {
+__global__ __launch_bounds__(256, 2) void dsa_attend_kernel(DsaArgs a, int nsplit) {
   __shared__ __attribute__((aligned(16))) char kv_s[2][2 * TK * RS];
+  __shared__ int row_s[SPLIT];  // cache row of each selected key of the split
   const int s = blockIdx.x, b = blockIdx.y;
   const int L = a.seqlens[b];
   const int nsel = min(L, a.topk);
@@ -425,10 +426,15 @@ __global__ __launch_bounds__(256) void dsa_attend_kernel(DsaArgs a, int nsplit) 
   const int k1 = min(nsel, k0 + SPLIT);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, r = lane & 15;
   const int head = wave * 16 + r;
-  const int* sel = a.sel + (size_t)b * a.topk;
-  const size_t r0 = (size_t)a.cu_rows[b];
   const bf16* kg = (const bf16*)a.k;
   const bf16* vg = (const bf16*)a.v;
+  {
+    // slots past k1 repeat the last selected key (their scores are masked);
+    // positions are clamped to the sequence's rows
+    const int* sel = a.sel + (size_t)b * a.topk;
+    const int kk = min(k0 + (int)threadIdx.x, k1 - 1);
+    row_s[threadIdx.x] = a.cu_rows[b] + min(max(sel[kk], 0), L - 1);
+  }
 
   bf16x8 qf[DD / 32];  // Q^T: lane l = head l%16, d = 32k + 8g .. +7
   {
@@ -436,14 +442,13 @@ __global__ __launch_bounds__(256) void dsa_attend_kernel(DsaArgs a, int nsplit) 
 #pragma unroll
     for (int kk = 0; kk < DD / 32; ++kk) qf[kk] = *(const bf16x8*)(qr + 32 * kk);
   }
-  // gather of one tile: thread t copies 16-byte chunks t, t+256 of the 32 K
-  // rows and of the 32 V rows (32 chunks per row)
+  // gather of one tile: thread t copies 16-byte chunks t, t+256, t+512, t+768
+  // of the 32 K rows and of the 32 V rows (32 chunks per row)
   auto load_tile = [&](int t0, bf16x8 (&st)[8]) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c = threadIdx.x + 256 * j, row = c >> 5, col = c & 31;
-      const int kk = t0 + row;
-      const size_t pos = r0 + (size_t)min(max(sel[min(kk, k1 - 1)], 0), L - 1);  // clamp: rows of the sequence
+      const size_t pos = (size_t)row_s[t0 - k0 + row];
       st[j] = *(const bf16x8*)(kg + pos * DD + 8 * col);
       st[4 + j] = *(const bf16x8*)(vg + pos * DD + 8 * col);
     }
@@ -461,15 +466,7 @@ __global__ __launch_bounds__(256) void dsa_attend_kernel(DsaArgs a, int nsplit) 
 #pragma unroll
   for (int ct = 0; ct < DD / 16; ++ct) o[ct] = f32x4{};
   float m = -INFINITY, l = 0.f;
-  bf16x8 st[8];
-  load_tile(k0, st);
-  store_tile((char HCA_LDS*)kv_s[0], st);
-  __syncthreads();
-  int buf = 0;
-  for (int t0 = k0; t0 < k1; t0 += TK, buf ^= 1) {
-    const bool more = t0 + TK < k1;
-    if (more) load_tile(t0 + TK, st);  // in flight during this tile's math
-    const char HCA_LDS* kb = (const char HCA_LDS*)kv_s[buf];
+  auto tile_math = [&](const char HCA_LDS* kb, int t0) {
     const char HCA_LDS* vb = kb + TK * RS;
     f32x4 s0 = {}, s1 = {};
 #pragma unroll
@@ -505,8 +502,29 @@ __global__ __launch_bounds__(256) void dsa_attend_kernel(DsaArgs a, int nsplit) 
     const char HCA_LDS* vt = vb + (4 * g + (r >> 2)) * RS + 8 * (lane & 3);
 #pragma unroll
     for (int ct = 0; ct < DD / 16; ++ct) o[ct] = mfma16(lds_tr(vt + 32 * ct), pb, o[ct]);
-    __syncthreads();  // every wave is done with the other buffer
-    if (more) store_tile((char HCA_LDS*)kv_s[buf ^ 1], st);
+  };
+  // two tiles in flight: tile t0 + TK arrives in one register set while tile
+  // t0 + 2 TK is issued into the other; buffers alternate with the tile
+  char HCA_LDS* buf0 = (char HCA_LDS*)kv_s[0];
+  char HCA_LDS* buf1 = (char HCA_LDS*)kv_s[1];
+  bf16x8 st0[8], st1[8];
+  __syncthreads();  // row_s
+  load_tile(k0, st0);
+  if (k0 + TK < k1) load_tile(k0 + TK, st1);
+  store_tile(buf0, st0);
+  __syncthreads();
+  for (int t0 = k0; t0 < k1; t0 += 2 * TK) {
+    if (t0 + 2 * TK < k1) load_tile(t0 + 2 * TK, st0);
+    tile_math(buf0, t0);
+    if (t0 + TK >= k1) break;  // uniform
+    __syncthreads();  // every wave is done with buf1's previous tile
+    store_tile(buf1, st1);
+    __syncthreads();
+    if (t0 + 3 * TK < k1) load_tile(t0 + 3 * TK, st1);
+    tile_math(buf1, t0 + TK);
+    if (t0 + 2 * TK >= k1) break;
+    __syncthreads();
+    store_tile(buf0, st0);
     __syncthreads();
   }
   // partial of this split: m (log2 units), l, O / l
@@ -529,40 +547,46 @@ __global__ __launch_bounds__(256) void dsa_attend_kernel(DsaArgs a, int nsplit) 
 }
 
 // Merge of the splits of sequence b in order: O = sum_s 2^(m_s - M) l_s O_s /
-// sum_s 2^(m_s - M) l_s.  256 threads: thread t takes head t / 4 and
-// columns 64 (t % 4) .. +63.
+// sum_s 2^(m_s - M) l_s.  Workgroup (8 heads, sequence), thread = (head, 8
+// columns); the splits' partials are loaded together, eight at a time, and
+// combined in split order.
 __global__ __launch_bounds__(256) void dsa_merge_kernel(DsaArgs a, int nsplit) {
-  const int b = blockIdx.x;
+  const int b = blockIdx.y;
   const int nsel = min(a.seqlens[b], a.topk);
   const int ns = (nsel + SPLIT - 1) / SPLIT;
-  const int head = threadIdx.x >> 2, c0 = 64 * (threadIdx.x & 3);
+  const int head = 8 * blockIdx.x + (threadIdx.x >> 5), c0 = 8 * (threadIdx.x & 31);
+  const size_t prow0 = (size_t)b * nsplit * HQ + head;  // split s: prow0 + s HQ
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_m[((size_t)b * nsplit + s) * HQ + head]);
-  float acc[64];
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_m[prow0 + (size_t)s * HQ]);
+  float acc[8];
 #pragma unroll
-  for (int i = 0; i < 64; ++i) acc[i] = 0.f;
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
   float den = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const size_t prow = ((size_t)b * nsplit + s) * HQ + head;
-    const float wgt = __builtin_amdgcn_exp2f(a.part_m[prow] - M) * a.part_l[prow];
-    den += wgt;
-    const bf16* po = a.part_o + prow * DD + c0;
+  for (int s0 = 0; s0 < ns; s0 += 8) {
+    bf16x8 v[8];
+    float wgt[8];
 #pragma unroll
-    for (int i = 0; i < 64; i += 8) {
-      const bf16x8 v = *(const bf16x8*)(po + i);
+    for (int j = 0; j < 8; ++j) {
+      if (s0 + j < ns) {
+        const size_t prow = prow0 + (size_t)(s0 + j) * HQ;
+        v[j] = *(const bf16x8*)(a.part_o + prow * DD + c0);
+        wgt[j] = __builtin_amdgcn_exp2f(a.part_m[prow] - M) * a.part_l[prow];
+      }
+    }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[i + e] = __builtin_fmaf(wgt, (float)v[e], acc[i + e]);
+    for (int j = 0; j < 8; ++j) {
+      if (s0 + j < ns) {
+        den += wgt[j];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(wgt[j], (float)v[j][e], acc[e]);
+      }
     }
   }
   const float inv = 1.f / den;
-  bf16* out = (bf16*)a.o + ((size_t)b * HQ + head) * DD + c0;
+  bf16x8 o;
 #pragma unroll
-  for (int i = 0; i < 64; i += 8) {
-    bf16x8 v;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = (bf16)(acc[i + e] * inv);
-    *(bf16x8*)(out + i) = v;
-  }
+  for (int e = 0; e < 8; ++e) o[e] = (bf16)(acc[e] * inv);
+  *(bf16x8*)((bf16*)a.o + ((size_t)b * HQ + head) * DD + c0) = o;
 }
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -611,7 +635,7 @@ hipError_t launch_dsa_decode(DsaArgs a, hipStream_t s) {
   dsa_count_kernel<<<chunks, 256, 0, s>>>(a, ks, nchunk);
   dsa_emit_kernel<<<dim3(std::max(nchunk, (a.topk + CH - 1) / CH), a.batch), 256, 0, s>>>(a, ks, nchunk);
   dsa_attend_kernel<<<dim3(nsplit, a.batch), 256, 0, s>>>(a, nsplit);
-  dsa_merge_kernel<<<a.batch, 256, 0, s>>>(a, nsplit);
+  dsa_merge_kernel<<<dim3(HQ / 8, a.batch), 256, 0, s>>>(a, nsplit);
   return hipGetLastError();
 }
 

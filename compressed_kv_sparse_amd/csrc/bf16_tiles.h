@@ -118,7 +118,11 @@ __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)
 // later).  Buffer loads rather than global ones: with a global->LDS load in
 // flight the compiler waits for every outstanding LDS read before each use
 // of one, which would serialise the fragment reads of the tile math.
-template <int NW, bool DO_K = true, bool DO_V = true>
+// CPOL is the loads' cache policy: 0, or kStreamed for rows that no other
+// workgroup reads again (the non-temporal hint keeps them from displacing
+// reused lines in L2).
+constexpr int kStreamed = 2;  // cache-policy bit of a non-temporal load
+template <int NW, bool DO_K = true, bool DO_V = true, int CPOL = 0>
 __device__ __forceinline__ void issue_tile(const KeySource& ks, int tile, char HCA_LDS* kbuf,
                                            char HCA_LDS* vbuf, int wave, int lane) {
   constexpr int RPW = NT / NW;
@@ -141,9 +145,9 @@ __device__ __forceinline__ void issue_tile(const KeySource& ks, int tile, char H
       // the row offset goes into the lane offset: the range check covers it
       const int off = (row0 + r) * rs + vo;
       if (DO_K)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (void HCA_LDS*)(kbuf + (kk0 + r) * KSTR), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (void HCA_LDS*)(kbuf + (kk0 + r) * KSTR), 16, off, 0, 0, CPOL);
       if (DO_V)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (void HCA_LDS*)(vbuf + (kk0 + r) * VSTR), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (void HCA_LDS*)(vbuf + (kk0 + r) * VSTR), 16, off, 0, 0, CPOL);
     }
     return;
   }
@@ -156,10 +160,10 @@ __device__ __forceinline__ void issue_tile(const KeySource& ks, int tile, char H
     const int off = row * rs + vo;
     if (DO_K)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(comp ? ks.comp_k : ks.raw_k, (void HCA_LDS*)(kbuf + kk * KSTR), 16,
-                                               off, 0, 0, 0);
+                                               off, 0, 0, CPOL);
     if (DO_V)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(comp ? ks.comp_v : ks.raw_v, (void HCA_LDS*)(vbuf + kk * VSTR), 16,
-                                               off, 0, 0, 0);
+                                               off, 0, 0, CPOL);
   }
 }
 

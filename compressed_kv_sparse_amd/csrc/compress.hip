@@ -85,7 +85,8 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a, int cw) {
     const size_t tok0 = (size_t)a.cu_seqlens[seq] + (size_t)kBlock * j;
     const T* x = (const T*)a.x[which] + tok0 * rstride + col;
 #pragma unroll
-    for (int ps = 0; ps < PASSES; ++ps) xv[ps] = *(const vec_t*)(x + (size_t)(ps * RPP + r0) * rstride);
+    for (int ps = 0; ps < PASSES; ++ps)  // rows pooled once: non-temporal
+      xv[ps] = __builtin_nontemporal_load((const vec_t*)(x + (size_t)(ps * RPP + r0) * rstride));
   }
   __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of their uses
 

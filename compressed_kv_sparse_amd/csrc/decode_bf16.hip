@@ -144,11 +144,11 @@ __device__ __forceinline__ bool tile_pass16(const KeySource& ks, int t_begin, in
   const int koff = (lane & 15) * KSTR + g * 16;
   const int voff = NT * KSTR + (4 * g + ((lane & 15) >> 2)) * VSTR + 4 * (lane & 3) * 2;
   if (MODE == kLazy && threadIdx.x == 0) flag[0] = flag[1] = 0;
-  issue_tile<4>(ks, t_begin, kv0, kv0 + NT * KSTR, wave, lane);
+  issue_tile<4, true, true, kStreamed>(ks, t_begin, kv0, kv0 + NT * KSTR, wave, lane);
   wait_vm_all();
   __syncthreads();
   for (int tile = t_begin; tile < t_end; tile += 2) {  // two buffers, unrolled (see tile_pass)
-    if (tile + 1 < t_end) issue_tile<4>(ks, tile + 1, kv1, kv1 + NT * KSTR, wave, lane);
+    if (tile + 1 < t_end) issue_tile<4, true, true, kStreamed>(ks, tile + 1, kv1, kv1 + NT * KSTR, wave, lane);
     bool over = compute_tile16<MODE>(kv0, kv0, qf, st, sc2, lane, koff, voff, rm, tile,
                                      tile_needs_mask(tile, rm.nc, rm.nkeys), two_term);
     if (MODE == kLazy && over && lane == 0) flag[0] = 1;
@@ -156,7 +156,7 @@ __device__ __forceinline__ bool tile_pass16(const KeySource& ks, int t_begin, in
     __syncthreads();
     if (MODE == kLazy && flag[0]) return true;
     if (tile + 1 >= t_end) break;
-    if (tile + 2 < t_end) issue_tile<4>(ks, tile + 2, kv0, kv0 + NT * KSTR, wave, lane);
+    if (tile + 2 < t_end) issue_tile<4, true, true, kStreamed>(ks, tile + 2, kv0, kv0 + NT * KSTR, wave, lane);
     over = compute_tile16<MODE>(kv1, kv1, qf, st, sc2, lane, koff, voff, rm, tile + 1,
                                 tile_needs_mask(tile + 1, rm.nc, rm.nkeys), two_term);
     if (MODE == kLazy && over && lane == 0) flag[1] = 1;

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void dsa_score_kernel(DsaArgs a) {
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       const int p = min(pb + 32 * x, p1 - 1);  // past the end: the last row again (not stored)
-      kv[x] = *(const i32x4*)(a.ki + (r0 + p) * DI + 16 * part);
+      kv[x] = __builtin_nontemporal_load((const i32x4*)(a.ki + (r0 + p) * DI + 16 * part));  // read once
     }
 #pragma unroll
     for (int x = 0; x < 4; ++x) {

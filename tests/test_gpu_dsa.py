@@ -79,3 +79,37 @@ def test_dsa_decode_rows_with_gaps():
     for b in range(len(lens)):
         assert np.array_equal(sel.cpu().numpy()[b, :min(lens[b], topk)], rsel[b])
     assert_close(o, torch.tensor(ref), torch.bfloat16, "dsa rows with gaps")
+
+
+def test_dsa_decode_bench_workload():
+    """The benchmarked workload at full size, in the launch configuration
+    bench.py times (64 sequences of 131072 positions, k = 2048, workspace,
+    o and sel passed in): every sequence's selection bit for bit, and the
+    output of 8 seeded-random sequences against the oracle, one sequence at
+    a time."""
+    import bench
+
+    B, L, K = bench.DSA_BATCH, bench.DSA_LEN, bench.DSA_TOPK
+    print(f"case bench workload B={B} L={L} k={K}", flush=True)
+    inp = dsa_inputs([L] * B, bench.DSA_SEED, DEV)
+    ws = torch.empty(hca.hca_dsa_decode_workspace_bytes(B, L, K), dtype=torch.uint8, device=DEV)
+    o = torch.empty_like(inp["q"])
+    sel = torch.empty((B, K), dtype=torch.int32, device=DEV)
+    for _ in range(2):  # a second call on the same workspace gives the same result
+        hca.hca_dsa_decode(inp["seqlens"], inp["cu_rows"], L, K, inp["q"], inp["qi"], inp["k"], inp["v"], inp["ki"],
+                           workspace=ws, o=o, sel=sel)
+        torch.cuda.synchronize()
+        got = sel.cpu().numpy()
+        ki = inp["ki"].cpu()
+        qi = inp["qi"].cpu()
+        for b in range(B):
+            r0 = inp["cu_rows_host"][b]
+            ref = oracle.select_topk(oracle.index_scores(qi[b], ki[r0:r0 + L]), K)
+            assert np.array_equal(got[b], ref), f"selection of sequence {b}"
+    rng = np.random.default_rng(17)
+    for b in sorted(rng.choice(B, size=8, replace=False).tolist()):
+        r0 = inp["cu_rows_host"][b]
+        rows = slice(r0, r0 + L)
+        ref, _ = oracle.dsa_decode(inp["q"][b:b + 1].cpu(), inp["qi"][b:b + 1].cpu(), inp["k"][rows].cpu(),
+                                   inp["v"][rows].cpu(), inp["ki"][rows].cpu(), [L], [0], K)
+        assert_close(o[b:b + 1], torch.tensor(ref), torch.bfloat16, f"dsa bench workload sequence {b}")

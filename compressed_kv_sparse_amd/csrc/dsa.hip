@@ -13,11 +13,12 @@
 //   shared key/value rows of the selected positions.
 //
 // Kernels, in launch order:
-//   dsa_zero_kernel    clears the per-sequence histogram of the score keys
+//   dsa_zero_kernel    clears the per-sequence histograms of the score keys
 //   dsa_score_kernel   (chunk of 4096 positions, sequence): integer scores
 //                      with v_dot4 (sdot4), 8 lanes per indexer row so that
-//                      the loads are contiguous, stored as keys u = score + 2^21
-//                      in [0, 2^22]; adds its histogram of u >> 11 to the
+//                      the loads are contiguous (and non-temporal: each row
+//                      is read once), stored as keys u = score + 2^21 in
+//                      [0, 2^22]; adds its histogram of u >> 11 to the
 //                      sequence's (global atomics on the non-empty bins)
 //   dsa_lohist_kernel, dsa_count_kernel, dsa_emit_kernel  (chunk,
 //                      sequence): the exact threshold key by a two-level
@@ -25,9 +26,10 @@
 //                      from a histogram of the keys in that bin), each
 //                      chunk's counts, then the selected positions in order
 //   dsa_attend_kernel  (split of 256 selected keys, sequence): 4 waves x 16
-//                      heads on v_mfma_f32_16x16x32_bf16, gathered K and V
-//                      rows double buffered in LDS, online softmax; writes
-//                      m, l and O / l per split
+//                      heads on v_mfma_f32_16x16x32_bf16; the split's cache
+//                      rows staged in LDS, two tiles of gathered K and V rows
+//                      in flight in registers while one is computed from LDS,
+//                      online softmax; writes m, l and O / l per split
 //   dsa_merge_kernel   (8 heads, sequence): combines the splits in order.
 #include <algorithm>
 

@@ -694,6 +694,19 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, int pair0, in
 // kinds share one launch (and one LDS layout); the branch is uniform per
 // workgroup, and the two bodies are separate inlined copies so neither
 // carries the other's register state.
+//
+// Workgroup x runs on XCD x mod 8, and neighbouring pairs read mostly the
+// same raw window rows.  In every run of 8 G pipelined workgroups, the G
+// workgroups of one XCD take G consecutive pairs, so each XCD's L2 fetches
+// the window rows of its own pairs instead of every row of the sequence
+// (a permutation of the pairs; a tail shorter than 8 G keeps its order).
+constexpr int kXcdGroup = 32;  // pairs per XCD per run: one per CU of an XCD
+__device__ __forceinline__ int xcd_local_pair(int u, int n) {
+  const int full = n / (8 * kXcdGroup) * (8 * kXcdGroup);
+  if (u >= full) return u;
+  const int r = u & 7, s = u >> 3;
+  return (s / kXcdGroup) * 8 * kXcdGroup + r * kXcdGroup + s % kXcdGroup;
+}
 template <bool EPI>
 __global__ __launch_bounds__(256, 1) void prefill_bf16_kernel(PrefillArgs a, int lo_n, int hi_begin) {
   __shared__ __attribute__((aligned(16))) char k0_s[KTILE];
@@ -710,7 +723,7 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_kernel(PrefillArgs a, int
   if ((int)blockIdx.x < lo_n)
     prefill_body<true, EPI>(a, 0, blockIdx.x, HCA_LDS_ARGS);
   else
-    prefill_body<false, EPI>(a, hi_begin, blockIdx.x - lo_n, HCA_LDS_ARGS);
+    prefill_body<false, EPI>(a, hi_begin, xcd_local_pair(blockIdx.x - lo_n, gridDim.x - lo_n), HCA_LDS_ARGS);
 #undef HCA_LDS_ARGS
 }
 

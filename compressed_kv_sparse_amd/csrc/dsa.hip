@@ -627,7 +627,7 @@ hipError_t launch_dsa_decode(DsaArgs a, hipStream_t s) {
   a.part_l = (float*)w;
   w += align256((size_t)a.batch * nsplit * HQ * sizeof(float));
   a.part_o = (bf16*)w;
-  // the two histograms are contiguous (HBINS + LBINS words per sequence, each part 256-byte aligned)
+  // hist [B, HBINS] and lohist [B, LBINS] are adjacent (256-byte alignment padding between): one clear
   const int nh = (int)(((char*)a.chunk_cnt - (char*)a.hist) / sizeof(unsigned));
   dsa_zero_kernel<<<(nh + 255) / 256, 256, 0, s>>>(a.hist, nh);
   const dim3 chunks(nchunk, a.batch);

@@ -409,10 +409,23 @@ __global__ __launch_bounds__(256) void bwd_pool_kernel(BackwardArgs a, BackwardP
     const size_t item0 = unit + (size_t)pl.raw_tiles * pl.nsr + (size_t)ctile * pl.nsc;
     for (int c = threadIdx.x; c < D; c += 256) {
       float sk = 0.f, sv = 0.f;
-      for (int sp = 0; sp < ns; ++sp) {
-        const size_t o = ((item0 + sp) * KT + key) * D + c;
-        sk += a.part_k[o];
-        sv += a.part_v[o];
+      for (int sp0 = 0; sp0 < ns; sp0 += 8) {  // eight runs' loads in flight, added in run order
+        float bk[8], bv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (sp0 + u < ns) {
+            const size_t o = ((item0 + sp0 + u) * KT + key) * D + c;
+            bk[u] = a.part_k[o];
+            bv[u] = a.part_v[o];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (sp0 + u < ns) {
+            sk += bk[u];
+            sv += bv[u];
+          }
+        }
       }
       dkc_s[c] = sk;
       dvc_s[c] = sv;
@@ -467,7 +480,15 @@ __global__ __launch_bounds__(128) void bwd_dw_kernel(BackwardArgs a) {
   __shared__ float red[2][2];
   const int kvh = blockIdx.x, i = threadIdx.x, lane = i & 63, wave = i >> 6;
   float gs = 0.f;
-  for (int e = 0; e < a.total_blocks; ++e) gs += a.gbuf[((size_t)e * a.hkv + kvh) * kBlock + i];
+  for (int e0 = 0; e0 < a.total_blocks; e0 += 16) {  // sixteen loads in flight, added in block order
+    float g[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (e0 + u < a.total_blocks) g[u] = a.gbuf[((size_t)(e0 + u) * a.hkv + kvh) * kBlock + i];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (e0 + u < a.total_blocks) gs += g[u];
+  }
   const float wi = a.w[kvh * kBlock + i];
   float mx = wi;
   for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));

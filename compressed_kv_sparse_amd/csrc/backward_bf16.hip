@@ -432,44 +432,70 @@ __global__ __launch_bounds__(256) void bwd_pool_kernel(BackwardArgs a, BackwardP
     }
   }
   __syncthreads();
-  // rows: wave w takes rows w, w+4, ...; lane l columns 8l .. 8l+7
+  // rows: wave w takes rows w, w+4, ..., two per step (i and i + 4: the
+  // loads of both are issued before either is used); lane l columns 8l ..
+  // 8l+7.  The plan always has two runs per raw tile (nsr = 2).
   const int rows = min(kBlock, len - j * kBlock);
-  for (int i = wave; i < rows; i += 4) {
-    const int rpos = j * kBlock + i;  // position in the sequence
-    const int rtile = rpos / KT;
-    const int t_last = min(len, rtile * KT + KT - 1 + a.window);
-    const size_t item0 = unit + (size_t)rtile * pl.nsr;
-    float dk8[8] = {}, dv8[8] = {};
-    for (int sp = 0; sp < pl.nsr && rtile * KT + sp * pl.prr < t_last; ++sp) {
-      const size_t o = ((item0 + sp) * KT + rpos % KT) * D + 8 * lane;
-      const f32x4 k0 = *(const f32x4*)(a.part_k + o), k1 = *(const f32x4*)(a.part_k + o + 4);
-      const f32x4 v0 = *(const f32x4*)(a.part_v + o), v1 = *(const f32x4*)(a.part_v + o + 4);
+  for (int ib = wave; ib < rows; ib += 8) {
+    f32x4 pk[2][2][2], pv[2][2][2];  // [row][run][half]
+    bool use[2][2];
+    bf16x8 kx[2], vx[2];
+    size_t rowg[2];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        dk8[e] += k0[e];
-        dk8[4 + e] += k1[e];
-        dv8[e] += v0[e];
-        dv8[4 + e] += v1[e];
+    for (int h = 0; h < 2; ++h) {
+      const int i = ib + 4 * h < rows ? ib + 4 * h : ib;  // past the end: load row ib again (not stored)
+      const int rpos = j * kBlock + i;  // position in the sequence
+      const int rtile = rpos / KT;
+      const int t_last = min(len, rtile * KT + KT - 1 + a.window);
+      const size_t item0 = unit + (size_t)rtile * pl.nsr;
+#pragma unroll
+      for (int sp = 0; sp < 2; ++sp) {
+        use[h][sp] = rtile * KT + sp * pl.prr < t_last;
+        if (use[h][sp]) {
+          const size_t o = ((item0 + sp) * KT + rpos % KT) * D + 8 * lane;
+          pk[h][sp][0] = *(const f32x4*)(a.part_k + o);
+          pk[h][sp][1] = *(const f32x4*)(a.part_k + o + 4);
+          pv[h][sp][0] = *(const f32x4*)(a.part_v + o);
+          pv[h][sp][1] = *(const f32x4*)(a.part_v + o + 4);
+        }
       }
+      rowg[h] = ((size_t)start + rpos) * a.hkv + kvh;
+      kx[h] = *(const bf16x8*)((const bf16*)a.k + rowg[h] * D + 8 * lane);
+      vx[h] = *(const bf16x8*)((const bf16*)a.v + rowg[h] * D + 8 * lane);
     }
-    const size_t row = ((size_t)start + rpos) * a.hkv + kvh;
-    bf16x8 ok, ov;
-    float gi = 0.f;
-    const float pi = full ? p_s[i] : 0.f;
-    const bf16x8 kx = *(const bf16x8*)((const bf16*)a.k + row * D + 8 * lane);
-    const bf16x8 vx = *(const bf16x8*)((const bf16*)a.v + row * D + 8 * lane);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float ck = full ? dkc_s[8 * lane + e] : 0.f, cv = full ? dvc_s[8 * lane + e] : 0.f;
-      ok[e] = (bf16)(dk8[e] + pi * ck);
-      ov[e] = (bf16)(dv8[e] + pi * cv);
-      gi = __builtin_fmaf(ck, (float)kx[e], __builtin_fmaf(cv, (float)vx[e], gi));
-    }
-    *(bf16x8*)((bf16*)a.dk + row * D + 8 * lane) = ok;
-    *(bf16x8*)((bf16*)a.dv + row * D + 8 * lane) = ov;
-    if (full) {
-      for (int o = 32; o > 0; o >>= 1) gi += __shfl_xor(gi, o);
-      if (lane == 0) a.gbuf[(((size_t)a.cu_blocks[b] + j) * a.hkv + kvh) * kBlock + i] = gi;
+    for (int h = 0; h < 2; ++h) {
+      const int i = ib + 4 * h;
+      if (i >= rows) break;  // uniform per wave
+      float dk8[8] = {}, dv8[8] = {};
+#pragma unroll
+      for (int sp = 0; sp < 2; ++sp) {  // runs in order, as in the single-row form
+        if (use[h][sp]) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            dk8[e] += pk[h][sp][0][e];
+            dk8[4 + e] += pk[h][sp][1][e];
+            dv8[e] += pv[h][sp][0][e];
+            dv8[4 + e] += pv[h][sp][1][e];
+          }
+        }
+      }
+      bf16x8 ok, ov;
+      float gi = 0.f;
+      const float pi = full ? p_s[i] : 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float ck = full ? dkc_s[8 * lane + e] : 0.f, cv = full ? dvc_s[8 * lane + e] : 0.f;
+        ok[e] = (bf16)(dk8[e] + pi * ck);
+        ov[e] = (bf16)(dv8[e] + pi * cv);
+        gi = __builtin_fmaf(ck, (float)kx[h][e], __builtin_fmaf(cv, (float)vx[h][e], gi));
+      }
+      *(bf16x8*)((bf16*)a.dk + rowg[h] * D + 8 * lane) = ok;
+      *(bf16x8*)((bf16*)a.dv + rowg[h] * D + 8 * lane) = ov;
+      if (full) {
+        for (int o = 32; o > 0; o >>= 1) gi += __shfl_xor(gi, o);
+        if (lane == 0) a.gbuf[(((size_t)a.cu_blocks[b] + j) * a.hkv + kvh) * kBlock + i] = gi;
+      }
     }
   }
 }

@@ -6,17 +6,21 @@ One step = one pass of the whole path over one batch of the workload:
   decode workload:   hca_attend_decode;
   mixed_1m:          pooling + prefill of the 32768-token chunk, then decode
                      of the 8 long-context sequences.
-The default workload is prefill_8k (B=1, T=8192, Hq=64, Hkv=1, d=512,
-W=128); `value` is its prefill throughput in tokens/s.  The same run also
-times decode_64x128k (64 queries against 128K-token caches) and reports it
-under "decode" (queries/s, HBM fraction).  Inputs are seeded synthetic
-tensors resident in HBM before the timed region.
+The default workload is prefill_128k (B=1, T=131072, Hq=64, Hkv=1, d=512,
+W=128, 1024 compressed entries): the largest prefill and the one bound by
+the matrix cores; `value` is its prefill throughput in tokens/s.  The same
+run also times decode_64x128k (64 queries against 128K-token caches, under
+"decode") and mixed_1m (8 decode queries at 256K-1M plus a 32768-token
+chunk as one step, under "mixed"), and the measurement probes (a streaming
+read and a matrix-core loop, under "measured_peaks").  Inputs are seeded
+synthetic tensors resident in HBM before the timed region.
 
 Per-kernel durations come from HIP events recorded on the stream the kernels
-run on, around every launch of the timed steps.  The roofline entries use
-algorithmic work: bytes (flops) the method must move (compute), not what the
-implementation adds.  `traffic` is filled from the counter summary in
-profiles/ when it was measured on the current kernel source, else null.
+run on, around every launch of the timed steps (mean, median and min are
+reported).  The roofline entries use algorithmic work: bytes (flops) the
+method must move (compute), not what the implementation adds.  `traffic` is
+filled from the counter summary in profiles/ when it was measured on the
+current kernel source, else null.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -161,9 +165,21 @@ class KernelClock:
         self.pairs.setdefault(name, []).append((a, b))
         return out
 
+    def times_ms(self, name):
+        return [a.elapsed_time(b) for a, b in self.pairs.get(name, [])]
+
     def mean_ms(self, name):
-        ps = self.pairs.get(name, [])
-        return sum(a.elapsed_time(b) for a, b in ps) / max(1, len(ps))
+        ts = self.times_ms(name)
+        return sum(ts) / max(1, len(ts))
+
+    def stats_ms(self, name):
+        """(mean, median, min) over the recorded launches."""
+        ts = sorted(self.times_ms(name))
+        if not ts:
+            return 0.0, 0.0, 0.0
+        n = len(ts)
+        med = ts[n // 2] if n % 2 else 0.5 * (ts[n // 2 - 1] + ts[n // 2])
+        return sum(ts) / n, med, ts[0]
 
     def reset(self):
         self.pairs = {}
@@ -197,16 +213,29 @@ def measured_traffic(kernel, workload):
         return None
 
 
-def roofline(kernel, workload, byt, flops, ms, bound):
+MEASURED = {}  # ceilings the probes reached in this run: "hbm" (GB/s), "mfma" (TFLOP/s)
+
+
+def roofline(kernel, workload, byt, flops, ms, bound, clock=None, name=None):
+    """Roofline entry of one kernel: achieved = algorithmic work per launch /
+    mean launch time (HIP events).  With the clock and the recorded name the
+    median and min per launch are added; `frac_of_measured` reads the same
+    achieved rate against the probe's ceiling of this run."""
     if bound == "hbm":
         ach = byt / (ms * 1e-3) / 1e9
         peak, unit = PEAK_HBM_GBS, "GB/s"
     else:
         ach = flops / (ms * 1e-3) / 1e12
         peak, unit = PEAK_BF16_TFLOPS, "TFLOP/s"
-    return {"kernel": kernel, "bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
-            "frac": round(ach / peak, 4), "traffic": measured_traffic(kernel, workload),
-            "algorithmic_bytes": int(byt), "algorithmic_flops": int(flops), "avg_ms": round(ms, 5)}
+    out = {"kernel": kernel, "bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
+           "frac": round(ach / peak, 4), "traffic": measured_traffic(kernel, workload),
+           "algorithmic_bytes": int(byt), "algorithmic_flops": int(flops), "avg_ms": round(ms, 5)}
+    if clock is not None and name is not None:
+        _, med, mn = clock.stats_ms(name)
+        out["median_ms"], out["min_ms"] = round(med, 5), round(mn, 5)
+    if MEASURED.get(bound):
+        out["frac_of_measured"] = round(ach / MEASURED[bound], 4)
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -222,7 +251,24 @@ def blas_threads():
         return 1
 
 
-def cpu_baseline_prefill(c, inp, seconds):
+def oracle_sample_rows(T, window, n_blocks=16):
+    """The query rows every prefill sample of the oracle includes: the
+    key-set boundaries t in {0, W-1, W, 126, 127, 128, 255, 256, T-1}, and
+    for n_blocks blocks spread over the sequence the rows 128j+126, 128j+127
+    and 128j+128 (the last row before a block completes, the row that
+    completes it, the first row of the next block)."""
+    fixed = {0, window - 1, window, 126, 127, 128, 255, 256, T - 1}
+    nb = T // 128
+    for j in range(0, nb, max(1, nb // n_blocks)):
+        fixed |= {128 * j + 126, 128 * j + 127, 128 * j + 128}
+    return sorted(x for x in fixed if 0 <= x < T)
+
+
+def cpu_baseline_prefill(c, inp, seconds, min_rows=0):
+    """The oracle on the boundary rows plus seeded random query rows (at
+    least min_rows in all, then as many as fit in `seconds`), and the pooling
+    of every block; the attention time per row is extrapolated to all T
+    rows (a uniform random sample gives an unbiased mean per row)."""
     import numpy as np
     import torch
 
@@ -230,27 +276,34 @@ def cpu_baseline_prefill(c, inp, seconds):
 
     T = inp["lens"][0]
     cu = inp["cu_seqlens_host"]
-    k, v, w = inp["k"].cpu(), inp["v"].cpu(), inp["w"].cpu()
+    # the raw rows decoded (exactly) to float64 once, as the oracle would
+    # decode them on every call
+    k, v, w = inp["k"].cpu().double().numpy(), inp["v"].cpu().double().numpy(), inp["w"].cpu()
     t0 = time.perf_counter()
     kc = oracle.compress(k, w, cu)
     vc = oracle.compress(v, w, cu)
     t_pool = time.perf_counter() - t0
-    order = np.random.default_rng(5).permutation(T)
+    fixed = oracle_sample_rows(T, c.window)
+    fixed_set = set(fixed)
+    rand = [int(x) for x in np.random.default_rng(5).permutation(T) if int(x) not in fixed_set]
+    order = fixed + rand
     done = 0
     t_att = 0.0
     step = 16
-    while t_att < seconds and done < T:
-        rows = sorted(int(x) for x in order[done:done + step])
+    while done < T and (done < min_rows or t_att < seconds):
+        rows = sorted(order[done:done + step])
         q_rows = inp["q"].index_select(0, torch.tensor(rows, device=inp["q"].device)).cpu()
         t1 = time.perf_counter()
         oracle.attend_prefill(q_rows, k, v, kc, vc, cu, c.window, rows=rows, q_holds_rows_only=True)
         t_att += time.perf_counter() - t1
         done += len(rows)
     per_tok = t_att / done + t_pool / T
+    how = "all" if done >= T else "extrapolated from"
     return {"value": round(1.0 / per_tok, 3), "unit": "tokens/s", "cores": blas_threads(),
             "kind": "oracle",
-            "sample": f"{done} of {T} query rows (seeded random) attended in {t_att:.1f} s plus "
-                      f"pooling of all {len(kc)} blocks in {t_pool:.1f} s, prorated per token"}
+            "sample": f"{done} of {T} query rows ({len(fixed)} block-boundary and window-edge rows, the rest "
+                      f"seeded random) attended in {t_att:.1f} s, plus pooling of all {len(kc)} blocks in "
+                      f"{t_pool:.1f} s; tokens/s {how} the sampled rows"}
 
 
 def cpu_baseline_decode(c, inp, seconds):
@@ -293,7 +346,15 @@ def warm_up(torch, step, warmup, min_s):
 # ---------------------------------------------------------------------------
 # workloads
 # ---------------------------------------------------------------------------
-def run_prefill(torch, hca, c, steps, warmup, clock, min_warm_s, lens=None):
+COLD_BYTES = 512 << 20  # overwritten between cold calls: twice the 256 MiB last-level cache
+
+
+def run_prefill(torch, hca, c, steps, warmup, clock, min_warm_s, lens=None, extras=True):
+    """The prefill step (pooling, then attention) timed `steps` times.  Then,
+    apart from the step: the pooling alone with a 512 MiB scratch buffer
+    overwritten before each call (so the last-level cache cannot serve its
+    rows; recorded as compress_cold), and with `extras` the fused epilogue,
+    the lse forward and the backward."""
     from hca_workloads import prefill_inputs
 
     inp = prefill_inputs(c, "cuda", lens=lens)
@@ -303,10 +364,12 @@ def run_prefill(torch, hca, c, steps, warmup, clock, min_warm_s, lens=None):
     vc = torch.empty_like(kc)
     o = torch.empty_like(inp["q"])
 
+    def compress():
+        return hca.hca_compress(p, inp["cu_seqlens"], inp["cu_blocks"], inp["total_blocks"], inp["k"], inp["w"],
+                                v=inp["v"], kc=kc, vc=vc)
+
     def step():
-        clock.run("compress", lambda: hca.hca_compress(p, inp["cu_seqlens"], inp["cu_blocks"],
-                                                       inp["total_blocks"], inp["k"], inp["w"],
-                                                       v=inp["v"], kc=kc, vc=vc))
+        clock.run("compress", compress)
         clock.run("prefill", lambda: hca.hca_attend_prefill(p, inp["cu_seqlens"], inp["cu_blocks"],
                                                             inp["max_seqlen"], inp["q"], inp["k"],
                                                             inp["v"], kc, vc, o=o))
@@ -318,7 +381,13 @@ def run_prefill(torch, hca, c, steps, warmup, clock, min_warm_s, lens=None):
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    if c.dtype == "bf16":
+    scratch = torch.empty(COLD_BYTES // 4, dtype=torch.int32, device="cuda")
+    for i in range(steps):
+        scratch.fill_(i)
+        clock.run("compress_cold", compress)
+    torch.cuda.synchronize()
+    del scratch
+    if c.dtype == "bf16" and extras:
         # the same attention with the fused epilogue (gate + rank-16 head
         # mixing), timed apart: its cost over the plain launch
         g = torch.Generator(device="cuda").manual_seed(c.seed + 29)
@@ -487,12 +556,19 @@ def cpu_baseline_dsa(inp, seconds):
             "sample": f"{done} of {len(inp['lens'])} sequences (131072 positions, k = 2048) in {el:.1f} s"}
 
 
-def run_decode(torch, hca, c, steps, warmup, clock, min_warm_s, n_sets=4):
+def run_decode(torch, hca, c, steps, warmup, clock, min_warm_s, n_sets=4, epilogue=True):
     """Rotates n_sets independent caches so repeats do not hit in the 256 MiB
-    last-level cache."""
+    last-level cache (n_sets x the cache bytes must exceed 512 MiB).  With
+    `epilogue` the same decode with the fused epilogue is timed apart."""
     from hca_workloads import decode_inputs
 
-    sets = [decode_inputs(c, "cuda", seed=c.seed + 17 * i) for i in range(n_sets)]
+    # every set has the workload's context lengths (drawn once, from the
+    # workload's seed) and its own cache contents; enough sets that together
+    # they exceed 512 MiB
+    first = decode_inputs(c, "cuda", seed=c.seed)
+    lens = first["lens"]
+    n_sets = max(n_sets, -(-COLD_BYTES // decode_work(c, lens, 2)[0]) + 1)
+    sets = [first] + [decode_inputs(c, "cuda", lens=lens, seed=c.seed + 17 * i) for i in range(1, n_sets)]
     p = hca.make_params(c.hq, c.hkv, c.d, c.window, torch.bfloat16)
     ws = [hca.new_decode_workspace(p, len(s["lens"]), s["max_blocks"]) for s in sets]
     outs = [torch.empty_like(s["q"]) for s in sets]
@@ -530,6 +606,8 @@ def run_decode(torch, hca, c, steps, warmup, clock, min_warm_s, n_sets=4):
         step(nwarm + i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if not epilogue:
+        return sets[0], wall, nwarm
     # the same decode with the fused epilogue (gate + rank-16 head mixing in
     # the merge), timed apart
     g = torch.Generator(device="cuda").manual_seed(c.seed + 31)
@@ -552,6 +630,55 @@ def run_decode(torch, hca, c, steps, warmup, clock, min_warm_s, n_sets=4):
     return sets[0], wall, nwarm
 
 
+def measure_peaks(torch, hca):
+    """Ceilings this part reaches in this run: a streaming read of a 2 GiB
+    buffer (HBM) and a loop of bf16 32x32x16 matrix-core products on register
+    operands, one and two wavefronts per SIMD (the clock of the MFMA loop
+    comes from the shader-clock and 100 MHz counters).  Fills MEASURED."""
+    dev = "cuda"
+    nbytes = 2 << 30
+    buf = torch.zeros(nbytes // 4, dtype=torch.int32, device=dev)
+    sink = torch.empty(4 * 2048, dtype=torch.int32, device=dev)
+    clock = KernelClock(torch)
+    for i in range(8):
+        clock.run("stream" if i >= 2 else "warm", lambda: hca.hca_probe_stream_read(buf, 2048, sink=sink))
+    torch.cuda.synchronize()
+    _, t_med, _ = clock.stats_ms("stream")
+    hbm = nbytes / (t_med * 1e-3) / 1e9
+    del buf, sink
+    out = {"hbm_stream_read_gbs": round(hbm, 1), "hbm_stream_bytes": nbytes}
+    best = 0.0
+    for wps in (1, 2):
+        grid = 256 * wps
+        iters = 40000
+        msink = torch.empty(4 + 4 * grid, dtype=torch.float32, device=dev)
+        name = f"mfma{wps}"
+        for i in range(6):
+            clock.run(name if i >= 2 else "warm", lambda: hca.hca_probe_mfma_bf16(iters, grid, sink=msink))
+        torch.cuda.synchronize()
+        _, t_med, _ = clock.stats_ms(name)
+        tf = grid * 4 * iters * 4 * 32768 / (t_med * 1e-3) / 1e12
+        cyc, ticks = float(msink[0]), float(msink[1])
+        ghz = cyc / (ticks / 100e6) / 1e9 if ticks > 0 else None
+        out[f"mfma_bf16_tflops_{wps}wave_per_simd"] = round(tf, 1)
+        out[f"mfma_loop_clock_ghz_{wps}wave_per_simd"] = round(ghz, 3) if ghz else None
+        best = max(best, tf)
+    out["mfma_bf16_tflops"] = round(best, 1)
+    for mode, per in ((0, 1024), (1, 512)):
+        grid, iters = 256, 20000
+        lsink = torch.empty(4 * grid, dtype=torch.int32, device=dev)
+        name = f"lds{mode}"
+        for i in range(5):
+            clock.run(name if i >= 1 else "warm", lambda: hca.hca_probe_lds_read(mode, iters, grid, sink=lsink))
+        torch.cuda.synchronize()
+        _, t_med, _ = clock.stats_ms(name)
+        byt = grid * 4 * iters * 8 * per
+        out["lds_b128_read_tbs" if mode == 0 else "lds_tr16_read_tbs"] = round(byt / (t_med * 1e-3) / 1e12, 2)
+    MEASURED["hbm"] = hbm
+    MEASURED["mfma"] = best
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -559,8 +686,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--min-warmup-s", type=float, default=0.3,
                     help="continue the warmup until this much GPU time has run (clock ramp)")
-    ap.add_argument("--workload", default="prefill_8k", choices=WORKLOADS)
+    ap.add_argument("--workload", default="prefill_128k", choices=WORKLOADS)
     ap.add_argument("--no-decode", action="store_true", help="skip the decode_64x128k companion")
+    ap.add_argument("--no-mixed", action="store_true", help="skip the mixed_1m companion of prefill_128k")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the fused-epilogue, lse and backward timings of the prefill workloads")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measurement probes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -612,6 +743,9 @@ def main():
             out["cpu_baseline"] = cpu_baseline_dsa(inp, args.cpu_seconds)
         print(json.dumps(out), flush=True)
         return
+    if not args.no_peaks:
+        log("[bench] measurement probes (stream read, matrix-core loop, LDS reads)")
+        peaks = measure_peaks(torch, hca)
     c = CONFIGS[args.workload]
     e = 2 if c.dtype == "bf16" else 4
     result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -631,11 +765,11 @@ def main():
         t_pre, t_cmp, t_app = clock.mean_ms("prefill"), clock.mean_ms("compress"), clock.mean_ms("ring_append")
         ms_step = wall * 1e3 / args.steps
         bound = "hbm" if pf / pb < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "mfma"
-        kernels["prefill"] = roofline("prefill_chunk", c.name, pb, pf, t_pre, bound)
+        kernels["prefill"] = roofline("prefill_chunk", c.name, pb, pf, t_pre, bound, clock, "prefill")
         kernels["prefill"]["mfma_frac"] = round(pf / (t_pre * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
         kernels["prefill"]["hbm_frac"] = round(pb / (t_pre * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
-        kernels["compress"] = roofline("compress_chunk", c.name, cb, cf, t_cmp, "hbm")
-        kernels["ring_append"] = roofline("ring_append", c.name, rb, 0, t_app, "hbm")
+        kernels["compress"] = roofline("compress_chunk", c.name, cb, cf, t_cmp, "hbm", clock, "compress")
+        kernels["ring_append"] = roofline("ring_append", c.name, rb, 0, t_app, "hbm", clock, "ring_append")
         result.update({"value": round(n / (ms_step * 1e-3), 1), "unit": "tokens/s",
                        "ms_per_step": round(ms_step, 4)})
         result["config"] = {"workload": c.name, "batch": 1, "chunk_tokens": n, "pos0": p0, "seq_len": p0 + n,
@@ -650,102 +784,153 @@ def main():
         torch.cuda.empty_cache()
     elif c.has_prefill:
         log(f"[bench] {c.name}: prefill lens={list(c.prefill_lens)} steps={args.steps}")
-        inp, wall, nwarm = run_prefill(torch, hca, c, args.steps, args.warmup, clock, args.min_warmup_s)
-        result["warmup_steps_run"] = nwarm
-        lens = inp["lens"]
-        pb, pf = prefill_work(c, lens, e)
-        cb, cf = compress_work(c, lens, e)
-        t_pre, t_cmp = clock.mean_ms("prefill"), clock.mean_ms("compress")
-        ms_step = wall * 1e3 / args.steps
-        ntok = sum(lens)
-        bound = "hbm" if pf / pb < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "mfma"
-        kernels["prefill"] = roofline("prefill", c.name, pb, pf, t_pre, bound)
-        kernels["prefill"]["mfma_frac"] = round(pf / (t_pre * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
-        kernels["prefill"]["hbm_frac"] = round(pb / (t_pre * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
-        kernels["compress"] = roofline("compress", c.name, cb, cf, t_cmp, "hbm")
-        if clock.pairs.get("prefill_gated_vha"):
-            t_epi = clock.mean_ms("prefill_gated_vha")
-            # + gate logits read; + 2 mixing products per (token, column): 4 * Hq * rank flops
-            eb = pb + ntok_of(lens) * c.hq * 4
-            ef = pf + ntok_of(lens) * c.d * 4 * c.hq * EPILOGUE_RANK
-            kernels["prefill_gated_vha"] = roofline("prefill_gated_vha", c.name, eb, ef, t_epi, bound)
-            kernels["prefill_gated_vha"]["overhead_vs_prefill"] = round(t_epi / t_pre - 1.0, 4)
-        if clock.pairs.get("backward"):
-            bb, bf = backward_work(c, lens, e)
-            t_bwd, t_lse = clock.mean_ms("backward"), clock.mean_ms("prefill_lse")
-            bbound = "hbm" if bf / bb < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "mfma"
-            kernels["backward"] = roofline("backward", c.name, bb, bf, t_bwd, bbound)
-            kernels["backward"]["mfma_frac"] = round(bf / (t_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
-            kernels["backward"]["hbm_frac"] = round(bb / (t_bwd * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
-            kernels["backward"]["ratio_to_forward"] = round(t_bwd / t_pre, 3)
-            kernels["prefill_lse"] = roofline("prefill_lse", c.name, pb + ntok_of(lens) * c.hq * 4, pf, t_lse, bound)
-            kernels["prefill_lse"]["overhead_vs_prefill"] = round(t_lse / t_pre - 1.0, 4)
-        result.update({"value": round(ntok / (ms_step * 1e-3), 1), "unit": "tokens/s",
-                       "ms_per_step": round(ms_step, 4)})
-        result["config"] = {"workload": c.name, "batch": len(lens), "seq_len": max(lens),
-                            "q_heads": c.hq, "kv_heads": c.hkv, "head_dim": c.d, "window": c.window,
-                            "block": c.block, "parallelism": "none (1 GPU)"}
-        result["roofline"] = kernels["prefill"]
-        if not args.no_cpu_baseline:
-            log(f"[bench] cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")
-            result["cpu_baseline"] = cpu_baseline_prefill(c, inp, args.cpu_seconds)
-        del inp
-        torch.cuda.empty_cache()
+        fields, kern = prefill_section(torch, hca, c, args, clock, extras=not args.no_extras,
+                                       cpu=not args.no_cpu_baseline)
+        result.update(fields)
+        kernels.update(kern)
 
     dcfg = None
-    if c.name == "decode_64x128k":
+    if c.name in ("decode_64x128k", "mixed_1m"):
         dcfg = c
-    elif c.name == "mixed_1m":
-        dcfg = c
-    elif c.name == "prefill_8k" and not args.no_decode:
+    elif c.name in ("prefill_8k", "prefill_128k") and not args.no_decode:
         dcfg = CONFIGS["decode_64x128k"]
     if dcfg is not None:
         log(f"[bench] {dcfg.name}: decode steps={args.steps}")
         clock.reset()
-        dinp, dwall, dwarm = run_decode(torch, hca, dcfg, args.steps, args.warmup, clock, args.min_warmup_s)
-        db, df = decode_work(dcfg, dinp["lens"], 2)
-        t_dec = clock.mean_ms("decode")
-        kernels["decode"] = roofline("decode", dcfg.name, db, df, t_dec, "hbm")
-        # the step's cache maintenance (pool the completed block, append the
-        # new row): one new K, V row in and 128 ring rows + the entry per sequence
-        if clock.pairs.get("decode_gated_vha"):
-            t_de = clock.mean_ms("decode_gated_vha")
-            kernels["decode_gated_vha"] = roofline("decode_gated_vha", dcfg.name, db, df, t_de, "hbm")
-            kernels["decode_gated_vha"]["overhead_vs_decode"] = round(t_de / t_dec - 1.0, 4)
-        t_mnt = clock.mean_ms("decode_maintenance")
-        mb = len(dinp["lens"]) * dcfg.hkv * dcfg.d * 2 * (2 * 128 + 2 + 2 + 2)
-        kernels["decode_maintenance"] = roofline("decode_maintenance", dcfg.name, mb, 0, t_mnt, "hbm")
-        dec = {"workload": dcfg.name, "queries_per_s": round(len(dinp["lens"]) / (t_dec * 1e-3), 1),
-               "unit": "queries/s", "ms_per_call": round(t_dec, 5), "batch": len(dinp["lens"]),
-               "context_lens": dinp["lens"] if len(dinp["lens"]) <= 8 else f"{dinp['lens'][0]} each",
-               "warmup_steps_run": dwarm, "roofline": kernels["decode"]}
-        if not args.no_cpu_baseline:
-            dec["cpu_baseline"] = cpu_baseline_decode(dcfg, dinp, min(10.0, args.cpu_seconds))
+        dec, kern = decode_section(torch, hca, dcfg, args, clock, epilogue=dcfg.name == "decode_64x128k",
+                                   cpu=not args.no_cpu_baseline)
+        kernels.update(kern)
         if c.has_prefill:
             result["decode"] = dec
             if c.name == "mixed_1m":
                 # one step = chunk prefill (pooling + attention) + the decode batch
-                ms_step = result["ms_per_step"] + t_dec
-                ntok = sum(c.prefill_lens) + len(dinp["lens"])
+                ms_step = result["ms_per_step"] + dec["ms_per_call"]
+                ntok = sum(c.prefill_lens) + dec["batch"]
                 result["value"] = round(ntok / (ms_step * 1e-3), 1)
                 result["ms_per_step"] = round(ms_step, 4)
                 result["unit"] = "tokens/s"
         else:
             result.update({"value": dec["queries_per_s"], "unit": "queries/s",
-                           "ms_per_step": round(dwall * 1e3 / args.steps, 4)})
-            result["config"] = {"workload": dcfg.name, "batch": len(dinp["lens"]),
-                                "context": dinp["lens"][0], "q_heads": dcfg.hq, "kv_heads": dcfg.hkv,
-                                "head_dim": dcfg.d, "window": dcfg.window, "block": dcfg.block,
-                                "parallelism": "none (1 GPU)"}
+                           "ms_per_step": dec["ms_per_step"]})
+            result["config"] = dec["config"]
             result["roofline"] = kernels["decode"]
             if "cpu_baseline" in dec:
                 result["cpu_baseline"] = dec["cpu_baseline"]
+    if c.name == "prefill_128k" and not args.no_mixed:
+        result["mixed"] = mixed_section(torch, hca, args)
+    if not args.no_peaks:
+        result["measured_peaks"] = peaks
     result["kernels"] = kernels
     order = ["metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
              "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"]
     out = {k: result[k] for k in order if k in result}
     out.update({k: v for k, v in result.items() if k not in out})
     print(json.dumps(out), flush=True)
+
+
+def prefill_section(torch, hca, c, args, clock, extras=True, cpu=True, prefix=""):
+    """Time the prefill step of workload c; returns (result fields, kernel
+    roofline entries named prefix + kernel)."""
+    e = 2 if c.dtype == "bf16" else 4
+    inp, wall, nwarm = run_prefill(torch, hca, c, args.steps, args.warmup, clock, args.min_warmup_s, extras=extras)
+    lens = inp["lens"]
+    pb, pf = prefill_work(c, lens, e)
+    cb, cf = compress_work(c, lens, e)
+    t_pre, t_cmp = clock.mean_ms("prefill"), clock.mean_ms("compress_cold")
+    ms_step = wall * 1e3 / args.steps
+    ntok = sum(lens)
+    bound = "hbm" if pf / pb < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "mfma"
+    k = {}
+    k["prefill"] = roofline("prefill", c.name, pb, pf, t_pre, bound, clock, "prefill")
+    k["prefill"]["mfma_frac"] = round(pf / (t_pre * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+    k["prefill"]["hbm_frac"] = round(pb / (t_pre * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+    # pooling with a cold last-level cache (its own loop); in-step time beside it
+    k["compress"] = roofline("compress", c.name, cb, cf, t_cmp, "hbm", clock, "compress_cold")
+    k["compress"]["in_step_avg_ms"] = round(clock.mean_ms("compress"), 5)
+    if clock.pairs.get("prefill_gated_vha"):
+        t_epi = clock.mean_ms("prefill_gated_vha")
+        # + gate logits read; + 2 mixing products per (token, column): 4 * Hq * rank flops
+        eb = pb + ntok_of(lens) * c.hq * 4
+        ef = pf + ntok_of(lens) * c.d * 4 * c.hq * EPILOGUE_RANK
+        k["prefill_gated_vha"] = roofline("prefill_gated_vha", c.name, eb, ef, t_epi, bound, clock,
+                                          "prefill_gated_vha")
+        k["prefill_gated_vha"]["overhead_vs_prefill"] = round(t_epi / t_pre - 1.0, 4)
+    if clock.pairs.get("backward"):
+        bb, bf = backward_work(c, lens, e)
+        t_bwd, t_lse = clock.mean_ms("backward"), clock.mean_ms("prefill_lse")
+        bbound = "hbm" if bf / bb < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "mfma"
+        k["backward"] = roofline("backward", c.name, bb, bf, t_bwd, bbound, clock, "backward")
+        k["backward"]["mfma_frac"] = round(bf / (t_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+        k["backward"]["hbm_frac"] = round(bb / (t_bwd * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        k["backward"]["ratio_to_forward"] = round(t_bwd / t_pre, 3)
+        k["prefill_lse"] = roofline("prefill_lse", c.name, pb + ntok_of(lens) * c.hq * 4, pf, t_lse, bound,
+                                    clock, "prefill_lse")
+        k["prefill_lse"]["overhead_vs_prefill"] = round(t_lse / t_pre - 1.0, 4)
+    fields = {"value": round(ntok / (ms_step * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(ms_step, 4),
+              "warmup_steps_run": nwarm,
+              "config": {"workload": c.name, "batch": len(lens), "seq_len": max(lens), "q_heads": c.hq,
+                         "kv_heads": c.hkv, "head_dim": c.d, "window": c.window, "block": c.block,
+                         "parallelism": "none (1 GPU)"},
+              "roofline": k["prefill"]}
+    if cpu:
+        log(f"[bench] cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")
+        fields["cpu_baseline"] = cpu_baseline_prefill(c, inp, args.cpu_seconds,
+                                                      min_rows=2048 if max(lens) > 65536 else 0)
+    del inp
+    torch.cuda.empty_cache()
+    return fields, {prefix + n: v for n, v in k.items()}
+
+
+def decode_section(torch, hca, dcfg, args, clock, epilogue=True, cpu=True, prefix=""):
+    """Time hca_attend_decode on workload dcfg (rotating caches); returns
+    (decode summary, kernel roofline entries named prefix + kernel)."""
+    dinp, dwall, dwarm = run_decode(torch, hca, dcfg, args.steps, args.warmup, clock, args.min_warmup_s,
+                                    epilogue=epilogue)
+    db, df = decode_work(dcfg, dinp["lens"], 2)
+    t_dec = clock.mean_ms("decode")
+    k = {"decode": roofline("decode", dcfg.name, db, df, t_dec, "hbm", clock, "decode")}
+    if clock.pairs.get("decode_gated_vha"):
+        t_de = clock.mean_ms("decode_gated_vha")
+        k["decode_gated_vha"] = roofline("decode_gated_vha", dcfg.name, db, df, t_de, "hbm", clock,
+                                         "decode_gated_vha")
+        k["decode_gated_vha"]["overhead_vs_decode"] = round(t_de / t_dec - 1.0, 4)
+    # the step's cache maintenance (pool the completed block, append the new
+    # row): one new K, V row in and 128 ring rows + the entry per sequence
+    t_mnt = clock.mean_ms("decode_maintenance")
+    mb = len(dinp["lens"]) * dcfg.hkv * dcfg.d * 2 * (2 * 128 + 2 + 2 + 2)
+    k["decode_maintenance"] = roofline("decode_maintenance", dcfg.name, mb, 0, t_mnt, "hbm", clock,
+                                       "decode_maintenance")
+    dec = {"workload": dcfg.name, "queries_per_s": round(len(dinp["lens"]) / (t_dec * 1e-3), 1),
+           "unit": "queries/s", "ms_per_call": round(t_dec, 5), "batch": len(dinp["lens"]),
+           "context_lens": dinp["lens"] if len(dinp["lens"]) <= 8 else f"{dinp['lens'][0]} each",
+           "warmup_steps_run": dwarm, "ms_per_step": round(dwall * 1e3 / args.steps, 4),
+           "config": {"workload": dcfg.name, "batch": len(dinp["lens"]), "context": dinp["lens"][0],
+                      "q_heads": dcfg.hq, "kv_heads": dcfg.hkv, "head_dim": dcfg.d, "window": dcfg.window,
+                      "block": dcfg.block, "parallelism": "none (1 GPU)"},
+           "roofline": k["decode"]}
+    if cpu:
+        dec["cpu_baseline"] = cpu_baseline_decode(dcfg, dinp, min(10.0, args.cpu_seconds))
+    return dec, {prefix + n: v for n, v in k.items()}
+
+
+def mixed_section(torch, hca, args):
+    """mixed_1m as a companion of the default run: the 32768-token chunk
+    (pooling + attention) and the decode of 8 sequences at 256K-1M, one step
+    = both on one stream.  Oracle baselines are left to --workload mixed_1m."""
+    from hca_workloads import CONFIGS
+
+    c = CONFIGS["mixed_1m"]
+    log(f"[bench] {c.name} (companion): chunk + decode, steps={args.steps}")
+    clock = KernelClock(torch)
+    fields, kern = prefill_section(torch, hca, c, args, clock, extras=False, cpu=False)
+    clock.reset()
+    dec, dk = decode_section(torch, hca, c, args, clock, epilogue=False, cpu=False)
+    ms_step = fields["ms_per_step"] + dec["ms_per_call"]
+    ntok = sum(c.prefill_lens) + dec["batch"]
+    return {"workload": c.name, "value": round(ntok / (ms_step * 1e-3), 1), "unit": "tokens/s",
+            "ms_per_step": round(ms_step, 4), "chunk_tokens": sum(c.prefill_lens),
+            "decode_context_lens": dec["context_lens"], "chunk": kern["prefill"], "compress": kern["compress"],
+            "decode": dk["decode"]}
 
 
 if __name__ == "__main__":

@@ -26,6 +26,9 @@ from .hca import (  # noqa: F401
     hca_dsa_decode,
     hca_dsa_decode_workspace_bytes,
     hca_prefill_chunk_workspace_bytes,
+    hca_probe_lds_read,
+    hca_probe_mfma_bf16,
+    hca_probe_stream_read,
     hca_ring_append,
     hca_status_string,
     hca_version,

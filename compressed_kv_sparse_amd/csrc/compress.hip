@@ -65,6 +65,10 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a, int cw) {
   const size_t col = (size_t)h * a.d + c0 + (tid % TPR) * VEC;  // this thread's first element in a row
   const int r0 = tid / TPR;
 
+  // the pooling logits first: loads complete in issue order, so logits
+  // issued after the rows would make the softmax below wait for every row
+  const float w0 = a.w[h * kBlock + lane], w1 = a.w[h * kBlock + 64 + lane];
+  __builtin_amdgcn_sched_barrier(0);
   // all of this thread's loads are issued before any is used, so a thread
   // keeps PASSES 16-byte loads in flight (the default schedule would wait
   // for each load before issuing the next)
@@ -92,11 +96,11 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a, int cw) {
 
   // pooling weights p = softmax(w_h), max-subtracted, in fp32, while the
   // rows are in flight.  Every wavefront computes all 128 weights (two per
-  // lane, wave-wide max and sum) and writes them to p_s itself: the waves
-  // write identical values and each reads only after its own writes, so no
-  // barrier (which would also wait for the row loads) is needed.
+  // lane, wave-wide max and sum) and writes them to its own p_s row, which
+  // only its lanes read afterwards: a wavefront-scope release / acquire
+  // around a wave barrier orders the lanes' stores before the other lanes'
+  // loads (no workgroup barrier, which would also wait for the row loads).
   {
-    const float w0 = a.w[h * kBlock + lane], w1 = a.w[h * kBlock + 64 + lane];
     float mx = fmaxf(w0, w1);
     for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
     const float e0 = expf(w0 - mx), e1 = expf(w1 - mx);
@@ -104,6 +108,9 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a, int cw) {
     for (int off = 32; off > 0; off >>= 1) sm += __shfl_xor(sm, off);
     p_s[wave][lane] = e0 / sm;
     p_s[wave][64 + lane] = e1 / sm;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
   float acc[VEC];
 #pragma unroll

@@ -63,6 +63,24 @@ size_t staged_plane_bytes(const hca_params* p, int32_t batch, int32_t total_rows
 
 extern "C" {
 
+hca_status hca_probe_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t grid, void* stream) {
+  if (!buf || !sink) return HCA_ERR_NULL;
+  if (bytes == 0 || bytes % 16 || grid < 1 || grid > 65536) return HCA_ERR_SHAPE;
+  return from_hip(hca::launch_probe_stream_read(buf, bytes, (unsigned*)sink, grid, (hipStream_t)stream));
+}
+
+hca_status hca_probe_mfma_bf16(int32_t iters, int32_t grid, float* sink, void* stream) {
+  if (!sink) return HCA_ERR_NULL;
+  if (iters < 1 || grid < 1 || grid > 65536) return HCA_ERR_SHAPE;
+  return from_hip(hca::launch_probe_mfma(iters, grid, sink, (hipStream_t)stream));
+}
+
+hca_status hca_probe_lds_read(int32_t mode, int32_t iters, int32_t grid, uint32_t* sink, void* stream) {
+  if (!sink) return HCA_ERR_NULL;
+  if ((mode != 0 && mode != 1) || iters < 1 || grid < 1 || grid > 65536) return HCA_ERR_SHAPE;
+  return from_hip(hca::launch_probe_lds(mode, iters, grid, (unsigned*)sink, (hipStream_t)stream));
+}
+
 const char* hca_version(void) { return "0.1.0"; }
 
 const char* hca_status_string(hca_status s) {

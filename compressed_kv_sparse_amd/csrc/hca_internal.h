@@ -208,4 +208,12 @@ struct DsaArgs {
 size_t dsa_workspace_bytes(int batch, int max_seqlen, int topk);
 hipError_t launch_dsa_decode(DsaArgs a, hipStream_t s);
 
+// Measurement probes (probe.hip): a streaming read of `bytes` bytes, a
+// matrix-core loop and LDS read loops (mode 0: 16-byte reads, 1: transposed
+// 8-byte reads).  Each writes 4 values per workgroup to `sink` (the MFMA
+// probe first writes its clock readings to sink[0..3]).
+hipError_t launch_probe_stream_read(const void* buf, size_t bytes, unsigned* sink, int grid, hipStream_t s);
+hipError_t launch_probe_mfma(int iters, int grid, float* sink, hipStream_t s);
+hipError_t launch_probe_lds(int mode, int iters, int grid, unsigned* sink, hipStream_t s);
+
 }  // namespace hca

@@ -10,7 +10,6 @@ no fallback implementation.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 
 import torch
@@ -26,6 +25,7 @@ EXPORTS = ("hca_compress", "hca_attend_prefill", "hca_decode_workspace_bytes",
            "hca_attend_decode_gated_vha", "hca_attend_prefill_chunk_gated_vha",
            "hca_attend_prefill_lse", "hca_attend_prefill_backward_workspace_bytes", "hca_attend_prefill_backward",
            "hca_dsa_decode_workspace_bytes", "hca_dsa_decode",
+           "hca_probe_stream_read", "hca_probe_mfma_bf16", "hca_probe_lds_read",
            "hca_status_string", "hca_version")
 
 
@@ -110,6 +110,12 @@ def library() -> ctypes.CDLL:
     lib.hca_dsa_decode_workspace_bytes.restype = sz
     lib.hca_dsa_decode.argtypes = [i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hca_dsa_decode.restype = ctypes.c_int
+    lib.hca_probe_stream_read.argtypes = [vp, sz, vp, i32, vp]
+    lib.hca_probe_stream_read.restype = ctypes.c_int
+    lib.hca_probe_mfma_bf16.argtypes = [i32, i32, vp, vp]
+    lib.hca_probe_mfma_bf16.restype = ctypes.c_int
+    lib.hca_probe_lds_read.argtypes = [i32, i32, i32, vp, vp]
+    lib.hca_probe_lds_read.restype = ctypes.c_int
     lib.hca_status_string.argtypes = [ctypes.c_int]
     lib.hca_status_string.restype = ctypes.c_char_p
     lib.hca_version.argtypes = []
@@ -310,10 +316,6 @@ def hca_attend_decode_gated_vha(params: HcaParams, seqlens, cu_blocks, max_block
     return o
 
 
-def default_scale(head_dim: int) -> float:
-    return 1.0 / math.sqrt(head_dim)
-
-
 # ---------------------------------------------------------------------------
 # Serving with a cache: new rows at positions pos0[b] .. pos0[b] + n_b - 1.
 # ---------------------------------------------------------------------------
@@ -386,3 +388,37 @@ def hca_attend_prefill_chunk_gated_vha(params: HcaParams, cu_seqlens, pos0, cu_b
         _ptr(vha_u), _ptr(vha_v), rank, _ptr(o), _ptr(workspace), ws_bytes, _stream(stream))
     _check("hca_attend_prefill_chunk_gated_vha", st)
     return o
+
+
+# ---------------------------------------------------------------------------
+# Measurement probes (not the layer): ceilings the benchmark reads the hot
+# path against.  Each returns the sink tensor it wrote.
+# ---------------------------------------------------------------------------
+def hca_probe_stream_read(buf, grid: int, sink=None, stream=None):
+    """Read every byte of `buf` (contiguous, byte size a multiple of 16) once."""
+    if sink is None:
+        sink = torch.empty(4 * grid, dtype=torch.int32, device=buf.device)
+    st = library().hca_probe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), int(grid),
+                                         _stream(stream))
+    _check("hca_probe_stream_read", st)
+    return sink
+
+
+def hca_probe_mfma_bf16(iters: int, grid: int, sink=None, device=None, stream=None):
+    """grid x 4 wavefronts, each iters x 4 bf16 32x32x16 matrix-core products;
+    sink[0] / sink[1] = shader-clock cycles / 100 MHz ticks of one loop."""
+    if sink is None:
+        sink = torch.empty(4 + 4 * grid, dtype=torch.float32, device=device or torch.cuda.current_device())
+    st = library().hca_probe_mfma_bf16(int(iters), int(grid), _ptr(sink), _stream(stream))
+    _check("hca_probe_mfma_bf16", st)
+    return sink
+
+
+def hca_probe_lds_read(mode: int, iters: int, grid: int, sink=None, device=None, stream=None):
+    """LDS reads, mode 0: 16-byte rows (1 KiB per instruction); mode 1:
+    transposed 8-byte V^T fragment reads (512 bytes per instruction)."""
+    if sink is None:
+        sink = torch.empty(4 * grid, dtype=torch.int32, device=device or torch.cuda.current_device())
+    st = library().hca_probe_lds_read(int(mode), int(iters), int(grid), _ptr(sink), _stream(stream))
+    _check("hca_probe_lds_read", st)
+    return sink

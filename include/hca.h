@@ -412,6 +412,33 @@ HCA_API hca_status hca_dsa_decode(int32_t batch, int32_t max_seqlen, int32_t top
                                   const int8_t* qi, const void* k, const void* v, const int8_t* ki, void* o,
                                   int32_t* sel, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Measurement probes.  Not part of the layer: they measure what the part
+ * reaches on plain streams of work, so that the benchmark can state the
+ * hot-path kernels' fractions against measured ceilings next to the
+ * published ones.  All are asynchronous on `stream`; `sink` is a
+ * caller-owned device buffer the kernels write so that their work is kept.
+ *
+ * hca_probe_stream_read - reads every byte of `buf` (device, `bytes` a
+ *   multiple of 16) once with 16-byte non-temporal loads; `grid` workgroups
+ *   of 256 threads; sink: device uint32 [4 * grid].
+ * hca_probe_mfma_bf16 - each of `grid` workgroups (4 wavefronts) runs
+ *   `iters` x 4 independent v_mfma_f32_32x32x16_bf16 per wavefront
+ *   (32768 flops each); sink: device float [4 + 4 * grid].  sink[0] and
+ *   sink[1] receive the shader-clock cycles and the fixed-rate (100 MHz)
+ *   ticks that the first wavefront's loop took, whose ratio is the clock the
+ *   loop ran at.
+ * hca_probe_lds_read - each wavefront of `grid` workgroups reads LDS `iters`
+ *   x 8 times: mode 0 one 1 KiB row per instruction (16-byte reads), mode 1
+ *   the transposed 8-byte reads of V^T fragments (512 bytes per
+ *   instruction); sink: device uint32 [4 * grid].
+ * Return HCA_ERR_NULL for a NULL buffer, HCA_ERR_SHAPE for sizes out of
+ * range (grid 1 .. 65536, iters >= 1), HCA_ERR_HIP if the launch fails.
+ */
+HCA_API hca_status hca_probe_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t grid, void* stream);
+HCA_API hca_status hca_probe_mfma_bf16(int32_t iters, int32_t grid, float* sink, void* stream);
+HCA_API hca_status hca_probe_lds_read(int32_t mode, int32_t iters, int32_t grid, uint32_t* sink, void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 HCA_API const char* hca_status_string(hca_status status);
 

@@ -45,7 +45,7 @@ from .hca_oracle import BLOCK, _f64, _ints, attend_prefill, compress, cu_blocks_
 
 
 def attend_prefill_backward(q, k, v, w, dout, cu_seqlens, window: int, scale=None, block: int = BLOCK,
-                            return_stats: bool = False):
+                            return_stats: bool = False, rows=None, q_holds_rows_only: bool = False):
     """Gradients of sum(dout * O) for O = the HCA prefill forward of q, k, v, w.
 
     q, dout: [N_tok, Hq, d]; k, v: [N_tok, Hkv, d] raw rows; w: [Hkv, block]
@@ -53,10 +53,21 @@ def attend_prefill_backward(q, k, v, w, dout, cu_seqlens, window: int, scale=Non
     (dq [N_tok, Hq, d], dk, dv [N_tok, Hkv, d], dw [Hkv, block]); with
     return_stats also a dict holding the per-row log-sum-exp of the scaled
     scores ('lse', [N_tok, Hq], natural log) and D = dO . O ('delta').
+
+    rows: optional global token indices.  Only those query rows are taken
+    through the chain rule: dq, lse and delta are [len(rows), ...] in that
+    order, and dk, dv, dw hold the contributions of those rows alone (the
+    exact gradient of sum over the selected rows of dout . O).  A raw row r
+    whose every reader is selected (the rows r .. r+W-1 of its window, and
+    every row that sees r's compressed entry) therefore gets its exact dk and
+    dv.  With q_holds_rows_only, q and dout are [len(rows), Hq, d] and hold
+    the rows of those tokens, so a sample of a very long sequence needs only
+    its own queries.
     """
-    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    k, v = _f64(k), _f64(v)
     cu = _ints(cu_seqlens)
     cub = cu_blocks_from_cu_seqlens(cu, block)
+    ntok = int(cu[-1])
     hq, d = q.shape[1], q.shape[2]
     hkv = k.shape[1]
     g = hq // hkv
@@ -64,39 +75,45 @@ def attend_prefill_backward(q, k, v, w, dout, cu_seqlens, window: int, scale=Non
         scale = 1.0 / math.sqrt(d)
     p = pooling_weights(w)  # [Hkv, block]
     kc, vc = compress(k, w, cu, block), compress(v, w, cu, block)
+    if rows is None:
+        rows = range(ntok)
+    rows = [int(r) for r in rows]
+    assert not q_holds_rows_only or (len(rows) == q.shape[0] and len(rows) == dout.shape[0])
+    seq_of = np.searchsorted(cu, np.asarray(rows, dtype=np.int64), side="right") - 1
 
-    dq = np.zeros_like(q)
+    dq = np.zeros((len(rows), hq, d))
     dk, dv = np.zeros_like(k), np.zeros_like(v)
     dkc, dvc = np.zeros_like(kc), np.zeros_like(vc)
-    lse = np.zeros((q.shape[0], hq))
-    delta = np.zeros((q.shape[0], hq))
-    for b in range(len(cu) - 1):
-        start, end = int(cu[b]), int(cu[b + 1])
-        for t in range(end - start):
-            tok = start + t
-            n, s0 = visible_sets(t, window, block)
-            for h in range(hkv):
-                hs = slice(h * g, (h + 1) * g)
-                keys = np.concatenate([kc[cub[b]: cub[b] + n, h], k[start + s0: tok + 1, h]])  # [nk, d]
-                vals = np.concatenate([vc[cub[b]: cub[b] + n, h], v[start + s0: tok + 1, h]])
-                qh, doh = q[tok, hs], dout[tok, hs]  # [G, d]
-                z = (qh @ keys.T) * scale  # [G, nk]
-                zmax = z.max(axis=1, keepdims=True)
-                e = np.exp(z - zmax)
-                a = e / e.sum(axis=1, keepdims=True)  # probabilities
-                o = a @ vals
-                dp = doh @ vals.T  # [G, nk]
-                dd = (doh * o).sum(axis=1)  # D = dO . O per row
-                dz = a * (dp - dd[:, None])
-                dq[tok, hs] = scale * (dz @ keys)
-                dkeys = scale * (dz.T @ qh)  # [nk, d]
-                dvals = a.T @ doh
-                dkc[cub[b]: cub[b] + n, h] += dkeys[:n]
-                dvc[cub[b]: cub[b] + n, h] += dvals[:n]
-                dk[start + s0: tok + 1, h] += dkeys[n:]
-                dv[start + s0: tok + 1, h] += dvals[n:]
-                lse[tok, hs] = zmax[:, 0] + np.log(e.sum(axis=1))
-                delta[tok, hs] = dd
+    lse = np.zeros((len(rows), hq))
+    delta = np.zeros((len(rows), hq))
+    for i, (tok, b) in enumerate(zip(rows, seq_of)):
+        start = int(cu[b])
+        t = tok - start
+        n, s0 = visible_sets(t, window, block)
+        qt = _f64(q[i] if q_holds_rows_only else q[tok])  # [Hq, d]
+        dot = _f64(dout[i] if q_holds_rows_only else dout[tok])
+        for h in range(hkv):
+            hs = slice(h * g, (h + 1) * g)
+            keys = np.concatenate([kc[cub[b]: cub[b] + n, h], k[start + s0: tok + 1, h]])  # [nk, d]
+            vals = np.concatenate([vc[cub[b]: cub[b] + n, h], v[start + s0: tok + 1, h]])
+            qh, doh = qt[hs], dot[hs]  # [G, d]
+            z = (qh @ keys.T) * scale  # [G, nk]
+            zmax = z.max(axis=1, keepdims=True)
+            e = np.exp(z - zmax)
+            a = e / e.sum(axis=1, keepdims=True)  # probabilities
+            o = a @ vals
+            dp = doh @ vals.T  # [G, nk]
+            dd = (doh * o).sum(axis=1)  # D = dO . O per row
+            dz = a * (dp - dd[:, None])
+            dq[i, hs] = scale * (dz @ keys)
+            dkeys = scale * (dz.T @ qh)  # [nk, d]
+            dvals = a.T @ doh
+            dkc[cub[b]: cub[b] + n, h] += dkeys[:n]
+            dvc[cub[b]: cub[b] + n, h] += dvals[:n]
+            dk[start + s0: tok + 1, h] += dkeys[n:]
+            dv[start + s0: tok + 1, h] += dvals[n:]
+            lse[i, hs] = zmax[:, 0] + np.log(e.sum(axis=1))
+            delta[i, hs] = dd
     dk_raw_only, dv_raw_only = dk.copy(), dv.copy()
     # pooling: entry j of sequence b is sum_i p_i x_{128j+i}
     gsum = np.zeros((hkv, block))
@@ -104,11 +121,11 @@ def attend_prefill_backward(q, k, v, w, dout, cu_seqlens, window: int, scale=Non
         start = int(cu[b])
         for j in range(int(cub[b + 1] - cub[b])):
             e = int(cub[b]) + j
-            rows = slice(start + block * j, start + block * (j + 1))
+            blk = slice(start + block * j, start + block * (j + 1))
             for h in range(hkv):
-                dk[rows, h] += p[h][:, None] * dkc[e, h][None, :]
-                dv[rows, h] += p[h][:, None] * dvc[e, h][None, :]
-                gsum[h] += k[rows, h] @ dkc[e, h] + v[rows, h] @ dvc[e, h]
+                dk[blk, h] += p[h][:, None] * dkc[e, h][None, :]
+                dv[blk, h] += p[h][:, None] * dvc[e, h][None, :]
+                gsum[h] += k[blk, h] @ dkc[e, h] + v[blk, h] @ dvc[e, h]
     dw = p * (gsum - (p * gsum).sum(axis=1, keepdims=True))
     if return_stats:
         return dq, dk, dv, dw, {"lse": lse, "delta": delta, "dkc": dkc, "dvc": dvc,

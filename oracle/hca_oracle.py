@@ -15,8 +15,9 @@ What the method computes (sources, by page title and section):
 * Zhidx article "280B total parameters, 14B activated ...", section
   "1. Latent-Gated Sparse Attention": attention runs only over the compressed
   entries and a window made of a small number of recent uncompressed tokens.
-* Model card "ERNIE 5.5 Flash Base" (nlp.com.ai): HCA layers cache one entry
-  per 128 tokens and use 512-dimensional heads.
+* Model card "ERNIE 5.5 Flash Base" (nlp.com.ai), architecture paragraph:
+  the HCA layers keep a single cached entry for each 128-token block, and
+  their attention heads are 512 wide.
 
 Readings taken where the pages leave a step open (each is restated where it is
 used below):

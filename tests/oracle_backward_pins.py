@@ -133,6 +133,38 @@ def pin_bwd_row_statistics(fwd, bwd):
             assert abs(st["lse"][t, head] - scipy.special.logsumexp(z)) < 1e-12
 
 
+def pin_bwd_row_subset_finite_differences(fwd, bwd):
+    """The rows= filter: with a subset of query rows (given as their own q
+    and dout rows), the gradients are those of sum over the subset of
+    dout . O, checked by central differences of the forward oracle on that
+    restricted loss; dq comes back for the subset only."""
+    lens, hq, hkv, d, block, window = [90, 60], 4, 2, 8, 16, 12
+    q, k, v, w, dout = _case(61, lens, hq, hkv, d, block)
+    cu = _cu(lens)
+    rows = [3, 15, 16, 47, 89, 90, 105, 149]
+    dq, dk, dv, dw = bwd.attend_prefill_backward(q[rows], k, v, w, dout[rows], cu, window, block=block, rows=rows,
+                                                 q_holds_rows_only=True)
+    assert dq.shape == (len(rows), hq, d)
+    r = np.random.default_rng(62)
+    eps = 1e-5
+
+    def loss(q_, k_, v_, w_):
+        kc = fwd.compress(k_, w_, cu, block)
+        vc = fwd.compress(v_, w_, cu, block)
+        o = fwd.attend_prefill(q_, k_, v_, kc, vc, cu, window, block=block, rows=rows, q_holds_rows_only=True)
+        return float((dout[rows] * o).sum())
+
+    args = {"q": q[rows], "k": k, "v": v, "w": w}
+    for name, grad in (("q", dq), ("k", dk), ("v", dv), ("w", dw)):
+        delta = r.standard_normal(args[name].shape)
+        hi, lo = dict(args), dict(args)
+        hi[name] = args[name] + eps * delta
+        lo[name] = args[name] - eps * delta
+        fd = (loss(**{x + "_": y for x, y in hi.items()}) - loss(**{x + "_": y for x, y in lo.items()})) / (2 * eps)
+        an = float((grad * delta).sum())
+        assert abs(fd - an) <= 1e-6 * max(abs(fd), 1.0), f"d{name} (row subset): finite difference {fd} vs {an}"
+
+
 BACKWARD_PINS = [
     pin_bwd_finite_differences_small_blocks,
     pin_bwd_finite_differences_block128,
@@ -140,4 +172,5 @@ BACKWARD_PINS = [
     pin_bwd_dw_sums_to_zero,
     pin_bwd_zero_dout,
     pin_bwd_row_statistics,
+    pin_bwd_row_subset_finite_differences,
 ]

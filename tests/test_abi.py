@@ -308,3 +308,19 @@ def test_dsa_validation(lib):
     assert dsa(ptr=NULL) == ERR_NULL
     assert dsa(ws=NULL) == ERR_WORKSPACE
     assert dsa(ws_bytes=100) == ERR_WORKSPACE
+
+
+def test_probe_validation(lib):
+    """The measurement probes reject missing buffers and sizes out of range
+    on the host."""
+    assert lib.hca_probe_stream_read(NULL, 1 << 20, DUMMY, 64, None) == ERR_NULL
+    assert lib.hca_probe_stream_read(DUMMY, 1 << 20, NULL, 64, None) == ERR_NULL
+    assert lib.hca_probe_stream_read(DUMMY, 0, DUMMY, 64, None) == ERR_SHAPE
+    assert lib.hca_probe_stream_read(DUMMY, 1000, DUMMY, 64, None) == ERR_SHAPE  # not a multiple of 16
+    assert lib.hca_probe_stream_read(DUMMY, 1 << 20, DUMMY, 0, None) == ERR_SHAPE
+    assert lib.hca_probe_mfma_bf16(100, 256, NULL, None) == ERR_NULL
+    assert lib.hca_probe_mfma_bf16(0, 256, DUMMY, None) == ERR_SHAPE
+    assert lib.hca_probe_mfma_bf16(100, 70000, DUMMY, None) == ERR_SHAPE
+    assert lib.hca_probe_lds_read(2, 100, 256, DUMMY, None) == ERR_SHAPE
+    assert lib.hca_probe_lds_read(0, 0, 256, DUMMY, None) == ERR_SHAPE
+    assert lib.hca_probe_lds_read(1, 100, 256, NULL, None) == ERR_NULL

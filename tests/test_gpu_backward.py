@@ -116,3 +116,47 @@ def test_backward_prefill_8k_full():
     _check("dk", dk, rdk)
     _check("dv", dv, rdv)
     _check("dw", dw, rdw)
+
+
+def test_backward_long_run_split_full():
+    """16640 tokens: 130 complete blocks, so the compressed keys span three
+    64-entry tiles, and the positions that see a compressed tile are split
+    into uneven runs of 65 (the long-context work split; at 8192 tokens and
+    below every run has 64 positions and only the first tile exists).  Every
+    row of dq, dk, dv and all of dw against the oracle."""
+    c, inp, kc, vc, o, lse, (dq, dk, dv, dw) = _run([16640], 1, 128, seed=531)
+    rdq, rdk, rdv, rdw, st = _oracle(c, inp)
+    _check("dq", dq, rdq)
+    _check("dk", dk, rdk)
+    _check("dv", dv, rdv)
+    _check("dw", dw, rdw)
+
+
+def test_backward_prefill_128k_sampled():
+    """The 128K training context (one 131072-token sequence, Hq 64, d 512,
+    W 128) in the launch configuration bench.py times: dq on sampled rows
+    (every key-set boundary plus seeded random rows), and dk, dv in full for
+    the last block.  Those rows are read only by the last 128 query rows
+    (their windows, and entry 1023, which only the last row sees), so the
+    oracle run over those query rows gives their exact gradients.  dw needs
+    every row of the sequence and is checked in full at 16640 tokens."""
+    from parity_util import sample_rows
+
+    c0 = CONFIGS["prefill_128k"]
+    T = c0.prefill_lens[0]
+    c, inp, kc, vc, o, lse, (dq, dk, dv, dw) = _run([T], c0.hkv, c0.window, seed=c0.seed)
+    last = list(range(T - 128, T))
+    rows = sorted(set(sample_rows(T, c.window, 40, seed=541)) | set(last))
+    idx = torch.tensor(rows, device=DEV)
+    q_rows, do_rows = inp["q"].index_select(0, idx).cpu(), inp["dout"].index_select(0, idx).cpu()
+    dq_rows = dq.index_select(0, idx)
+    del inp["q"], inp["dout"], o, dq
+    torch.cuda.empty_cache()
+    print(f"oracle over {len(rows)} query rows", flush=True)
+    rdq, rdk, rdv, _ = oracle.attend_prefill_backward(q_rows, inp["k"].cpu(), inp["v"].cpu(), inp["w"].cpu(),
+                                                      do_rows, inp["cu_seqlens_host"], c.window, rows=rows,
+                                                      q_holds_rows_only=True)
+    _check("dq (sampled rows)", dq_rows, rdq)
+    _check("dk (last block)", dk[T - 128:], rdk[T - 128:])
+    _check("dv (last block)", dv[T - 128:], rdv[T - 128:])
+    assert torch.isfinite(dw).all() and abs(float(dw.sum())) <= 1e-3 * float(dw.abs().sum())

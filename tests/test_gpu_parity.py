@@ -263,3 +263,70 @@ def test_decode_equals_last_prefill_row(dtype):
     assert_close(o_dec, to_np(o_pre[rows]), dt, "decode vs prefill row (GPU)", beyond_rounding=True)
     _, _, o_ref = oracle_prefill(inp, c.window, rows=rows)
     assert_close(o_dec, o_ref, dt, "decode vs oracle prefill row")
+
+
+def _decode_splits(p, batch, max_blocks):
+    """Key splits per (sequence, KV head), read back from the workspace size
+    the library asks for: two fp32 [splits, 64] arrays (m, l; each rounded
+    up to 256 bytes) plus the bf16 partial outputs [splits, 64, 512] per
+    unit.  The test needs it to place its score ramps inside each split."""
+    ws = hca.hca_decode_workspace_bytes(p, batch, max_blocks)
+    per_split = 2 * 64 * 4 + 64 * 512 * 2  # unit count * 64 * 4 is a multiple of 256 here
+    assert ws % (batch * per_split) == 0, ws
+    return ws // (batch * per_split)
+
+
+@pytest.mark.parametrize("lens", [
+    [131035] * 32 + [131072] * 32,   # 64 sequences, a few splits each; half the rings wrap
+    [1048575],                       # one long context: many two-tile splits, a wrapped ring
+], ids=["b64", "b1_1m"])
+def test_decode_bf16_headroom_fallback(lens):
+    """Scores that climb by more than 40 (log2 units) inside every key split
+    of the decode kernel: each split's first tile holds only low scores, so
+    its single-pass schedule is abandoned and the split reruns in the exact
+    two-pass one (row max, then weights <= 1).  Every output must match."""
+    c = cfg(CONFIGS["decode_64x128k"], decode_batch=len(lens))
+    inp = decode_inputs(c, DEV, lens=lens, seed=131)
+    p = params_for(c)
+    B, R = len(lens), c.ring
+    max_blocks = inp["max_blocks"]
+    splits = _decode_splits(p, B, max_blocks)
+    ntiles = (max_blocks + c.window + 31) // 32
+    tps = -(-ntiles // splits)
+    assert tps >= 2, (ntiles, splits)  # a one-tile split can never restart
+    span = 32 * tps  # keys per split
+    # slope per key so that a split's last tile max beats its first tile max
+    # by 40 log2 units: k = a(slot) u, q = u, score = a 512 / sqrt(512) log2(e)
+    lg = 512 ** 0.5 * 1.4426950408889634
+    slope = 40.0 / (lg * (span - 32))
+    u = inp["q"][0, 0].float()
+    u = u / u.pow(2).mean().sqrt()
+    inp["q"] = u.expand(B, 64, 512).to(torch.bfloat16).contiguous()
+    cub = inp["cu_blocks_host"]
+    kc = inp["kc"].clone()
+    kw = inp["kw"].clone()
+    for b, L in enumerate(lens):
+        nc = L // 128
+        lo = L - min(c.window, L)
+        a_c = slope * (torch.arange(nc, device=DEV) % span).float()
+        kc[int(cub[b]):int(cub[b]) + nc, 0] = (a_c[:, None] * u).to(torch.bfloat16)
+        pos = torch.arange(lo, L, device=DEV)
+        a_r = slope * ((nc + pos - lo) % span).float()
+        kw[b, pos % R, 0] = (a_r[:, None] * u).to(torch.bfloat16)
+    inp["kc"], inp["kw"] = kc.contiguous(), kw.contiguous()
+    # the ramp as the kernel sees it (sequence 0, head 0): in every split some
+    # later tile's max exceeds the first tile's max by more than 32
+    L0, nc0 = lens[0], lens[0] // 128
+    keys = torch.cat([kc[int(cub[0]):int(cub[0]) + nc0, 0].float(),
+                      kw[0, torch.arange(L0 - min(c.window, L0), L0, device=DEV) % R, 0].float()])
+    sc = (keys @ inp["q"][0, 0].float()) / 512 ** 0.5 * 1.4426950408889634
+    nk = sc.shape[0]
+    for s0 in range(0, nk, span):
+        seg = sc[s0:min(nk, s0 + span)]
+        if seg.shape[0] > 32:
+            assert (seg[32:].max() - seg[:32].max()).item() > 32, s0
+    o = run_decode(p, inp)
+    torch.cuda.synchronize()
+    ref = oracle.attend_decode(inp["q"].cpu(), inp["kc"].cpu(), inp["vc"].cpu(), inp["kw"].cpu(),
+                               inp["vw"].cpu(), lens, cub, c.window)
+    assert_close(o, ref, torch.bfloat16, f"decode fallback B={B} splits={splits} tiles/split={tps}")

@@ -15,19 +15,19 @@ SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), 
 # (name, original text, mutated text)
 MUTANTS = [
     ("softmax Jacobian without the -D term", "dz = a * (dp - dd[:, None])", "dz = a * dp"),
-    ("dq without the score scale", "dq[tok, hs] = scale * (dz @ keys)", "dq[tok, hs] = dz @ keys"),
+    ("dq without the score scale", "dq[i, hs] = scale * (dz @ keys)", "dq[i, hs] = dz @ keys"),
     ("value gradient through dz", "dvals = a.T @ doh", "dvals = dz.T @ doh"),
     ("key gradient from dO instead of q", "dkeys = scale * (dz.T @ qh)", "dkeys = scale * (dz.T @ doh)"),
     ("compressed keys get no gradient", "dkc[cub[b]: cub[b] + n, h] += dkeys[:n]",
      "dkc[cub[b]: cub[b] + n, h] += 0 * dkeys[:n]"),
     ("window gradient to reversed positions", "dk[start + s0: tok + 1, h] += dkeys[n:]",
      "dk[start + s0: tok + 1, h] += dkeys[n:][::-1]"),
-    ("pooling scatter with reversed weights", "dk[rows, h] += p[h][:, None] * dkc[e, h][None, :]",
-     "dk[rows, h] += p[h][::-1, None] * dkc[e, h][None, :]"),
-    ("dw without the V path", "gsum[h] += k[rows, h] @ dkc[e, h] + v[rows, h] @ dvc[e, h]",
-     "gsum[h] += k[rows, h] @ dkc[e, h]"),
+    ("pooling scatter with reversed weights", "dk[blk, h] += p[h][:, None] * dkc[e, h][None, :]",
+     "dk[blk, h] += p[h][::-1, None] * dkc[e, h][None, :]"),
+    ("dw without the V path", "gsum[h] += k[blk, h] @ dkc[e, h] + v[blk, h] @ dvc[e, h]",
+     "gsum[h] += k[blk, h] @ dkc[e, h]"),
     ("dw without centring", "dw = p * (gsum - (p * gsum).sum(axis=1, keepdims=True))", "dw = p * gsum"),
-    ("lse without the max", "lse[tok, hs] = zmax[:, 0] + np.log(e.sum(axis=1))", "lse[tok, hs] = np.log(e.sum(axis=1))"),
+    ("lse without the max", "lse[i, hs] = zmax[:, 0] + np.log(e.sum(axis=1))", "lse[i, hs] = np.log(e.sum(axis=1))"),
 ]
 
 

@@ -59,6 +59,49 @@ size_t staged_plane_bytes(const hca_params* p, int32_t batch, int32_t total_rows
   return (bytes + 255) / 256 * 256;
 }
 
+// Host checks and argument packing shared by the decode entry points
+// (everything but the workspace).  The status is HCA_OK with nothing to do
+// when batch == 0.
+hca_status decode_args(const hca_params* params, int32_t batch, int32_t max_blocks, const int32_t* seqlens,
+                       const int32_t* cu_blocks, const void* q, const void* kc, const void* vc, const void* kw,
+                       const void* vw, int32_t ring_cap, const float* gate, const float* vha_u,
+                       const float* vha_v, int32_t vha_rank, void* o, hca::DecodeArgs* a) {
+  hca_status st = check_params(params);
+  if (st != HCA_OK) return st;
+  if (batch < 0 || max_blocks < 0 || batch > 65535) return HCA_ERR_SHAPE;
+  if (ring_cap < params->window) return HCA_ERR_SHAPE;
+  if (params->dtype == HCA_BF16 && !mfma_shape(params)) return HCA_ERR_UNSUPPORTED;
+  if (params->dtype == HCA_BF16 && !(mfma_rows_fit(params, ring_cap) && mfma_rows_fit(params, max_blocks)))
+    return HCA_ERR_SHAPE;
+  st = check_epilogue(params, gate, vha_u, vha_v, vha_rank);
+  if (st != HCA_OK) return st;
+  if (batch == 0) return HCA_OK;
+  if (!seqlens || !cu_blocks || !q || !kw || !vw || !o) return HCA_ERR_NULL;
+  if (max_blocks > 0 && (!kc || !vc)) return HCA_ERR_NULL;
+  a->batch = batch;
+  a->max_blocks = max_blocks;
+  a->hq = params->num_q_heads;
+  a->hkv = params->num_kv_heads;
+  a->d = params->head_dim;
+  a->window = params->window;
+  a->ring = ring_cap;
+  a->scale = scale_of(params);
+  a->seqlens = seqlens;
+  a->cu_blocks = cu_blocks;
+  a->q = q;
+  a->kc = kc;
+  a->vc = vc;
+  a->kw = kw;
+  a->vw = vw;
+  a->o = o;
+  a->ws = nullptr;
+  a->gate = gate;
+  a->mix_u = vha_u;
+  a->mix_v = vha_v;
+  a->mix_rank = vha_u ? vha_rank : 0;
+  return HCA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -327,46 +370,17 @@ hca_status hca_attend_decode_gated_vha(const hca_params* params, int32_t batch, 
                                        int32_t ring_cap, const float* gate, const float* vha_u,
                                        const float* vha_v, int32_t vha_rank, void* o, void* workspace,
                                        size_t workspace_bytes, void* stream) {
-  hca_status st = check_params(params);
-  if (st != HCA_OK) return st;
-  if (batch < 0 || max_blocks < 0 || batch > 65535) return HCA_ERR_SHAPE;
-  if (ring_cap < params->window) return HCA_ERR_SHAPE;
-  if (params->dtype == HCA_BF16 && !mfma_shape(params)) return HCA_ERR_UNSUPPORTED;
-  if (params->dtype == HCA_BF16 && !(mfma_rows_fit(params, ring_cap) && mfma_rows_fit(params, max_blocks)))
-    return HCA_ERR_SHAPE;
-  st = check_epilogue(params, gate, vha_u, vha_v, vha_rank);
-  if (st != HCA_OK) return st;
-  if (batch == 0) return HCA_OK;
-  if (!seqlens || !cu_blocks || !q || !kw || !vw || !o) return HCA_ERR_NULL;
-  if (max_blocks > 0 && (!kc || !vc)) return HCA_ERR_NULL;
   hca::DecodeArgs a{};
-  a.batch = batch;
-  a.max_blocks = max_blocks;
-  a.hq = params->num_q_heads;
-  a.hkv = params->num_kv_heads;
-  a.d = params->head_dim;
-  a.window = params->window;
-  a.ring = ring_cap;
-  a.scale = scale_of(params);
-  a.seqlens = seqlens;
-  a.cu_blocks = cu_blocks;
-  a.q = q;
-  a.kc = kc;
-  a.vc = vc;
-  a.kw = kw;
-  a.vw = vw;
-  a.o = o;
-  a.ws = workspace;
-  a.gate = gate;
-  a.mix_u = vha_u;
-  a.mix_v = vha_v;
-  a.mix_rank = vha_u ? vha_rank : 0;
+  hca_status st = decode_args(params, batch, max_blocks, seqlens, cu_blocks, q, kc, vc, kw, vw, ring_cap, gate,
+                              vha_u, vha_v, vha_rank, o, &a);
+  if (st != HCA_OK || batch == 0) return st;
   hipStream_t s = (hipStream_t)stream;
   if (params->dtype == HCA_F32) return from_hip(hca::launch_decode_f32(a, s));
   const size_t need =
       hca::decode_workspace_bytes_bf16(batch, params->num_kv_heads, max_blocks, params->window);
   if (!workspace || workspace_bytes < need) return HCA_ERR_WORKSPACE;
   if (((uintptr_t)workspace) & 255) return HCA_ERR_WORKSPACE;
+  a.ws = workspace;
   return from_hip(hca::launch_decode_bf16(a, s));
 }
 

@@ -665,7 +665,7 @@ def measure_peaks(torch, hca):
         best = max(best, tf)
     out["mfma_bf16_tflops"] = round(best, 1)
     for mode, per in ((0, 1024), (1, 512)):
-        grid, iters = 256, 20000
+        grid, iters = 1024, 5000  # four workgroups (16 wavefronts) per CU keep enough reads in flight
         lsink = torch.empty(4 * grid, dtype=torch.int32, device=dev)
         name = f"lds{mode}"
         for i in range(5):

@@ -5,6 +5,7 @@ the C ABI of include/hca.h); this package is its Python binding.  Build the
 library with `python -m compressed_kv_sparse_amd.build`.
 """
 from .hca import (  # noqa: F401
+    DECODE_NOALLOC_SCRATCH_BYTES,
     EXPORTS,
     HCA_BF16,
     HCA_F32,
@@ -12,6 +13,7 @@ from .hca import (  # noqa: F401
     HcaLibraryMissing,
     HcaParams,
     hca_attend_decode,
+    hca_attend_decode_noalloc,
     hca_attend_decode_gated_vha,
     hca_attend_prefill,
     hca_attend_prefill_backward,

@@ -3,6 +3,8 @@
 // synchronisation, no global mutable state.
 #include <math.h>
 
+#include <mutex>
+
 #include "../../include/hca.h"
 #include "hca_internal.h"
 
@@ -100,6 +102,31 @@ hca_status decode_args(const hca_params* params, int32_t batch, int32_t max_bloc
   a->mix_v = vha_v;
   a->mix_rank = vha_u ? vha_rank : 0;
   return HCA_OK;
+}
+
+// Scratch of hca_attend_decode_noalloc: the split partials of one decode call
+// live in this file-scope device array instead of a caller workspace.  Each
+// GPU holds its own copy (at its own address) until the process ends.  Host
+// code never passes the array's name to a kernel (on the host it only stands
+// for the symbol): it asks the runtime for the device address once per
+// device, with that device current, and uses that pointer.
+static __device__ __align__(256) unsigned char scratch[HCA_DECODE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// Device address of `scratch` on the current device (NULL on failure).
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  ScratchSlot& slot = g_scratch[dev];
+  std::call_once(slot.once, [&slot] { slot.err = hipGetSymbolAddress(&slot.ptr, HIP_SYMBOL(scratch)); });
+  return slot.err == hipSuccess ? slot.ptr : nullptr;
 }
 
 }  // namespace
@@ -381,6 +408,27 @@ hca_status hca_attend_decode_gated_vha(const hca_params* params, int32_t batch, 
   if (!workspace || workspace_bytes < need) return HCA_ERR_WORKSPACE;
   if (((uintptr_t)workspace) & 255) return HCA_ERR_WORKSPACE;
   a.ws = workspace;
+  return from_hip(hca::launch_decode_bf16(a, s));
+}
+
+hca_status hca_attend_decode_noalloc(const hca_params* params, int32_t batch, int32_t max_blocks,
+                                     const int32_t* seqlens, const int32_t* cu_blocks, const void* q, const void* kc,
+                                     const void* vc, const void* kw, const void* vw, int32_t ring_cap, void* o,
+                                     void* stream) {
+  hca::DecodeArgs a{};
+  hca_status st = decode_args(params, batch, max_blocks, seqlens, cu_blocks, q, kc, vc, kw, vw, ring_cap, nullptr,
+                              nullptr, nullptr, 0, o, &a);
+  if (st != HCA_OK || batch == 0) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (params->dtype == HCA_F32) return from_hip(hca::launch_decode_f32(a, s));  // no scratch
+  const size_t need =
+      hca::decode_workspace_bytes_bf16(batch, params->num_kv_heads, max_blocks, params->window);
+  if (need > HCA_DECODE_NOALLOC_SCRATCH_BYTES) return HCA_ERR_WORKSPACE;
+  void* ws = scratch_on_current_device();
+  if (!ws) return HCA_ERR_HIP;
+  // the split kernel writes every partial the merge kernel reads: nothing
+  // in the scratch has to start at zero
+  a.ws = ws;
   return from_hip(hca::launch_decode_bf16(a, s));
 }
 

@@ -25,7 +25,7 @@ EXPORTS = ("hca_compress", "hca_attend_prefill", "hca_decode_workspace_bytes",
            "hca_attend_decode_gated_vha", "hca_attend_prefill_chunk_gated_vha",
            "hca_attend_prefill_lse", "hca_attend_prefill_backward_workspace_bytes", "hca_attend_prefill_backward",
            "hca_dsa_decode_workspace_bytes", "hca_dsa_decode",
-           "hca_probe_stream_read", "hca_probe_mfma_bf16", "hca_probe_lds_read",
+           "hca_probe_stream_read", "hca_probe_mfma_bf16", "hca_probe_lds_read", "hca_attend_decode_noalloc",
            "hca_status_string", "hca_version")
 
 
@@ -110,6 +110,8 @@ def library() -> ctypes.CDLL:
     lib.hca_dsa_decode_workspace_bytes.restype = sz
     lib.hca_dsa_decode.argtypes = [i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hca_dsa_decode.restype = ctypes.c_int
+    lib.hca_attend_decode_noalloc.argtypes = [P, i32, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp]
+    lib.hca_attend_decode_noalloc.restype = ctypes.c_int
     lib.hca_probe_stream_read.argtypes = [vp, sz, vp, i32, vp]
     lib.hca_probe_stream_read.restype = ctypes.c_int
     lib.hca_probe_mfma_bf16.argtypes = [i32, i32, vp, vp]
@@ -387,6 +389,22 @@ def hca_attend_prefill_chunk_gated_vha(params: HcaParams, cu_seqlens, pos0, cu_b
         _ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), _ptr(kw), _ptr(vw), int(kw.shape[1]), _ptr(gate),
         _ptr(vha_u), _ptr(vha_v), rank, _ptr(o), _ptr(workspace), ws_bytes, _stream(stream))
     _check("hca_attend_prefill_chunk_gated_vha", st)
+    return o
+
+
+DECODE_NOALLOC_SCRATCH_BYTES = 32 << 20  # HCA_DECODE_NOALLOC_SCRATCH_BYTES
+
+
+def hca_attend_decode_noalloc(params: HcaParams, seqlens, cu_blocks, max_blocks: int, q, kc, vc, kw, vw, o,
+                              stream=None):
+    """hca_attend_decode without a workspace: the library's static per-device
+    scratch holds the split partials (calls overlapping on one GPU race).
+    `o` must be given: this path allocates nothing.  Returns o."""
+    batch = seqlens.numel()
+    st = library().hca_attend_decode_noalloc(ctypes.byref(params), batch, int(max_blocks), _ptr(seqlens),
+                                             _ptr(cu_blocks), _ptr(q), _ptr(kc), _ptr(vc), _ptr(kw), _ptr(vw),
+                                             int(kw.shape[1]), _ptr(o), _stream(stream))
+    _check("hca_attend_decode_noalloc", st)
     return o
 
 

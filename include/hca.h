@@ -183,6 +183,32 @@ HCA_API hca_status hca_attend_decode(const hca_params* params, int32_t batch, in
                              void* o, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * hca_attend_decode_noalloc - hca_attend_decode (bf16 or fp32, no epilogue)
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  It takes
+ * no workspace: the split partials go to a static device array of
+ * HCA_DECODE_NOALLOC_SCRATCH_BYTES (32 MiB) that each GPU the library runs
+ * on holds until the process ends, and the call allocates and frees
+ * nothing.  Its device address is looked up once per device, on the first
+ * call with that device current.
+ *
+ * Arguments, layouts and results are those of hca_attend_decode (same
+ * kernels, bit-identical output).  Errors: as hca_attend_decode, plus
+ * HCA_ERR_WORKSPACE when the call needs more scratch than the array holds
+ * (hca_decode_workspace_bytes(params, batch, max_blocks) >
+ * HCA_DECODE_NOALLOC_SCRATCH_BYTES; 64 sequences at 131072 tokens need
+ * 16.9 MB) and HCA_ERR_HIP if the runtime cannot give the array's address.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (two streams, or two host threads) race on it; calls on one
+ * stream are ordered and safe.
+ */
+#define HCA_DECODE_NOALLOC_SCRATCH_BYTES (32u << 20)
+HCA_API hca_status hca_attend_decode_noalloc(const hca_params* params, int32_t batch, int32_t max_blocks,
+                                             const int32_t* seqlens, const int32_t* cu_blocks, const void* q,
+                                             const void* kc, const void* vc, const void* kw, const void* vw,
+                                             int32_t ring_cap, void* o, void* stream);
+
+/*
  * Serving with a cache: chunks of new tokens and decode steps.
  *
  * A sequence's HCA cache is its compressed entries (one per complete block,

@@ -324,3 +324,18 @@ def test_probe_validation(lib):
     assert lib.hca_probe_lds_read(2, 100, 256, DUMMY, None) == ERR_SHAPE
     assert lib.hca_probe_lds_read(0, 0, 256, DUMMY, None) == ERR_SHAPE
     assert lib.hca_probe_lds_read(1, 100, 256, NULL, None) == ERR_NULL
+
+
+def test_decode_noalloc_validation(lib):
+    """The allocation-free decode entry point checks its arguments like
+    hca_attend_decode, and refuses a batch whose partials would not fit its
+    static scratch, all before any HIP call."""
+    p = _p()
+    args = [DUMMY] * 7
+    assert lib.hca_attend_decode_noalloc(None, 4, 10, *args, 128, DUMMY, None) == ERR_NULL
+    assert lib.hca_attend_decode_noalloc(ctypes.byref(p), -1, 10, *args, 128, DUMMY, None) == ERR_SHAPE
+    assert lib.hca_attend_decode_noalloc(ctypes.byref(p), 4, 10, *args, 64, DUMMY, None) == ERR_SHAPE  # ring < W
+    assert lib.hca_attend_decode_noalloc(ctypes.byref(p), 4, 10, *args, 128, NULL, None) == ERR_NULL
+    assert lib.hca_attend_decode_noalloc(ctypes.byref(p), 0, 10, *args, 128, DUMMY, None) == OK
+    assert lib.hca_decode_workspace_bytes(ctypes.byref(p), 1024, 1024) > hca.DECODE_NOALLOC_SCRATCH_BYTES
+    assert lib.hca_attend_decode_noalloc(ctypes.byref(p), 1024, 1024, *args, 128, DUMMY, None) == ERR_WORKSPACE

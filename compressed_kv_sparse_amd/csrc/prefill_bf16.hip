@@ -578,6 +578,26 @@ __device__ __forceinline__ void load_epilogue_inputs(const PrefillArgs& a, char 
   if (a.gate && i8 < 128) ((float HCA_LDS*)(epi + kEpiGate))[i8] = sigmoid(gv);
 }
 
+// The Q^T fragments of one wave's 32 score rows (lane l: row l%32, elements
+// 16k + 8(l/32) .. +7 of k-step k).  The rows are 32 KiB contiguous in HBM
+// (qwave: heads 32hg .. +31 of one position); they come into `buf` with
+// direct loads, one 1 KiB row per instruction (row offset in the scalar
+// offset, lane offset fixed), and are read back with the K fragment pattern.
+// Loading the fragments straight from HBM (each lane 16 bytes of 32
+// different rows per instruction) touched every cache line four times and
+// took about four times as long.
+__device__ __forceinline__ void load_q(const bf16* qwave, char HCA_LDS* buf, int lane, int koff,
+                                       bf16x8 (&qf)[DSTEPS]) {
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(qwave, (size_t)32 * D * sizeof(bf16));
+#pragma unroll
+  for (int row = 0; row < 32; ++row)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void HCA_LDS*)(buf + row * KSTR), 16, lane * 16,
+                                             row * D * (int)sizeof(bf16), 0, 0);
+  wait_vm_all();
+#pragma unroll
+  for (int k = 0; k < DSTEPS; ++k) qf[k] = lds_k_frag(buf + koff + k * 32);
+}
+
 // Keys of position pair (t0, t_last): the later position's complete entries
 // plus the raw rows from the earlier position's window start to t_last.
 __host__ __device__ inline int pair_keys(int t0, int t_last, int window) {
@@ -661,27 +681,39 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, int pair0, in
   c.wpar = (wave ^ 1) * WSLOT + lane * 16;
   c.sc2 = a.scale * kLog2e;
 
-  // the empty parts of the first pipeline stages read the K and V buffers:
-  // make them finite.  Not kb[0]: the pass's K(0) load fills all of it, and
-  // other waves may issue that load before this wave's stores land.
-  for (int o = threadIdx.x * 16; !LO && o < KTILE; o += 256 * 16) *(u32x4 HCA_LDS*)(c.kb[1] + o) = u32x4{};
+  // Q^T fragments of the wave's 32 rows (heads 32hg .. +31 of position t),
+  // staged through the wave's own tile buffer (see load_q); each buffer
+  // names a distinct array, so the branches are uniform and compile-time.
+  const bf16* qwave = (const bf16*)a.q + ((size_t)qrow * a.hq + kvh * G + 32 * hg) * D;
+  bf16x8 qf[DSTEPS];
+  if constexpr (EPI) {
+    // the epilogue instantiation has no registers to spare for the staged
+    // form (it spills): strided fragment loads straight from HBM
+    const bf16* qr = qwave + (size_t)(lane & 31) * D + 8 * (lane >> 5);
+#pragma unroll
+    for (int k = 0; k < DSTEPS; ++k) qf[k] = *(const bf16x8*)(qr + 16 * k);
+    // the epilogue's inputs: their latency overlaps the Q loads, and the
+    // pass's barriers order the LDS writes before their use
+    load_epilogue_inputs(a, epi_s, kvh, start + (t0 - p0), t1_ok);
+  } else {
+    if (wave == 0)
+      load_q(qwave, c.kb[0], lane, c.koff, qf);
+    else if (wave == 1)
+      load_q(qwave, c.kb[1], lane, c.koff, qf);
+    else if (wave == 2)
+      load_q(qwave, c.vb[0], lane, c.koff, qf);
+    else
+      load_q(qwave, c.vb[1], lane, c.koff, qf);
+    __syncthreads();  // every wave holds its fragments: the buffers are free
+  }
+
+  // the empty parts of the first pipeline stages read the V buffers with
+  // zero weights: make them finite.  (Stale K only feeds scores of missing
+  // tiles, whose weights are masked to zero bit for bit.)
   for (int o = threadIdx.x * 16; !LO && o < VTILE; o += 256 * 16) {
     *(u32x4 HCA_LDS*)(c.vb[0] + o) = u32x4{};
     *(u32x4 HCA_LDS*)(c.vb[1] + o) = u32x4{};
   }
-
-  // Q^T fragments of the wave's 32 rows (heads 32hg .. +31 of position t):
-  // lane l holds row l%32, elements 16k + 8(l/32) .. +7
-  const bf16* qbase = (const bf16*)a.q + ((size_t)qrow * a.hq + kvh * G) * D;
-  bf16x8 qf[DSTEPS];
-  {
-    const bf16* qrow = qbase + (size_t)(32 * hg + (lane & 31)) * D + 8 * (lane >> 5);
-#pragma unroll
-    for (int k = 0; k < DSTEPS; ++k) qf[k] = *(const bf16x8*)(qrow + 16 * k);
-  }
-  // the epilogue's inputs: their latency overlaps the Q loads, and the
-  // pass's barriers order the LDS writes before their use
-  if constexpr (EPI) load_epilogue_inputs(a, epi_s, kvh, start + (t0 - p0), t1_ok);
   PState st;
   attend_pair<LO>(c, qf, st);
   bf16* obase = (bf16*)a.o + ((size_t)qrow * a.hq + kvh * G) * D + hg * 256;

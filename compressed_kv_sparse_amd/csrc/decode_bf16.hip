@@ -296,11 +296,10 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a, int t
 }
 
 // Merge of the split partials: O = sum_s 2^(m_s - M) l_s O_s / sum_s 2^(m_s - M) l_s
-// with M = max_s m_s, splits taken in order (deterministic).  One workgroup
-// of 256 threads merges two heads of one (sequence, KV head) unit; each
-// thread owns 4 columns of one head.  Splits are read kMergeBatch at a time
-// with all loads of a batch in flight together; the merge of unit u runs on
-// XCD u % 8 like its split workgroups, whose L2 may still hold the partials.
+// with M = max_s m_s, splits taken in order (deterministic).  Splits are
+// read a batch at a time with all loads of a batch in flight together; a
+// running M rescales what earlier batches added (exact when one batch
+// covers all splits).
 constexpr int kMergeBatch = 8;
 
 // Merged O (normalised) of head r, columns c .. c+3 of one unit.
@@ -346,22 +345,75 @@ __device__ __forceinline__ f32x4 merge_cols(const WsLayout& w, int unit, int r, 
   return n0 * (1.f / den);
 }
 
+// Merged O (normalised) of head r, columns c .. c+7 of one unit, splits
+// read NB at a time (NB = 4 when the unit has at most 4 splits, so that no
+// load repeats a split); the arithmetic is merge_cols', column by column.
+template <int NB>
+__device__ __forceinline__ void merge_cols8(const WsLayout& w, int unit, int r, int c, int nsplit,
+                                            int max_splits, float (&out)[8]) {
+  const float* mrow = w.m + (size_t)unit * max_splits * G + r;
+  const float* lrow = w.l + (size_t)unit * max_splits * G + r;
+  const bf16* orow = w.o + ((size_t)unit * max_splits * G + r) * D + c;
+  float M = -INFINITY, den = 0.f, n0[8] = {};
+  for (int s0 = 0; s0 < nsplit; s0 += NB) {
+    float mv[NB], lv[NB];
+    bf16x8 ov[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int sp = min(s0 + j, nsplit - 1);  // repeats of the last split are dropped below
+      mv[j] = mrow[(size_t)sp * G];
+      lv[j] = lrow[(size_t)sp * G];
+      ov[j] = *(const bf16x8*)(orow + (size_t)sp * G * D);
+    }
+    float Mb = M;
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      if (s0 + j < nsplit) Mb = fmaxf(Mb, mv[j]);
+    if (Mb != M) {  // rescale what earlier batches added
+      const float f = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mb);
+      den *= f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) n0[i] *= f;
+      M = Mb;
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (s0 + j >= nsplit) break;
+      const float wgt = __builtin_amdgcn_exp2f(mv[j] - M) * lv[j];
+      den += wgt;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) n0[i] = __builtin_fmaf(wgt, (float)ov[j][i], n0[i]);
+    }
+  }
+  const float inv = 1.f / den;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) out[i] = n0[i] * inv;
+}
+
+// Merge without epilogue: one workgroup of 4 wavefronts merges 4 heads of
+// one (sequence, KV head) unit, wavefront = head, lane l = columns 8l ..
+// 8l+7 (16-byte loads and stores).  The merge of unit u runs on XCD u % 8
+// like its split workgroups, whose L2 may still hold the partials.
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int tps, int max_splits) {
   const int wg = (int)blockIdx.x;
-  const int unit = (wg & 7) + 8 * ((wg >> 3) / (G / 2));  // b * Hkv + kvh
+  const int unit = (wg & 7) + 8 * ((wg >> 3) / (G / 4));  // b * Hkv + kvh
   if (unit >= a.batch * a.hkv) return;
   const int b = unit / a.hkv, kvh = unit % a.hkv;
-  const int r = ((wg >> 3) % (G / 2)) * 2 + (threadIdx.x >> 7);  // head within the KV group
-  const int c = (threadIdx.x & 127) * 4;
+  const int r = ((wg >> 3) % (G / 4)) * 4 + (threadIdx.x >> 6);  // head within the KV group
+  const int c = (threadIdx.x & 63) * 8;
   const int L = a.seqlens[b];
   const int nkeys = L / kBlock + min(a.window, L);
   const int nsplit = ((nkeys + NT - 1) / NT + tps - 1) / tps;
   const WsLayout w = ws_layout(a.ws, a.batch, a.hkv, max_splits);
-  const f32x4 n = merge_cols(w, unit, r, c, nsplit, max_splits);
-  bf16x4 v;
+  float n[8];
+  if (nsplit <= 4)
+    merge_cols8<4>(w, unit, r, c, nsplit, max_splits, n);
+  else
+    merge_cols8<kMergeBatch>(w, unit, r, c, nsplit, max_splits, n);
+  bf16x8 v;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = (bf16)n[i];
-  *(bf16x4*)((bf16*)a.o + ((size_t)b * a.hq + kvh * G + r) * D + c) = v;
+  for (int i = 0; i < 8; ++i) v[i] = (bf16)n[i];
+  *(bf16x8*)((bf16*)a.o + ((size_t)b * a.hq + kvh * G + r) * D + c) = v;
 }
 
 // Merge with the attention epilogue (release blog "ERNIE 5.5 Flash Base",
@@ -457,7 +509,7 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
   if (a.gate || a.mix_u)
     decode_merge_epi_kernel<<<(unsigned)(8 * (D / 32) * groups), 256, 0, s>>>(a, p.tiles_per_split, p.max_splits);
   else
-    decode_merge_kernel<<<(unsigned)(8 * (G / 2) * groups), 256, 0, s>>>(a, p.tiles_per_split, p.max_splits);
+    decode_merge_kernel<<<(unsigned)(8 * (G / 4) * groups), 256, 0, s>>>(a, p.tiles_per_split, p.max_splits);
   return hipGetLastError();
 }
 

@@ -632,9 +632,11 @@ def run_decode(torch, hca, c, steps, warmup, clock, min_warm_s, n_sets=4, epilog
 
 def measure_peaks(torch, hca):
     """Ceilings this part reaches in this run: a streaming read of a 2 GiB
-    buffer (HBM) and a loop of bf16 32x32x16 matrix-core products on register
-    operands, one and two wavefronts per SIMD (the clock of the MFMA loop
-    comes from the shader-clock and 100 MHz counters).  Fills MEASURED."""
+    buffer (HBM) into registers and through LDS with direct loads (the
+    better one is the HBM ceiling), a loop of bf16 32x32x16 matrix-core
+    products on register operands, one and two wavefronts per SIMD (the
+    clock of the MFMA loop comes from the shader-clock and 100 MHz
+    counters), and LDS reads.  Fills MEASURED."""
     dev = "cuda"
     nbytes = 2 << 30
     buf = torch.zeros(nbytes // 4, dtype=torch.int32, device=dev)
@@ -644,9 +646,21 @@ def measure_peaks(torch, hca):
         clock.run("stream" if i >= 2 else "warm", lambda: hca.hca_probe_stream_read(buf, 2048, sink=sink))
     torch.cuda.synchronize()
     _, t_med, _ = clock.stats_ms("stream")
-    hbm = nbytes / (t_med * 1e-3) / 1e9
+    hbm_vgpr = nbytes / (t_med * 1e-3) / 1e9
+    # the same bytes through LDS with the attention kernels' direct loads
+    # (one workgroup per CU); the buffer is rewritten between runs so that
+    # no run starts from the last-level cache
+    lds_bytes = nbytes // hca.PROBE_LDS_TILE * hca.PROBE_LDS_TILE
+    for i in range(6):
+        buf.fill_(i)
+        clock.run("stream_lds" if i >= 1 else "warm", lambda: hca.hca_probe_stream_lds(buf, 256, sink=sink))
+    torch.cuda.synchronize()
+    _, t_med, _ = clock.stats_ms("stream_lds")
+    hbm_lds = lds_bytes / (t_med * 1e-3) / 1e9
+    hbm = max(hbm_vgpr, hbm_lds)
     del buf, sink
-    out = {"hbm_stream_read_gbs": round(hbm, 1), "hbm_stream_bytes": nbytes}
+    out = {"hbm_stream_read_gbs": round(hbm_vgpr, 1), "hbm_stream_lds_gbs": round(hbm_lds, 1),
+           "hbm_stream_bytes": nbytes, "hbm_gbs": round(hbm, 1)}
     best = 0.0
     for wps in (1, 2):
         grid = 256 * wps

@@ -31,6 +31,8 @@ from .hca import (  # noqa: F401
     hca_probe_lds_read,
     hca_probe_mfma_bf16,
     hca_probe_stream_read,
+    hca_probe_stream_lds,
+    PROBE_LDS_TILE,
     hca_ring_append,
     hca_status_string,
     hca_version,

@@ -139,6 +139,12 @@ hca_status hca_probe_stream_read(const void* buf, size_t bytes, uint32_t* sink, 
   return from_hip(hca::launch_probe_stream_read(buf, bytes, (unsigned*)sink, grid, (hipStream_t)stream));
 }
 
+hca_status hca_probe_stream_lds(const void* buf, size_t bytes, uint32_t* sink, int32_t grid, void* stream) {
+  if (!buf || !sink) return HCA_ERR_NULL;
+  if (hca::probe_stream_lds_bytes(bytes) == 0 || grid < 1 || grid > 65536) return HCA_ERR_SHAPE;
+  return from_hip(hca::launch_probe_stream_lds(buf, bytes, (unsigned*)sink, grid, (hipStream_t)stream));
+}
+
 hca_status hca_probe_mfma_bf16(int32_t iters, int32_t grid, float* sink, void* stream) {
   if (!sink) return HCA_ERR_NULL;
   if (iters < 1 || grid < 1 || grid > 65536) return HCA_ERR_SHAPE;

@@ -213,6 +213,9 @@ hipError_t launch_dsa_decode(DsaArgs a, hipStream_t s);
 // 8-byte reads).  Each writes 4 values per workgroup to `sink` (the MFMA
 // probe first writes its clock readings to sink[0..3]).
 hipError_t launch_probe_stream_read(const void* buf, size_t bytes, unsigned* sink, int grid, hipStream_t s);
+// The LDS stream reads whole 48 KiB tiles: the bytes it reads of `bytes`.
+size_t probe_stream_lds_bytes(size_t bytes);
+hipError_t launch_probe_stream_lds(const void* buf, size_t bytes, unsigned* sink, int grid, hipStream_t s);
 hipError_t launch_probe_mfma(int iters, int grid, float* sink, hipStream_t s);
 hipError_t launch_probe_lds(int mode, int iters, int grid, unsigned* sink, hipStream_t s);
 

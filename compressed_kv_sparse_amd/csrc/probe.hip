@@ -6,6 +6,9 @@
 //
 //  * stream read: every byte of a buffer read once with 16-byte
 //    non-temporal loads, four in flight per thread.
+//  * stream through LDS: every byte read once by direct buffer->LDS loads
+//    (one 1 KiB row per wave instruction, the attention kernels' tile path),
+//    48 KiB tiles with two in flight per workgroup, one workgroup per CU.
 //  * matrix-core loop: v_mfma_f32_32x32x16_bf16 on register operands, four
 //    independent accumulators per wavefront; one wavefront of the first
 //    workgroup also reads the shader-clock and fixed-rate (100 MHz) counters
@@ -13,7 +16,7 @@
 //  * LDS reads: 16-byte reads (one 1 KiB row per instruction) or the
 //    transposed 8-byte reads (ds_read_b64_tr_b16) in the lane pattern the
 //    attention kernels use for V^T fragments (1088-byte rows).
-#include "hca_internal.h"
+#include "bf16_tiles.h"
 
 namespace hca {
 namespace {
@@ -80,6 +83,46 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, float* sink)
   if (lane == 0) sink[4 + blockIdx.x * 4 + (threadIdx.x >> 6)] = s;
 }
 
+constexpr int kDmaTile = 49152;  // bytes per tile of the LDS stream (48 rows of 1 KiB)
+constexpr int kDmaDepth = 2;     // tiles in flight per workgroup
+
+// Workgroup g streams tiles g, g + grid, ... of the buffer through
+// kDmaDepth + 1 LDS slots.  Loads issued past the workgroup's last tile use
+// an empty range (they read zeros without touching memory), so that every
+// wait keeps the same count.
+__global__ __launch_bounds__(256, 1) void probe_stream_lds_kernel(const char* src, size_t ntiles, unsigned* sink) {
+  __shared__ __attribute__((aligned(16))) char buf[(kDmaDepth + 1) * kDmaTile];
+  constexpr int kRows = kDmaTile / 1024 / 4;  // rows per wavefront per tile
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const size_t grid = gridDim.x;
+  const size_t mine = ntiles > blockIdx.x ? (ntiles - blockIdx.x + grid - 1) / grid : 0;
+  auto issue = [&](size_t it) {
+    const bool ok = it < mine;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(src) + (ok ? (blockIdx.x + it * grid) * kDmaTile : 0), (short)0, ok ? kDmaTile : 0,
+        0x00020000);
+    char HCA_LDS* dst = (char HCA_LDS*)buf + (it % (kDmaDepth + 1)) * kDmaTile;
+#pragma unroll
+    for (int rr = 0; rr < kRows; ++rr) {
+      const int row = wave * kRows + rr;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void HCA_LDS*)(dst + row * 1024), 16, row * 1024 + lane * 16, 0,
+                                               0, kStreamed);
+    }
+  };
+#pragma unroll
+  for (int it = 0; it < kDmaDepth; ++it) issue(it);
+  unsigned x = 0;
+  for (size_t it = 0; it < mine; ++it) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kDmaDepth - 1) * kRows) : "memory");  // tile `it` has landed
+    __syncthreads();  // ... in every wavefront; the slot of tile it - 1 is free
+    issue(it + kDmaDepth);
+    x ^= *(const unsigned HCA_LDS*)((const char HCA_LDS*)buf + (it % (kDmaDepth + 1)) * kDmaTile + threadIdx.x * 4);
+  }
+  wait_vm_all();
+  for (int o = 32; o > 0; o >>= 1) x ^= __shfl_xor(x, o);
+  if (lane == 0) sink[blockIdx.x * 4 + wave] = x;
+}
+
 constexpr int kProbeRow = 1088;            // bytes per LDS row (the V tile stride)
 constexpr int kProbeRows = 32;             // one 32-key tile
 constexpr int kProbeBytes = kProbeRows * kProbeRow;
@@ -122,6 +165,13 @@ __global__ __launch_bounds__(256) void probe_lds_kernel(int mode, int iters, uns
 
 hipError_t launch_probe_stream_read(const void* buf, size_t bytes, unsigned* sink, int grid, hipStream_t s) {
   probe_stream_read_kernel<<<grid, 256, 0, s>>>((const u32x4_p*)buf, bytes / 16, sink);
+  return hipGetLastError();
+}
+
+size_t probe_stream_lds_bytes(size_t bytes) { return bytes / kDmaTile * kDmaTile; }
+
+hipError_t launch_probe_stream_lds(const void* buf, size_t bytes, unsigned* sink, int grid, hipStream_t s) {
+  probe_stream_lds_kernel<<<grid, 256, 0, s>>>((const char*)buf, bytes / kDmaTile, sink);
   return hipGetLastError();
 }
 

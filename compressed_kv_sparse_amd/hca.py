@@ -25,7 +25,7 @@ EXPORTS = ("hca_compress", "hca_attend_prefill", "hca_decode_workspace_bytes",
            "hca_attend_decode_gated_vha", "hca_attend_prefill_chunk_gated_vha",
            "hca_attend_prefill_lse", "hca_attend_prefill_backward_workspace_bytes", "hca_attend_prefill_backward",
            "hca_dsa_decode_workspace_bytes", "hca_dsa_decode",
-           "hca_probe_stream_read", "hca_probe_mfma_bf16", "hca_probe_lds_read", "hca_attend_decode_noalloc",
+           "hca_probe_stream_read", "hca_probe_stream_lds", "hca_probe_mfma_bf16", "hca_probe_lds_read", "hca_attend_decode_noalloc",
            "hca_status_string", "hca_version")
 
 
@@ -114,6 +114,8 @@ def library() -> ctypes.CDLL:
     lib.hca_attend_decode_noalloc.restype = ctypes.c_int
     lib.hca_probe_stream_read.argtypes = [vp, sz, vp, i32, vp]
     lib.hca_probe_stream_read.restype = ctypes.c_int
+    lib.hca_probe_stream_lds.argtypes = [vp, sz, vp, i32, vp]
+    lib.hca_probe_stream_lds.restype = ctypes.c_int
     lib.hca_probe_mfma_bf16.argtypes = [i32, i32, vp, vp]
     lib.hca_probe_mfma_bf16.restype = ctypes.c_int
     lib.hca_probe_lds_read.argtypes = [i32, i32, i32, vp, vp]
@@ -419,6 +421,20 @@ def hca_probe_stream_read(buf, grid: int, sink=None, stream=None):
     st = library().hca_probe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), int(grid),
                                          _stream(stream))
     _check("hca_probe_stream_read", st)
+    return sink
+
+
+PROBE_LDS_TILE = 49152  # bytes per tile of hca_probe_stream_lds
+
+
+def hca_probe_stream_lds(buf, grid: int, sink=None, stream=None):
+    """Read the whole 48 KiB tiles of `buf` once through LDS (direct
+    buffer->LDS loads); returns the sink."""
+    if sink is None:
+        sink = torch.empty(4 * grid, dtype=torch.int32, device=buf.device)
+    st = library().hca_probe_stream_lds(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), int(grid),
+                                        _stream(stream))
+    _check("hca_probe_stream_lds", st)
     return sink
 
 

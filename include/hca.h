@@ -448,6 +448,11 @@ HCA_API hca_status hca_dsa_decode(int32_t batch, int32_t max_seqlen, int32_t top
  * hca_probe_stream_read - reads every byte of `buf` (device, `bytes` a
  *   multiple of 16) once with 16-byte non-temporal loads; `grid` workgroups
  *   of 256 threads; sink: device uint32 [4 * grid].
+ * hca_probe_stream_lds - reads the first floor(bytes / 49152) 48 KiB tiles of
+ *   `buf` once through LDS with direct buffer->LDS loads (the attention
+ *   kernels' key-tile path), two tiles in flight per workgroup of 256
+ *   threads (144 KiB of LDS, so one workgroup per CU); `grid` workgroups;
+ *   sink: device uint32 [4 * grid]; bytes < 49152 is HCA_ERR_SHAPE.
  * hca_probe_mfma_bf16 - each of `grid` workgroups (4 wavefronts) runs
  *   `iters` x 4 independent v_mfma_f32_32x32x16_bf16 per wavefront
  *   (32768 flops each); sink: device float [4 + 4 * grid].  sink[0] and
@@ -462,6 +467,7 @@ HCA_API hca_status hca_dsa_decode(int32_t batch, int32_t max_seqlen, int32_t top
  * range (grid 1 .. 65536, iters >= 1), HCA_ERR_HIP if the launch fails.
  */
 HCA_API hca_status hca_probe_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t grid, void* stream);
+HCA_API hca_status hca_probe_stream_lds(const void* buf, size_t bytes, uint32_t* sink, int32_t grid, void* stream);
 HCA_API hca_status hca_probe_mfma_bf16(int32_t iters, int32_t grid, float* sink, void* stream);
 HCA_API hca_status hca_probe_lds_read(int32_t mode, int32_t iters, int32_t grid, uint32_t* sink, void* stream);
 

@@ -318,6 +318,10 @@ def test_probe_validation(lib):
     assert lib.hca_probe_stream_read(DUMMY, 0, DUMMY, 64, None) == ERR_SHAPE
     assert lib.hca_probe_stream_read(DUMMY, 1000, DUMMY, 64, None) == ERR_SHAPE  # not a multiple of 16
     assert lib.hca_probe_stream_read(DUMMY, 1 << 20, DUMMY, 0, None) == ERR_SHAPE
+    assert lib.hca_probe_stream_lds(NULL, 1 << 20, DUMMY, 64, None) == ERR_NULL
+    assert lib.hca_probe_stream_lds(DUMMY, 1 << 20, NULL, 64, None) == ERR_NULL
+    assert lib.hca_probe_stream_lds(DUMMY, 49151, DUMMY, 64, None) == ERR_SHAPE  # not one whole tile
+    assert lib.hca_probe_stream_lds(DUMMY, 1 << 20, DUMMY, 0, None) == ERR_SHAPE
     assert lib.hca_probe_mfma_bf16(100, 256, NULL, None) == ERR_NULL
     assert lib.hca_probe_mfma_bf16(0, 256, DUMMY, None) == ERR_SHAPE
     assert lib.hca_probe_mfma_bf16(100, 70000, DUMMY, None) == ERR_SHAPE

@@ -302,52 +302,9 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a, int t
 // covers all splits).
 constexpr int kMergeBatch = 8;
 
-// Merged O (normalised) of head r, columns c .. c+3 of one unit.
-__device__ __forceinline__ f32x4 merge_cols(const WsLayout& w, int unit, int r, int c, int nsplit,
-                                           int max_splits) {
-  const float* mrow = w.m + (size_t)unit * max_splits * G + r;
-  const float* lrow = w.l + (size_t)unit * max_splits * G + r;
-  const bf16* orow = w.o + ((size_t)unit * max_splits * G + r) * D + c;
-  // running M with rescaling between batches (exact when one batch covers
-  // all splits, as in the common case)
-  float M = -INFINITY, den = 0.f;
-  f32x4 n0 = {};
-  for (int s0 = 0; s0 < nsplit; s0 += kMergeBatch) {
-    float mv[kMergeBatch], lv[kMergeBatch];
-    f32x4 ov[kMergeBatch];
-#pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) {
-      const int sp = min(s0 + j, nsplit - 1);  // repeats of the last split are dropped below
-      mv[j] = mrow[(size_t)sp * G];
-      lv[j] = lrow[(size_t)sp * G];
-      const bf16x4 ob = *(const bf16x4*)(orow + (size_t)sp * G * D);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ov[j][i] = (float)ob[i];
-    }
-    float Mb = M;
-#pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j)
-      if (s0 + j < nsplit) Mb = fmaxf(Mb, mv[j]);
-    if (Mb != M) {  // rescale what earlier batches added
-      const float f = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mb);
-      den *= f;
-      n0 *= f;
-      M = Mb;
-    }
-#pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) {
-      if (s0 + j >= nsplit) break;
-      const float wgt = __builtin_amdgcn_exp2f(mv[j] - M) * lv[j];
-      den += wgt;
-      n0 += wgt * ov[j];
-    }
-  }
-  return n0 * (1.f / den);
-}
-
 // Merged O (normalised) of head r, columns c .. c+7 of one unit, splits
 // read NB at a time (NB = 4 when the unit has at most 4 splits, so that no
-// load repeats a split); the arithmetic is merge_cols', column by column.
+// load repeats a split).
 template <int NB>
 __device__ __forceinline__ void merge_cols8(const WsLayout& w, int unit, int r, int c, int nsplit,
                                             int max_splits, float (&out)[8]) {
@@ -439,22 +396,33 @@ __global__ __launch_bounds__(256) void decode_merge_epi_kernel(DecodeArgs a, int
   const int nsplit = ((nkeys + NT - 1) / NT + tps - 1) / tps;
   const WsLayout w = ws_layout(a.ws, a.batch, a.hkv, max_splits);
   const int c0 = 32 * slice + cq;
-  float y[8];
-  {
-    const f32x4 m0 = merge_cols(w, unit, hr, c0, nsplit, max_splits);
-    const f32x4 m1 = merge_cols(w, unit, hr, c0 + 4, nsplit, max_splits);
+  // the epilogue's inputs are loaded first, so that their latency overlaps
+  // the merge's loads: U of this thread's head (rank <= 32), this thread's
+  // share of V (G x rank <= 8 per thread) and the gate logit
+  const int rank = a.mix_u ? a.mix_rank : 0;
+  float u_r[32], vv[8];
+  if (rank) {
+    const float* ug = a.mix_u + ((size_t)kvh * G + hr) * rank;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      y[i] = m0[i];
-      y[4 + i] = m1[i];
-    }
+    for (int rk = 0; rk < 32; ++rk) u_r[rk] = rk < rank ? ug[rk] : 0.f;
+    const float* vg = a.mix_v + (size_t)kvh * G * rank;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vv[j] = tid + 256 * j < G * rank ? vg[tid + 256 * j] : 0.f;
   }
-  if (a.mix_u) {
-    const int rank = a.mix_rank;
+  const float glogit = a.gate ? a.gate[(size_t)b * a.hq + kvh * G + hr] : 0.f;
+  float y[8];
+  if (nsplit <= 4)
+    merge_cols8<4>(w, unit, hr, c0, nsplit, max_splits, y);
+  else
+    merge_cols8<kMergeBatch>(w, unit, hr, c0, nsplit, max_splits, y);
+  if (rank) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) o_s[hr][cq + i] = y[i];
-    const float* vg = a.mix_v + (size_t)kvh * G * rank;
-    for (int e = tid; e < G * rank; e += 256) v_s[e / rank][e % rank] = vg[e];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = tid + 256 * j;
+      if (e < G * rank) v_s[e / rank][e % rank] = vv[j];
+    }
     __syncthreads();
     for (int e = tid; e < rank * 32; e += 256) {  // Z[rk][c] = sum_h V[h][rk] O[h][c]
       const int rk = e >> 5, c = e & 31;
@@ -464,14 +432,15 @@ __global__ __launch_bounds__(256) void decode_merge_epi_kernel(DecodeArgs a, int
       z_s[rk][c] = z;
     }
     __syncthreads();
-    const float* ug = a.mix_u + ((size_t)kvh * G + hr) * rank;
-    for (int rk = 0; rk < rank; ++rk) {
-      const float u = ug[rk];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) y[i] = fmaf(u, z_s[rk][cq + i], y[i]);
+    for (int rk = 0; rk < 32; ++rk) {
+      if (rk < rank) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = fmaf(u_r[rk], z_s[rk][cq + i], y[i]);
+      }
     }
   }
-  const float gsc = a.gate ? 1.f / (1.f + __expf(-a.gate[(size_t)b * a.hq + kvh * G + hr])) : 1.f;
+  const float gsc = a.gate ? 1.f / (1.f + __expf(-glogit)) : 1.f;
   bf16x8 v;
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = (bf16)(y[i] * gsc);

@@ -184,14 +184,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BackwardArgs a) {
   for (int ct = 0; ct < DQ_TILES; ++ct) st.acc[ct] = f32x4{};
   wait_vm_all();
   __syncthreads();
-  for (int tile = 0; tile < ntiles; tile += 2) {
-    if (tile + 1 < ntiles) issue_tile<4>(ks, tile + 1, kv1, kv1 + NT * KSTR, wave, lane);
-    dq_tile(kv0, kv0 + NT * KSTR, qf, df, st, sc2, lse2, dd, lane, tile, ks.nkeys);
-    wait_vm_all();
-    __syncthreads();
-    if (tile + 1 >= ntiles) break;
-    if (tile + 2 < ntiles) issue_tile<4>(ks, tile + 2, kv0, kv0 + NT * KSTR, wave, lane);
-    dq_tile(kv1, kv1 + NT * KSTR, qf, df, st, sc2, lse2, dd, lane, tile + 1, ks.nkeys);
+  // One tile per iteration with the buffers chosen at run time: a loop
+  // unrolled by two (one copy per buffer) made the register allocator keep
+  // both copies' values, spill the Q and dO fragments, and reload them
+  // behind waits that also waited for the next tile's loads.
+#pragma unroll 1
+  for (int tile = 0; tile < ntiles; ++tile) {
+    char HCA_LDS* cur = (tile & 1) ? kv1 : kv0;
+    char HCA_LDS* nxt = (tile & 1) ? kv0 : kv1;
+    if (tile + 1 < ntiles) issue_tile<4>(ks, tile + 1, nxt, nxt + NT * KSTR, wave, lane);
+    dq_tile(cur, cur + NT * KSTR, qf, df, st, sc2, lse2, dd, lane, tile, ks.nkeys);
     wait_vm_all();
     __syncthreads();
   }

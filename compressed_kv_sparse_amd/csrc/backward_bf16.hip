@@ -28,6 +28,7 @@
 //                   to bf16 and writes the block's terms of g.
 //   bwd_dw_kernel   sums g over all blocks and applies the softmax Jacobian.
 #include <algorithm>
+#include <type_traits>
 
 #include "bf16_tiles.h"
 
@@ -254,8 +255,14 @@ __device__ __forceinline__ void stage_rows(const BackwardArgs& a, size_t tok, in
 }
 
 __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BackwardArgs a, BackwardPlan pl) {
-  __shared__ __attribute__((aligned(16))) char st_s[2][2 * QSTAGE];
-  __shared__ __attribute__((aligned(16))) float rs_s[2][128];
+  // two staging buffers as distinct arrays: each step names its buffers at
+  // compile time, so the compiler can tell that a step's LDS reads do not
+  // touch the rows that the next step's direct loads are writing (with one
+  // array indexed at run time it made every step wait for those loads)
+  __shared__ __attribute__((aligned(16))) char st0_s[2 * QSTAGE];
+  __shared__ __attribute__((aligned(16))) char st1_s[2 * QSTAGE];
+  __shared__ __attribute__((aligned(16))) float rs0_s[128];
+  __shared__ __attribute__((aligned(16))) float rs1_s[128];
 
   const int b = blockIdx.y, kvh = blockIdx.z;
   const int start = a.cu_seqlens[b];
@@ -307,20 +314,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BackwardArgs a, Backwar
 
   const float sc2 = a.scale * kLog2e;
   const int nsteps = 2 * (t_end - t_begin);
-  char HCA_LDS* const buf0 = (char HCA_LDS*)&st_s[0][0];
-  float HCA_LDS* const rs0 = (float HCA_LDS*)&rs_s[0][0];
-  stage_rows(a, (size_t)start + t_begin, kvh, 0, buf0, rs0, wave, lane);
+  char HCA_LDS* const st0 = (char HCA_LDS*)st0_s;
+  char HCA_LDS* const st1 = (char HCA_LDS*)st1_s;
+  float HCA_LDS* const rs0 = (float HCA_LDS*)rs0_s;
+  float HCA_LDS* const rs1 = (float HCA_LDS*)rs1_s;
+  stage_rows(a, (size_t)start + t_begin, kvh, 0, st0, rs0, wave, lane);
   wait_vm_all();
   __syncthreads();
   const int tro = (4 * g + (r >> 2)) * BSTR + 8 * (lane & 3);
-  for (int i = 0; i < nsteps; ++i) {
-    const int t = t_begin + (i >> 1), hh = i & 1;
+  // step i: position t_begin + i/2, head half i%2, staged in buffer i%2
+  auto step = [&](int i, auto parity) {
+    constexpr int P = decltype(parity)::value;
+    const int t = t_begin + (i >> 1);
     if (i + 1 < nsteps)
-      stage_rows(a, (size_t)start + t_begin + ((i + 1) >> 1), kvh, (i + 1) & 1, buf0 + ((i + 1) & 1) * 2 * QSTAGE,
-                 rs0 + ((i + 1) & 1) * 128, wave, lane);
-    const char HCA_LDS* qs = buf0 + (i & 1) * 2 * QSTAGE;
+      stage_rows(a, (size_t)start + t_begin + ((i + 1) >> 1), kvh, 1 - P, P ? st0 : st1, P ? rs0 : rs1, wave, lane);
+    const char HCA_LDS* qs = P ? st1 : st0;
     const char HCA_LDS* ds = qs + QSTAGE;
-    const float HCA_LDS* rs = rs0 + (i & 1) * 128;
+    const float HCA_LDS* rs = P ? rs1 : rs0;
     // S, dP of the 32 rows and the wave's 16 keys
     f32x4 sx[2] = {}, px[2] = {};
 #pragma unroll
@@ -358,6 +368,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BackwardArgs a, Backwar
     }
     wait_vm_all();
     __syncthreads();
+  };
+  // nsteps is even (two head halves per position)
+  for (int i = 0; i < nsteps; i += 2) {
+    step(i, std::integral_constant<int, 0>{});
+    step(i + 1, std::integral_constant<int, 1>{});
   }
 
   // this item's partial: keys 16w + 4g + i, columns 16u + l%16

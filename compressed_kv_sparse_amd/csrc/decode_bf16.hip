@@ -377,37 +377,41 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int tps
 // section 2.1, last paragraph: per-head output gate and Virtual Head
 // Attention, a cross-head low-rank mixing with identity skip):
 // y[h] = sigmoid(gate[b, h]) (O[h] + sum_r U[h, r] sum_h' V[h', r] O[h']).
-// One workgroup covers all 64 heads of a unit for 32 columns (the mixing
-// runs across heads); thread t merges head t/4, columns 8(t%4) .. +7, the
-// merged tile goes through LDS, Z = V^T O and U Z are fp32 dot products.
-// Grid 8 x 16 column slices x unit groups, XCD-aware like the split kernel.
-__global__ __launch_bounds__(256) void decode_merge_epi_kernel(DecodeArgs a, int tps, int max_splits) {
-  __shared__ float o_s[G][33];
-  __shared__ float z_s[32][33];
+// One workgroup of 512 threads covers all 64 heads of a unit for 64
+// columns (the mixing runs across heads); thread t merges head t/8, columns
+// 8(t%8) .. +7 (eight lanes read a 128-byte row segment), the merged tile
+// goes through LDS, Z = V^T O and U Z are fp32 dot products.  Grid 8 x 8
+// column slices x unit groups, XCD-aware like the split kernel.
+constexpr int kEpiCols = 64;  // columns per workgroup of the epilogue merge (128-byte row segments)
+__global__ __launch_bounds__(512) void decode_merge_epi_kernel(DecodeArgs a, int tps, int max_splits) {
+  // rows padded to a multiple of 16 bytes: the tiles are read and written
+  // four floats at a time
+  __shared__ __attribute__((aligned(16))) float o_s[G][kEpiCols + 4];
+  __shared__ __attribute__((aligned(16))) float z_s[32][kEpiCols + 4];
   __shared__ float v_s[G][33];  // V of the unit's KV head, [head][rank]
   const int wg = (int)blockIdx.x;
-  const int unit = (wg & 7) + 8 * ((wg >> 3) / (D / 32));
+  const int unit = (wg & 7) + 8 * ((wg >> 3) / (D / kEpiCols));
   if (unit >= a.batch * a.hkv) return;
-  const int slice = (wg >> 3) % (D / 32);
+  const int slice = (wg >> 3) % (D / kEpiCols);
   const int b = unit / a.hkv, kvh = unit % a.hkv;
-  const int tid = threadIdx.x, hr = tid >> 2, cq = (tid & 3) * 8;
+  const int tid = threadIdx.x, hr = tid >> 3, cq = (tid & 7) * 8;
   const int L = a.seqlens[b];
   const int nkeys = L / kBlock + min(a.window, L);
   const int nsplit = ((nkeys + NT - 1) / NT + tps - 1) / tps;
   const WsLayout w = ws_layout(a.ws, a.batch, a.hkv, max_splits);
-  const int c0 = 32 * slice + cq;
+  const int c0 = kEpiCols * slice + cq;
   // the epilogue's inputs are loaded first, so that their latency overlaps
   // the merge's loads: U of this thread's head (rank <= 32), this thread's
-  // share of V (G x rank <= 8 per thread) and the gate logit
+  // share of V (G x rank <= 4 per thread) and the gate logit
   const int rank = a.mix_u ? a.mix_rank : 0;
-  float u_r[32], vv[8];
+  float u_r[32], vv[4];
   if (rank) {
     const float* ug = a.mix_u + ((size_t)kvh * G + hr) * rank;
 #pragma unroll
     for (int rk = 0; rk < 32; ++rk) u_r[rk] = rk < rank ? ug[rk] : 0.f;
     const float* vg = a.mix_v + (size_t)kvh * G * rank;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) vv[j] = tid + 256 * j < G * rank ? vg[tid + 256 * j] : 0.f;
+    for (int j = 0; j < 4; ++j) vv[j] = tid + 512 * j < G * rank ? vg[tid + 512 * j] : 0.f;
   }
   const float glogit = a.gate ? a.gate[(size_t)b * a.hq + kvh * G + hr] : 0.f;
   float y[8];
@@ -416,27 +420,36 @@ __global__ __launch_bounds__(256) void decode_merge_epi_kernel(DecodeArgs a, int
   else
     merge_cols8<kMergeBatch>(w, unit, hr, c0, nsplit, max_splits, y);
   if (rank) {
+    *(f32x4*)&o_s[hr][cq] = f32x4{y[0], y[1], y[2], y[3]};
+    *(f32x4*)&o_s[hr][cq + 4] = f32x4{y[4], y[5], y[6], y[7]};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o_s[hr][cq + i] = y[i];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int e = tid + 256 * j;
+    for (int j = 0; j < 4; ++j) {
+      const int e = tid + 512 * j;
       if (e < G * rank) v_s[e / rank][e % rank] = vv[j];
     }
     __syncthreads();
-    for (int e = tid; e < rank * 32; e += 256) {  // Z[rk][c] = sum_h V[h][rk] O[h][c]
-      const int rk = e >> 5, c = e & 31;
-      float z = 0.f;
+    for (int e = tid; e < rank * (kEpiCols / 4); e += 512) {  // Z[rk][c] = sum_h V[h][rk] O[h][c], 4 columns
+      const int rk = e / (kEpiCols / 4), c = (e % (kEpiCols / 4)) * 4;
+      f32x4 z = {};
 #pragma unroll 16
-      for (int h = 0; h < G; ++h) z = fmaf(v_s[h][rk], o_s[h][c], z);
-      z_s[rk][c] = z;
+      for (int h = 0; h < G; ++h) {
+        const float vh = v_s[h][rk];
+        const f32x4 oh = *(const f32x4*)&o_s[h][c];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[i] = fmaf(vh, oh[i], z[i]);
+      }
+      *(f32x4*)&z_s[rk][c] = z;
     }
     __syncthreads();
 #pragma unroll
     for (int rk = 0; rk < 32; ++rk) {
       if (rk < rank) {
+        const f32x4 z0 = *(const f32x4*)&z_s[rk][cq], z1 = *(const f32x4*)&z_s[rk][cq + 4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) y[i] = fmaf(u_r[rk], z_s[rk][cq + i], y[i]);
+        for (int i = 0; i < 4; ++i) {
+          y[i] = fmaf(u_r[rk], z0[i], y[i]);
+          y[4 + i] = fmaf(u_r[rk], z1[i], y[4 + i]);
+        }
       }
     }
   }
@@ -476,7 +489,7 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.gate || a.mix_u)
-    decode_merge_epi_kernel<<<(unsigned)(8 * (D / 32) * groups), 256, 0, s>>>(a, p.tiles_per_split, p.max_splits);
+    decode_merge_epi_kernel<<<(unsigned)(8 * (D / kEpiCols) * groups), 512, 0, s>>>(a, p.tiles_per_split, p.max_splits);
   else
     decode_merge_kernel<<<(unsigned)(8 * (G / 4) * groups), 256, 0, s>>>(a, p.tiles_per_split, p.max_splits);
   return hipGetLastError();

@@ -48,6 +48,15 @@ namespace hca {
 namespace {
 
 constexpr int DSTEPS = D / 16;  // k-steps of the score product (32)
+
+// s_waitcnt on the vector-memory count alone (gfx9 encoding: vmcnt bits 3:0
+// and 15:14, expcnt and lgkmcnt at their "no wait" maxima).  The builtin
+// updates the compiler's own count of outstanding loads.
+template <int N>
+__device__ __forceinline__ void wait_vm_count() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
 constexpr int HCT = 8;          // 32-column output tiles per wave (256 columns)
 constexpr int WSLOT = 2048;     // LDS bytes of one wave's bf16 weights of one tile (64 lanes x 32 B)
 constexpr int OSTR = 528;       // LDS bytes per staged output half-row (512 + 16 pad)
@@ -548,34 +557,67 @@ __device__ __forceinline__ void store_output(const Ctx& c, PState& st, float* li
 // The epilogue's inputs into LDS, once per workgroup: V^T and U^T of KV head
 // kvh as bf16 fragments (rank rows past `mix_rank` zero) and the gate's
 // sigmoid for the pair's positions (rows row0, row0 + 1; the second only if
-// it exists).  All loads are in bounds and issued before the first wait.
-__device__ __forceinline__ void load_epilogue_inputs(const PrefillArgs& a, char HCA_LDS* epi, int kvh, int row0,
-                                                     bool t1_ok) {
+// it exists).  In two steps around the query loads:
+//  * issue_epilogue_inputs: U and V of the KV head (fp32, 64 x rank each,
+//    contiguous) and the gate logits of the two positions (64 fp32 each) go
+//    into `stage` with direct loads, one row of up to 1 KiB per instruction
+//    (a range check zero-fills the rest of a partial row).  The caller
+//    issues the query loads after these, so that waiting for the inputs
+//    leaves the queries in flight.
+//  * build_epilogue_inputs (after every wave's rows have landed): each
+//    thread gathers its 8 + 8 values from `stage`, rounds them to bf16 and
+//    writes one V^T and one U^T fragment chunk, and threads 0..127 write
+//    the gate's sigmoid.
+constexpr int kEpiStageV = 8192;      // byte offset of V in the stage (U at 0; 64 x 32 fp32 max each)
+constexpr int kEpiStageGate = 16384;  // gate logits of position 0, then position 1 (1 KiB apart)
+
+__device__ __forceinline__ void issue_epilogue_inputs(const PrefillArgs& a, char HCA_LDS* stage, int kvh, int row0,
+                                                      bool t1_ok, int wave, int lane) {
+  if (a.mix_u) {
+    const int bytes = G * a.mix_rank * (int)sizeof(float);
+    const int rows = (bytes + 1023) / 1024;  // <= 8
+    const __amdgpu_buffer_rsrc_t ru = make_rsrc(a.mix_u + (size_t)kvh * G * a.mix_rank, (size_t)bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.mix_v + (size_t)kvh * G * a.mix_rank, (size_t)bytes);
+    for (int row = wave; row < rows; row += 4) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ru, (void HCA_LDS*)(stage + row * 1024), 16, lane * 16, row * 1024,
+                                               0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (void HCA_LDS*)(stage + kEpiStageV + row * 1024), 16, lane * 16,
+                                               row * 1024, 0, 0);
+    }
+  }
+  if (a.gate && wave < 2) {  // wave p loads position p's 64 logits (the first position again if p absent)
+    const int row = row0 + (wave == 1 && t1_ok ? 1 : 0);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.gate + (size_t)row * a.hq + kvh * G, G * sizeof(float));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rg, (void HCA_LDS*)(stage + kEpiStageGate + wave * 1024), 16, lane * 16,
+                                             0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void build_epilogue_inputs(const PrefillArgs& a, const char HCA_LDS* stage,
+                                                      char HCA_LDS* epi) {
   const int i8 = threadIdx.x, gh = i8 & 1;
-  bf16x8 fv = {}, fu = {};
-  float gv = 0.f;
   if (a.mix_u) {
     const int rank = a.mix_rank;
-    const float* vg = a.mix_v + (size_t)kvh * G * rank;
-    const float* ug = a.mix_u + (size_t)kvh * G * rank;
+    const float HCA_LDS* us = (const float HCA_LDS*)stage;
+    const float HCA_LDS* vs = (const float HCA_LDS*)(stage + kEpiStageV);
     const int rv = i8 >> 3, sv = (i8 >> 1) & 3;  // V^T chunk: rank rv, heads 16 sv + kslot_index(gh, j)
     const int hu = i8 >> 2, su = (i8 >> 1) & 1;  // U^T chunk: head hu, ranks 16 su + kslot_index(gh, j)
+    bf16x8 fv, fu;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int ru = 16 * su + kslot_index(gh, j);
-      const float x = vg[(16 * sv + kslot_index(gh, j)) * rank + min(rv, rank - 1)];
-      const float y = ug[hu * rank + min(ru, rank - 1)];
+      const float x = vs[(16 * sv + kslot_index(gh, j)) * rank + min(rv, rank - 1)];
+      const float y = us[hu * rank + min(ru, rank - 1)];
       fv[j] = (bf16)(rv < rank ? x : 0.f);
       fu[j] = (bf16)(ru < rank ? y : 0.f);
     }
-  }
-  const int pos = t1_ok ? (i8 >> 6) & 1 : 0;
-  if (a.gate) gv = a.gate[(size_t)(row0 + pos) * a.hq + kvh * G + (i8 & 63)];
-  if (a.mix_u) {
     *(bf16x8 HCA_LDS*)(epi + kEpiV + 16 * i8) = fv;
     *(bf16x8 HCA_LDS*)(epi + kEpiU + 16 * i8) = fu;
   }
-  if (a.gate && i8 < 128) ((float HCA_LDS*)(epi + kEpiGate))[i8] = sigmoid(gv);
+  if (a.gate && i8 < 128) {
+    const float gv = ((const float HCA_LDS*)(stage + kEpiStageGate))[(i8 >> 6) * 256 + (i8 & 63)];
+    ((float HCA_LDS*)(epi + kEpiGate))[i8] = sigmoid(gv);
+  }
 }
 
 // The Q^T fragments of one wave's 32 score rows (lane l: row l%32, elements
@@ -687,14 +729,22 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, int pair0, in
   const bf16* qwave = (const bf16*)a.q + ((size_t)qrow * a.hq + kvh * G + 32 * hg) * D;
   bf16x8 qf[DSTEPS];
   if constexpr (EPI) {
-    // the epilogue instantiation has no registers to spare for the staged
-    // form (it spills): strided fragment loads straight from HBM
+    // the epilogue's inputs first (into the free buffer k1_s), then the
+    // query fragments: the epilogue instantiation has no registers to spare
+    // for the staged form (it spills), so they are strided loads straight
+    // from HBM.  The asm statements keep the three groups of loads in this
+    // order; the wait then covers the inputs and leaves the queries in
+    // flight.  The pass's barriers order the LDS writes before their use,
+    // and before the first tile load into k1_s.
+    issue_epilogue_inputs(a, c.kb[1], kvh, start + (t0 - p0), t1_ok, wave, lane);
+    asm volatile("" ::: "memory");
     const bf16* qr = qwave + (size_t)(lane & 31) * D + 8 * (lane >> 5);
 #pragma unroll
     for (int k = 0; k < DSTEPS; ++k) qf[k] = *(const bf16x8*)(qr + 16 * k);
-    // the epilogue's inputs: their latency overlaps the Q loads, and the
-    // pass's barriers order the LDS writes before their use
-    load_epilogue_inputs(a, epi_s, kvh, start + (t0 - p0), t1_ok);
+    asm volatile("" ::: "memory");
+    wait_vm_count<DSTEPS>();                 // this wave's input rows are in
+    asm volatile("s_barrier" ::: "memory");  // every wave's
+    build_epilogue_inputs(a, c.kb[1], epi_s);
   } else {
     if (wave == 0)
       load_q(qwave, c.kb[0], lane, c.koff, qf);

@@ -395,10 +395,9 @@ __device__ __forceinline__ void attend_pair(const Ctx& c, const bf16x8 (&qf)[DST
 // matrix-core products:
 //   Z [ranks x cols] = V^T O: A = V^T (constant), B = O read back transposed
 //     from bf16 rows (one per head) staged in the wave's own LDS buffer;
-//   acc + l M^T = acc + Z^T (l U)^T: A = Z^T straight from Z's accumulators
-//     (lane = column), B = U^T with each head's column scaled by its row
-//     sum l, C = the accumulator tile itself (only read); then
-//     y = sigmoid(g) (acc + l M) / l elementwise, one multiply per value.
+//   M^T = Z^T U^T: A = Z^T straight from Z's accumulators (lane = column),
+//     B = U^T, from zero; then y = sigmoid(g) (acc / l + M) elementwise
+//     (the accumulators are only read).
 // The ranks run in the k-slot order Z's accumulator layout gives (lane
 // group h: ranks 4h..4h+3, 8+4h..8+4h+3 of each 16), and V^T follows the
 // head order of the transposed reads.  V^T, U^T and the gate come from LDS,
@@ -451,7 +450,6 @@ __device__ __forceinline__ void store_output(const Ctx& c, PState& st, float* li
       gs[0] = gr[32 * hg];
       gs[1] = gr[32 * (hg ^ 1)];
     }
-    const float sc[2] = {inv_own * gs[0], inv_par * gs[1]};  // per head: 1/l times the gate
     bf16x8 vt[4], ut[2][2];
     if (mix) {
       // stage O / l as bf16 rows: row = head (0..63), the wave's 256 columns
@@ -473,15 +471,10 @@ __device__ __forceinline__ void store_output(const Ctx& c, PState& st, float* li
       for (int s = 0; s < 4; ++s)  // A = V^T, k-step s
         vt[s] = *(const bf16x8 HCA_LDS*)(epi + kEpiV + ((r * 4 + s) * 2 + h) * 16);
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {  // B = U^T of head group g, k-step s2, times the head's l
-        const float lg = g ? l_par : lt;
+      for (int g = 0; g < 2; ++g)  // B = U^T of head group g, k-step s2
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const bf16x8 u = *(const bf16x8 HCA_LDS*)(epi + kEpiU + (((32 * (hg ^ g) + r) * 2 + s2) * 2 + h) * 16);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) ut[g][s2][j] = (bf16)((float)u[j] * lg);
-        }
-      }
+        for (int s2 = 0; s2 < 2; ++s2)
+          ut[g][s2] = *(const bf16x8 HCA_LDS*)(epi + kEpiU + (((32 * (hg ^ g) + r) * 2 + s2) * 2 + h) * 16);
     }
     const int off = (4 * h + ((lane & 15) >> 2)) * MSTR + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
     __builtin_amdgcn_sched_barrier(0);
@@ -505,20 +498,18 @@ __device__ __forceinline__ void store_output(const Ctx& c, PState& st, float* li
       }
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        // acc + l M for these 32 heads x 32 columns: the matrix cores add
-        // the mixing term to the accumulator tile (only read), with U^T
-        // scaled by each head's l; then y = (acc + l M) / l * gate
-        f32x16 y = st.o[g][ct];
+        f32x16 y = {};  // the mixing term of these 32 heads x 32 columns
         if (mix) {
-          y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za[0], ut[g][0], st.o[g][ct], 0, 0, 0);
+          y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za[0], ut[g][0], y, 0, 0, 0);
           if (rank > 16) y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za[1], ut[g][1], y, 0, 0, 0);
         }
+        const float inv = g ? inv_par : inv_own;
         char HCA_LDS* rowp = stg + (32 * (hg ^ g) + r) * MSTR + h * 8 + 64 * ct;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           bf16x4 v;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = (bf16)(y[4 * q4 + i] * sc[g]);
+          for (int i = 0; i < 4; ++i) v[i] = (bf16)((st.o[g][ct][4 * q4 + i] * inv + y[4 * q4 + i]) * gs[g]);
           *(bf16x4 HCA_LDS*)(rowp + 16 * q4) = v;
         }
       }

@@ -427,7 +427,7 @@ constexpr int kEpiBytes = 8704;
 template <bool EPI>
 __device__ __forceinline__ void store_output(const Ctx& c, PState& st, float* linv, bf16* obase,
                                              bool row_ok, const PrefillArgs& a, const char HCA_LDS* epi,
-                                             float* lse_row) {
+                                             float* lse_row, const char* pf0, const char* pf1) {
   const int lane = c.lane, wave = c.wave, hg = wave & 1;
   const float lt = st.l + __shfl_xor(st.l, 32);
   const float inv_own = 1.f / lt;
@@ -435,7 +435,33 @@ __device__ __forceinline__ void store_output(const Ctx& c, PState& st, float* li
   __syncthreads();  // every wave is past its last tile: K/V buffers are free
   const float l_par = linv[(wave ^ 1) * 32 + (lane & 31)];
   const float inv_par = 1.f / l_par;
-  if (!row_ok) return;
+  // Fused epilogue only: warm this XCD's L2 with the query rows of the
+  // workgroup that most likely runs next on it (kPrefetchAhead), whose
+  // strided fragment loads (see prefill_body) then hit L2.  One dword of
+  // every 128-byte line, issued after the barrier so that its fence does not
+  // wait for them; the values only feed an empty asm statement at the very
+  // end, so the wait for them comes after the output stores are issued.
+  // (The plain kernel stages its queries with direct loads and did not gain
+  // from this: +1 % at 128K.)
+  typedef const __attribute__((address_space(1))) unsigned* gptr;
+  unsigned pfv[4] = {0u, 0u, 0u, 0u};
+  if (EPI && pf0) {
+    const int o = threadIdx.x * 256;  // 64 KiB per position: two lines per thread
+    pfv[0] = *(gptr)(pf0 + o);
+    pfv[1] = *(gptr)(pf0 + o + 128);
+    if (pf1) {
+      pfv[2] = *(gptr)(pf1 + o);
+      pfv[3] = *(gptr)(pf1 + o + 128);
+    }
+  }
+  if constexpr (EPI) asm volatile("" ::: "memory");  // the loads stay here
+  auto consume = [&]() {
+    if constexpr (EPI) asm volatile("" ::"v"(pfv[0]), "v"(pfv[1]), "v"(pfv[2]), "v"(pfv[3]));
+  };
+  if (!row_ok) {
+    consume();
+    return;
+  }
   // log-sum-exp of the row's scaled scores (natural log): the weights are
   // exp2(s sc2 - m), so sum exp(scale s) = 2^m lt
   if (lse_row && lane < 32) lse_row[lane] = (st.m + __log2f(lt)) * kLn2;
@@ -527,6 +553,7 @@ __device__ __forceinline__ void store_output(const Ctx& c, PState& st, float* li
       const u32x4 v = {v0[0], v0[1], v1[0], v1[1]};
       __builtin_nontemporal_store(v, (u32x4*)(obase + (size_t)row * D + cw));
     }
+    consume();
     return;
   }
   const int hr = lane >> 5, cw = (lane & 31) * 8;
@@ -553,6 +580,7 @@ __device__ __forceinline__ void store_output(const Ctx& c, PState& st, float* li
                                   (bf16x8*)(og + (size_t)row * D + cw));
     }
   }
+  consume();
 }
 
 // The epilogue's inputs into LDS, once per workgroup: V^T and U^T of KV head
@@ -655,7 +683,7 @@ __host__ __device__ inline int pair_keys(int t0, int t_last, int window) {
 // skips the pairs of the other kind.
 // ---------------------------------------------------------------------------
 template <bool LO, bool EPI>
-__device__ __forceinline__ void prefill_body(const PrefillArgs& a, int pair0, int bx, char HCA_LDS* k0_s,
+__device__ __forceinline__ void prefill_body(const PrefillArgs& a, int pair0, int bx, int pf_pair, char HCA_LDS* k0_s,
                                              char HCA_LDS* k1_s, char HCA_LDS* v0_s, char HCA_LDS* v1_s,
                                              char HCA_LDS* w0_s, char HCA_LDS* w1_s, int* flag_s, float* linv_s,
                                              char HCA_LDS* epi_s) {
@@ -769,7 +797,14 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, int pair0, in
   attend_pair<LO>(c, qf, st);
   bf16* obase = (bf16*)a.o + ((size_t)qrow * a.hq + kvh * G) * D + hg * 256;
   float* lse_row = a.lse ? a.lse + (size_t)qrow * a.hq + kvh * G + 32 * hg : nullptr;
-  store_output<EPI>(c, st, linv_s, obase, row_ok, a, epi_s, lse_row);
+  const char* pf0 = nullptr;
+  const char* pf1 = nullptr;
+  if (pf_pair >= 0 && 2 * pf_pair < len) {
+    const char* q0 = (const char*)a.q + ((size_t)(start + 2 * pf_pair) * a.hq + kvh * G) * D * sizeof(bf16);
+    pf0 = q0;
+    if (2 * pf_pair + 1 < len) pf1 = q0 + (size_t)a.hq * D * sizeof(bf16);
+  }
+  store_output<EPI>(c, st, linv_s, obase, row_ok, a, epi_s, lse_row, pf0, pf1);
 }
 
 // Grid (lo_n + npairs - hi_begin, batch, Hkv), 256 threads: workgroup x <
@@ -784,6 +819,10 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, int pair0, in
 // the window rows of its own pairs instead of every row of the sequence
 // (a permutation of the pairs; a tail shorter than 8 G keeps its order).
 constexpr int kXcdGroup = 32;  // pairs per XCD per run: one per CU of an XCD
+// Workgroups are dispatched in id order, each XCD taking every eighth; with
+// 32 CUs per XCD busy, the workgroup that starts on an XCD when one ends
+// there is about 256 ids later.  Its query rows are prefetched into L2.
+constexpr int kPrefetchAhead = 8 * kXcdGroup;
 __device__ __forceinline__ int xcd_local_pair(int u, int n) {
   const int full = n / (8 * kXcdGroup) * (8 * kXcdGroup);
   if (u >= full) return u;
@@ -803,10 +842,14 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_kernel(PrefillArgs a, int
   __shared__ __attribute__((aligned(16))) char epi_s[EPI ? kEpiBytes : 16];
 #define HCA_LDS_ARGS (char HCA_LDS*)k0_s, (char HCA_LDS*)k1_s, (char HCA_LDS*)v0_s, (char HCA_LDS*)v1_s, \
     (char HCA_LDS*)w0_s, (char HCA_LDS*)w1_s, flag_s, linv_s, (char HCA_LDS*)epi_s
-  if ((int)blockIdx.x < lo_n)
-    prefill_body<true, EPI>(a, 0, blockIdx.x, HCA_LDS_ARGS);
-  else
-    prefill_body<false, EPI>(a, hi_begin, xcd_local_pair(blockIdx.x - lo_n, gridDim.x - lo_n), HCA_LDS_ARGS);
+  if ((int)blockIdx.x < lo_n) {
+    prefill_body<true, EPI>(a, 0, blockIdx.x, -1, HCA_LDS_ARGS);
+  } else {
+    const int n = gridDim.x - lo_n, x = blockIdx.x - lo_n;
+    prefill_body<false, EPI>(a, hi_begin, xcd_local_pair(x, n),
+                             EPI && x + kPrefetchAhead < n ? hi_begin + xcd_local_pair(x + kPrefetchAhead, n) : -1,
+                             HCA_LDS_ARGS);
+  }
 #undef HCA_LDS_ARGS
 }
 

@@ -389,6 +389,7 @@ __global__ __launch_bounds__(512) void decode_merge_epi_kernel(DecodeArgs a, int
   __shared__ __attribute__((aligned(16))) float o_s[G][kEpiCols + 4];
   __shared__ __attribute__((aligned(16))) float z_s[32][kEpiCols + 4];
   __shared__ float v_s[G][33];  // V of the unit's KV head, [head][rank]
+  __shared__ float u_s[G][33];  // U of the unit's KV head, [head][rank]
   const int wg = (int)blockIdx.x;
   const int unit = (wg & 7) + 8 * ((wg >> 3) / (D / kEpiCols));
   if (unit >= a.batch * a.hkv) return;
@@ -401,17 +402,19 @@ __global__ __launch_bounds__(512) void decode_merge_epi_kernel(DecodeArgs a, int
   const WsLayout w = ws_layout(a.ws, a.batch, a.hkv, max_splits);
   const int c0 = kEpiCols * slice + cq;
   // the epilogue's inputs are loaded first, so that their latency overlaps
-  // the merge's loads: U of this thread's head (rank <= 32), this thread's
-  // share of V (G x rank <= 4 per thread) and the gate logit
+  // the merge's loads: this thread's share of U and V (G x rank <= 4 each
+  // per thread, coalesced) and the gate logit
   const int rank = a.mix_u ? a.mix_rank : 0;
-  float u_r[32], vv[4];
+  float uu[4], vv[4];
   if (rank) {
-    const float* ug = a.mix_u + ((size_t)kvh * G + hr) * rank;
-#pragma unroll
-    for (int rk = 0; rk < 32; ++rk) u_r[rk] = rk < rank ? ug[rk] : 0.f;
+    const float* ug = a.mix_u + (size_t)kvh * G * rank;
     const float* vg = a.mix_v + (size_t)kvh * G * rank;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) vv[j] = tid + 512 * j < G * rank ? vg[tid + 512 * j] : 0.f;
+    for (int j = 0; j < 4; ++j) {
+      const bool in = tid + 512 * j < G * rank;
+      uu[j] = in ? ug[tid + 512 * j] : 0.f;
+      vv[j] = in ? vg[tid + 512 * j] : 0.f;
+    }
   }
   const float glogit = a.gate ? a.gate[(size_t)b * a.hq + kvh * G + hr] : 0.f;
   float y[8];
@@ -425,30 +428,40 @@ __global__ __launch_bounds__(512) void decode_merge_epi_kernel(DecodeArgs a, int
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = tid + 512 * j;
-      if (e < G * rank) v_s[e / rank][e % rank] = vv[j];
+      if (e < G * rank) {
+        v_s[e / rank][e % rank] = vv[j];
+        u_s[e / rank][e % rank] = uu[j];
+      }
     }
     __syncthreads();
-    for (int e = tid; e < rank * (kEpiCols / 4); e += 512) {  // Z[rk][c] = sum_h V[h][rk] O[h][c], 4 columns
-      const int rk = e / (kEpiCols / 4), c = (e % (kEpiCols / 4)) * 4;
+    // Z[rk][c] = sum_h V[h][rk] O[h][c] for 4 columns: two threads (lanes
+    // e, e ^ 1) per item, 32 heads each, summed by a lane exchange
+    for (int e = tid; e < 2 * rank * (kEpiCols / 4); e += 512) {
+      const int item = e >> 1, half = e & 1;
+      const int rk = item / (kEpiCols / 4), c = (item % (kEpiCols / 4)) * 4;
       f32x4 z = {};
 #pragma unroll 16
-      for (int h = 0; h < G; ++h) {
+      for (int hh = 0; hh < G / 2; ++hh) {
+        const int h = 2 * hh + half;
         const float vh = v_s[h][rk];
         const f32x4 oh = *(const f32x4*)&o_s[h][c];
 #pragma unroll
         for (int i = 0; i < 4; ++i) z[i] = fmaf(vh, oh[i], z[i]);
       }
-      *(f32x4*)&z_s[rk][c] = z;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[i] += __shfl_xor(z[i], 1);
+      if (!half) *(f32x4*)&z_s[rk][c] = z;
     }
     __syncthreads();
 #pragma unroll
     for (int rk = 0; rk < 32; ++rk) {
       if (rk < rank) {
+        const float ur = u_s[hr][rk];
         const f32x4 z0 = *(const f32x4*)&z_s[rk][cq], z1 = *(const f32x4*)&z_s[rk][cq + 4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          y[i] = fmaf(u_r[rk], z0[i], y[i]);
-          y[4 + i] = fmaf(u_r[rk], z1[i], y[4 + i]);
+          y[i] = fmaf(ur, z0[i], y[i]);
+          y[4 + i] = fmaf(ur, z1[i], y[4 + i]);
         }
       }
     }

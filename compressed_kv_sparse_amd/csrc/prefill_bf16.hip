@@ -424,7 +424,7 @@ constexpr int kEpiBytes = 8704;
 // OSTR bytes) at a time, and stored two per instruction (lanes 0-31 row 2i,
 // lanes 32-63 row 2i+1; 512 contiguous bytes each).  EPI: the head mixing
 // and the per-head gate first, with their inputs from `epi`.
-template <bool EPI>
+template <bool EPI, bool INL>
 __device__ __forceinline__ void store_output(const Ctx& c, PState& st, float* linv, bf16* obase,
                                              bool row_ok, const PrefillArgs& a, const char HCA_LDS* epi,
                                              float* lse_row, const char* pf0, const char* pf1) {
@@ -446,7 +446,7 @@ __device__ __forceinline__ void store_output(const Ctx& c, PState& st, float* li
   typedef const __attribute__((address_space(1))) unsigned* gptr;
   unsigned pfv[4] = {0u, 0u, 0u, 0u};
   if (EPI && pf0) {
-    const int o = threadIdx.x * 256;  // 64 KiB per position: two lines per thread
+    const int o = (wave * 64 + lane) * 256;  // 64 KiB per position: two lines per thread
     pfv[0] = *(gptr)(pf0 + o);
     pfv[1] = *(gptr)(pf0 + o + 128);
     if (pf1) {
@@ -476,7 +476,6 @@ __device__ __forceinline__ void store_output(const Ctx& c, PState& st, float* li
       gs[0] = gr[32 * hg];
       gs[1] = gr[32 * (hg ^ 1)];
     }
-    bf16x8 vt[4], ut[2][2];
     if (mix) {
       // stage O / l as bf16 rows: row = head (0..63), the wave's 256 columns
 #pragma unroll
@@ -493,29 +492,76 @@ __device__ __forceinline__ void store_output(const Ctx& c, PState& st, float* li
             *(bf16x4 HCA_LDS*)(rowp + (32 * ct + 8 * q4) * 2) = v;
           }
       }
+    }
+    // V^T (A of Z = V^T O, k-step s) and U^T (B of U Z, head group g, k-step s2)
+    auto load_vt = [&](bf16x8(&vt)[4]) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s)  // A = V^T, k-step s
-        vt[s] = *(const bf16x8 HCA_LDS*)(epi + kEpiV + ((r * 4 + s) * 2 + h) * 16);
+      for (int s = 0; s < 4; ++s) vt[s] = *(const volatile bf16x8 HCA_LDS*)(epi + kEpiV + ((r * 4 + s) * 2 + h) * 16);
+    };
+    auto load_ut = [&](bf16x8(&ut)[2][2]) {
 #pragma unroll
-      for (int g = 0; g < 2; ++g)  // B = U^T of head group g, k-step s2
+      for (int g = 0; g < 2; ++g)
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
-          ut[g][s2] = *(const bf16x8 HCA_LDS*)(epi + kEpiU + (((32 * (hg ^ g) + r) * 2 + s2) * 2 + h) * 16);
+          ut[g][s2] =
+              *(const volatile bf16x8 HCA_LDS*)(epi + kEpiU + (((32 * (hg ^ g) + r) * 2 + s2) * 2 + h) * 16);
+    };
+    bf16x8 vt0[4], ut0[2][2];
+    if (!INL && mix) {
+      load_vt(vt0);
+      load_ut(ut0);
     }
     const int off = (4 * h + ((lane & 15) >> 2)) * MSTR + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ct = 0; ct < HCT; ++ct) {
-      bf16x8 za[2];
+      // Two forms of the Z and mixing products.  Builtin MFMAs with V^T, U^T
+      // held across the loop (the pipelined pairs: the compiler overlaps the
+      // products with the VALU work and the LDS reads), and inline MFMAs
+      // with VGPR accumulators, V^T, U^T read again for every column tile
+      // (the two-term pairs).  The second form needs far fewer registers:
+      // there, with the builtin form the allocator put the products'
+      // operands in AGPRs and spilled the O accumulators it moved out of
+      // them.  The compiler does not see inside an inline MFMA, so each asm
+      // chain also spends the wait states around it: 5 before (its operands
+      // may just have been written by the VALU) and 24 after (a VALU read of
+      // the result, or a write to one of its operand registers, waits for
+      // the matrix core).
+      bf16x8 za[2], vt[4], ut[2][2];
       if (mix) {
-        f32x16 z = {};
+        if constexpr (INL) {
+          load_vt(vt);
+          load_ut(ut);
+        } else {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) vt[s] = vt0[s];
+#pragma unroll
+          for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) ut[g][s2] = ut0[g][s2];
+        }
+        bf16x8 bq[4];  // B = the staged O/l, k-step s (64 heads)
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const char HCA_LDS* base = stg + off + 16 * s * MSTR + 64 * ct;
           const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 HCA_LDS*)base);
           const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 HCA_LDS*)(base + 8 * MSTR));
-          const bf16x8 bq = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
-          z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt[s], bq, z, 0, 0, 0);
+          bq[s] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+        f32x16 z = {};
+        if constexpr (INL) {
+          asm volatile(
+              "s_nop 4\n\t"
+              "v_mfma_f32_32x32x16_bf16 %0, %1, %5, 0\n\t"
+              "v_mfma_f32_32x32x16_bf16 %0, %2, %6, %0\n\t"
+              "v_mfma_f32_32x32x16_bf16 %0, %3, %7, %0\n\t"
+              "v_mfma_f32_32x32x16_bf16 %0, %4, %8, %0\n\t"
+              "s_nop 15\n\ts_nop 7"
+              : "=&v"(z)
+              : "v"(vt[0]), "v"(vt[1]), "v"(vt[2]), "v"(vt[3]), "v"(bq[0]), "v"(bq[1]), "v"(bq[2]), "v"(bq[3]));
+        } else {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt[s], bq[s], z, 0, 0, 0);
         }
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
@@ -526,8 +572,23 @@ __device__ __forceinline__ void store_output(const Ctx& c, PState& st, float* li
       for (int g = 0; g < 2; ++g) {
         f32x16 y = {};  // the mixing term of these 32 heads x 32 columns
         if (mix) {
-          y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za[0], ut[g][0], y, 0, 0, 0);
-          if (rank > 16) y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za[1], ut[g][1], y, 0, 0, 0);
+          if constexpr (INL) {
+            if (rank > 16)
+              asm volatile(
+                  "s_nop 4\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %0, %1, %3, 0\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %0, %2, %4, %0\n\t"
+                  "s_nop 15\n\ts_nop 7"
+                  : "=&v"(y)
+                  : "v"(za[0]), "v"(za[1]), "v"(ut[g][0]), "v"(ut[g][1]));
+            else
+              asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0\n\ts_nop 15\n\ts_nop 7"
+                           : "=&v"(y)
+                           : "v"(za[0]), "v"(ut[g][0]));
+          } else {
+            y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za[0], ut[g][0], y, 0, 0, 0);
+            if (rank > 16) y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za[1], ut[g][1], y, 0, 0, 0);
+          }
         }
         const float inv = g ? inv_par : inv_own;
         char HCA_LDS* rowp = stg + (32 * (hg ^ g) + r) * MSTR + h * 8 + 64 * ct;
@@ -699,7 +760,11 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, int pair0, in
     const int t_last = 2 * pair + 1 < len ? t0 + 1 : t0;
     if ((pair_keys(t0, t_last, a.window) <= kTwoTermKeys) != LO) return;
   }
-  const int lane = threadIdx.x & 63;
+  // the fused epilogue takes the lane index from mbcnt, which the compiler
+  // can recompute where it is needed: derived from threadIdx.x, it kept that
+  // register live to the end and spilled it, and the reload's wait then
+  // also waited for the L2 prefetch of the output epilogue
+  const int lane = EPI ? __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) : threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int pw = wave >> 1, hg = wave & 1;
   const bool t1_ok = 2 * pair + 1 < len;
@@ -804,7 +869,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, int pair0, in
     pf0 = q0;
     if (2 * pf_pair + 1 < len) pf1 = q0 + (size_t)a.hq * D * sizeof(bf16);
   }
-  store_output<EPI>(c, st, linv_s, obase, row_ok, a, epi_s, lse_row, pf0, pf1);
+  store_output<EPI, LO>(c, st, linv_s, obase, row_ok, a, epi_s, lse_row, pf0, pf1);
 }
 
 // Grid (lo_n + npairs - hi_begin, batch, Hkv), 256 threads: workgroup x <

@@ -437,12 +437,12 @@ __device__ __forceinline__ void store_output(const Ctx& c, PState& st, float* li
   const float inv_par = 1.f / l_par;
   // Fused epilogue only: warm this XCD's L2 with the query rows of the
   // workgroup that most likely runs next on it (kPrefetchAhead), whose
-  // strided fragment loads (see prefill_body) then hit L2.  One dword of
+  // query loads (see prefill_body) then hit L2.  One dword of
   // every 128-byte line, issued after the barrier so that its fence does not
   // wait for them; the values only feed an empty asm statement at the very
   // end, so the wait for them comes after the output stores are issued.
-  // (The plain kernel stages its queries with direct loads and did not gain
-  // from this: +1 % at 128K.)
+  // (The plain kernel did not gain from this: +1 % at 128K.  Without it the
+  // fused epilogue is 8 % slower at 8K and 4 % at 128K.)
   typedef const __attribute__((address_space(1))) unsigned* gptr;
   unsigned pfv[4] = {0u, 0u, 0u, 0u};
   if (EPI && pf0) {
@@ -822,24 +822,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, int pair0, in
   // names a distinct array, so the branches are uniform and compile-time.
   const bf16* qwave = (const bf16*)a.q + ((size_t)qrow * a.hq + kvh * G + 32 * hg) * D;
   bf16x8 qf[DSTEPS];
-  if constexpr (EPI) {
-    // the epilogue's inputs first (into the free buffer k1_s), then the
-    // query fragments: the epilogue instantiation has no registers to spare
-    // for the staged form (it spills), so they are strided loads straight
-    // from HBM.  The asm statements keep the three groups of loads in this
-    // order; the wait then covers the inputs and leaves the queries in
-    // flight.  The pass's barriers order the LDS writes before their use,
-    // and before the first tile load into k1_s.
-    issue_epilogue_inputs(a, c.kb[1], kvh, start + (t0 - p0), t1_ok, wave, lane);
-    asm volatile("" ::: "memory");
-    const bf16* qr = qwave + (size_t)(lane & 31) * D + 8 * (lane >> 5);
-#pragma unroll
-    for (int k = 0; k < DSTEPS; ++k) qf[k] = *(const bf16x8*)(qr + 16 * k);
-    asm volatile("" ::: "memory");
-    wait_vm_count<DSTEPS>();                 // this wave's input rows are in
-    asm volatile("s_barrier" ::: "memory");  // every wave's
-    build_epilogue_inputs(a, c.kb[1], epi_s);
-  } else {
+  {
     if (wave == 0)
       load_q(qwave, c.kb[0], lane, c.koff, qf);
     else if (wave == 1)
@@ -849,6 +832,15 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, int pair0, in
     else
       load_q(qwave, c.vb[1], lane, c.koff, qf);
     __syncthreads();  // every wave holds its fragments: the buffers are free
+    if constexpr (EPI) {
+      // the epilogue's inputs, staged in the freed k1_s and built into
+      // epi_s; the pass's barriers order these LDS accesses before the
+      // first tile load into k1_s
+      issue_epilogue_inputs(a, c.kb[1], kvh, start + (t0 - p0), t1_ok, wave, lane);
+      wait_vm_all();
+      __syncthreads();
+      build_epilogue_inputs(a, c.kb[1], epi_s);
+    }
   }
 
   // the empty parts of the first pipeline stages read the V buffers with

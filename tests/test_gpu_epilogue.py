@@ -12,7 +12,7 @@ import torch
 import compressed_kv_sparse_amd as hca
 import oracle
 from hca_workloads import CONFIGS, decode_inputs, prefill_inputs, ring_from_raw
-from parity_util import assert_close, params_for
+from parity_util import assert_close, params_for, sample_rows
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -88,6 +88,45 @@ def test_zero_mixing_is_plain_prefill():
                                      inp["v"], kc, vc)
     torch.cuda.synchronize()
     assert torch.equal(o_mix.view(torch.int16), o_plain.view(torch.int16))
+
+
+@pytest.mark.parametrize("name,n_random", [("prefill_8k", None), ("prefill_128k", 48)])
+def test_gated_vha_workload(name, n_random):
+    """The fused epilogue (gate + rank-16 mixing, gate logits N(0, 1), factors
+    of standard deviation 0.1, as the benchmark times it) at the workload's
+    full size and launch configuration: every row at 8K, sampled rows (the
+    key-set boundaries plus seeded random rows) at 128K.  The mixing and the
+    gate act within one row, so the oracle's prefill of the sampled rows
+    followed by its mixing gives those rows' exact outputs."""
+    c = CONFIGS[name]
+    inp = prefill_inputs(c, DEV)
+    p = params_for(c)
+    kc, vc = hca.hca_compress(p, inp["cu_seqlens"], inp["cu_blocks"], inp["total_blocks"], inp["k"], inp["w"],
+                              v=inp["v"])
+    u, v = _factors(c.hkv, 16, seed=451)
+    T = inp["lens"][0]
+    g = torch.Generator(device=DEV).manual_seed(452)
+    gate = torch.randn((T, c.hq), generator=g, device=DEV)
+    o = hca.hca_attend_prefill_gated_vha(p, inp["cu_seqlens"], inp["cu_blocks"], inp["max_seqlen"], inp["q"],
+                                         inp["k"], inp["v"], kc, vc, gate=gate, vha_u=u, vha_v=v)
+    torch.cuda.synchronize()
+    cu = inp["cu_seqlens_host"]
+    w = inp["w"].cpu()
+    k, vv = inp["k"].cpu(), inp["v"].cpu()
+    kc_ref, vc_ref = oracle.compress(k, w, cu), oracle.compress(vv, w, cu)
+    if n_random is None:
+        rows = list(range(T))
+        ref = oracle.attend_prefill(inp["q"].cpu(), k, vv, kc_ref, vc_ref, cu, c.window)
+    else:
+        rows = sample_rows(T, c.window, n_random, seed=c.seed)
+        q_rows = inp["q"].index_select(0, torch.tensor(rows, device=DEV)).cpu()
+        ref = oracle.attend_prefill(q_rows, k, vv, kc_ref, vc_ref, cu, c.window, rows=rows, q_holds_rows_only=True)
+    idx = torch.tensor(rows, device=DEV)
+    ref = oracle.head_mix_and_gate(ref, u.cpu(), v.cpu(), gate.index_select(0, idx).cpu())
+    assert_close(o.index_select(0, idx), ref, torch.bfloat16, f"{name} gated VHA rank 16 ({len(rows)} rows)",
+                 beyond_rounding=True)
+    del inp, o, gate
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("lens,rank,with_gate", [

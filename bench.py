@@ -47,7 +47,9 @@ EPILOGUE_RANK = 16  # head-mixing rank of the fused-epilogue measurement (the pa
 _CS = "compressed_kv_sparse_amd/csrc/"
 KERNEL_SOURCES = {
     "prefill": (_CS + "prefill_bf16.hip", _CS + "bf16_tiles.h"),
+    "prefill_gated_vha": (_CS + "prefill_bf16.hip", _CS + "bf16_tiles.h"),
     "decode": (_CS + "decode_bf16.hip", _CS + "bf16_tiles.h"),
+    "decode_gated_vha": (_CS + "decode_bf16.hip", _CS + "bf16_tiles.h"),
     "compress": (_CS + "compress.hip",),
     "prefill_chunk": (_CS + "chunk.hip", _CS + "prefill_bf16.hip", _CS + "bf16_tiles.h"),
     "compress_chunk": (_CS + "compress.hip",),

@@ -476,23 +476,6 @@ __device__ __forceinline__ void store_output(const Ctx& c, PState& st, float* li
       gs[0] = gr[32 * hg];
       gs[1] = gr[32 * (hg ^ 1)];
     }
-    if (mix) {
-      // stage O / l as bf16 rows: row = head (0..63), the wave's 256 columns
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const float inv = g ? inv_par : inv_own;
-        char HCA_LDS* rowp = stg + (32 * (hg ^ g) + r) * MSTR + h * 8;
-#pragma unroll
-        for (int ct = 0; ct < HCT; ++ct)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            bf16x4 v;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = (bf16)(st.o[g][ct][4 * q4 + i] * inv);
-            *(bf16x4 HCA_LDS*)(rowp + (32 * ct + 8 * q4) * 2) = v;
-          }
-      }
-    }
     // V^T (A of Z = V^T O, k-step s) and U^T (B of U Z, head group g, k-step s2)
     auto load_vt = [&](bf16x8(&vt)[4]) {
 #pragma unroll
@@ -527,8 +510,28 @@ __device__ __forceinline__ void store_output(const Ctx& c, PState& st, float* li
       // may just have been written by the VALU) and 24 after (a VALU read of
       // the result, or a write to one of its operand registers, waits for
       // the matrix core).
+      // this column tile of O (both head groups), read from the accumulators
+      // once: staged as bf16 rows (row = head 0..63, the wave's own columns)
+      // for the Z product's transposed reads, then reused for the output
+      float ov[2][16];
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ov[g][i] = st.o[g][ct][i];
       bf16x8 za[2], vt[4], ut[2][2];
       if (mix) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const float inv = g ? inv_par : inv_own;
+          char HCA_LDS* rowp = stg + (32 * (hg ^ g) + r) * MSTR + h * 8 + 64 * ct;
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            bf16x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = (bf16)(ov[g][4 * q4 + i] * inv);
+            *(bf16x4 HCA_LDS*)(rowp + 16 * q4) = v;
+          }
+        }
         if constexpr (INL) {
           load_vt(vt);
           load_ut(ut);
@@ -596,7 +599,7 @@ __device__ __forceinline__ void store_output(const Ctx& c, PState& st, float* li
         for (int q4 = 0; q4 < 4; ++q4) {
           bf16x4 v;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = (bf16)((st.o[g][ct][4 * q4 + i] * inv + y[4 * q4 + i]) * gs[g]);
+          for (int i = 0; i < 4; ++i) v[i] = (bf16)((ov[g][4 * q4 + i] * inv + y[4 * q4 + i]) * gs[g]);
           *(bf16x4 HCA_LDS*)(rowp + 16 * q4) = v;
         }
       }

@@ -651,20 +651,22 @@ __device__ __forceinline__ void store_output(const Ctx& c, PState& st, float* li
 // kvh as bf16 fragments (rank rows past `mix_rank` zero) and the gate's
 // sigmoid for the pair's positions (rows row0, row0 + 1; the second only if
 // it exists).  In two steps around the query loads:
-//  * issue_epilogue_inputs: U and V of the KV head (fp32, 64 x rank each,
-//    contiguous) and the gate logits of the two positions (64 fp32 each) go
-//    into `stage` with direct loads, one row of up to 1 KiB per instruction
-//    (a range check zero-fills the rest of a partial row).  The caller
-//    issues the query loads after these, so that waiting for the inputs
-//    leaves the queries in flight.
+//  * issue_epilogue_inputs, before the query loads: U and V of the KV head
+//    (fp32, 64 x rank each, contiguous) go into `ustage` and `vstage` (8 KiB
+//    each: the weight slots, free until the pass starts) with direct loads,
+//    one row of up to 1 KiB per instruction (a range check zero-fills the
+//    rest of a partial row); the gate logits of the two positions (64 fp32
+//    each) go straight into the gate area of `epi` with one dword per lane.
+//    The query loads' wait then covers these too: no round trip of their own.
 //  * build_epilogue_inputs (after every wave's rows have landed): each
-//    thread gathers its 8 + 8 values from `stage`, rounds them to bf16 and
-//    writes one V^T and one U^T fragment chunk, and threads 0..127 write
-//    the gate's sigmoid.
-constexpr int kEpiStageV = 8192;      // byte offset of V in the stage (U at 0; 64 x 32 fp32 max each)
-constexpr int kEpiStageGate = 16384;  // gate logits of position 0, then position 1 (1 KiB apart)
+//    thread gathers its 8 + 8 values from the stages, rounds them to bf16
+//    and writes one V^T and one U^T fragment chunk, and threads 0..127 turn
+//    their gate logit into its sigmoid in place.
+constexpr int kEpiStageBytes = G * 32 * 4;  // one staged factor: 64 heads x rank <= 32, fp32
+static_assert(kEpiStageBytes <= 4 * WSLOT, "a staged mixing factor fits in one weight slot array");
 
-__device__ __forceinline__ void issue_epilogue_inputs(const PrefillArgs& a, char HCA_LDS* stage, int kvh, int row0,
+__device__ __forceinline__ void issue_epilogue_inputs(const PrefillArgs& a, char HCA_LDS* ustage,
+                                                      char HCA_LDS* vstage, char HCA_LDS* epi, int kvh, int row0,
                                                       bool t1_ok, int wave, int lane) {
   if (a.mix_u) {
     const int bytes = G * a.mix_rank * (int)sizeof(float);
@@ -672,27 +674,27 @@ __device__ __forceinline__ void issue_epilogue_inputs(const PrefillArgs& a, char
     const __amdgpu_buffer_rsrc_t ru = make_rsrc(a.mix_u + (size_t)kvh * G * a.mix_rank, (size_t)bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.mix_v + (size_t)kvh * G * a.mix_rank, (size_t)bytes);
     for (int row = wave; row < rows; row += 4) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ru, (void HCA_LDS*)(stage + row * 1024), 16, lane * 16, row * 1024,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ru, (void HCA_LDS*)(ustage + row * 1024), 16, lane * 16, row * 1024,
                                                0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (void HCA_LDS*)(stage + kEpiStageV + row * 1024), 16, lane * 16,
-                                               row * 1024, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (void HCA_LDS*)(vstage + row * 1024), 16, lane * 16, row * 1024,
+                                               0, 0);
     }
   }
   if (a.gate && wave < 2) {  // wave p loads position p's 64 logits (the first position again if p absent)
     const int row = row0 + (wave == 1 && t1_ok ? 1 : 0);
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.gate + (size_t)row * a.hq + kvh * G, G * sizeof(float));
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rg, (void HCA_LDS*)(stage + kEpiStageGate + wave * 1024), 16, lane * 16,
-                                             0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rg, (void HCA_LDS*)(epi + kEpiGate + wave * G * 4), 4, lane * 4, 0, 0,
+                                             0);
   }
 }
 
-__device__ __forceinline__ void build_epilogue_inputs(const PrefillArgs& a, const char HCA_LDS* stage,
-                                                      char HCA_LDS* epi) {
+__device__ __forceinline__ void build_epilogue_inputs(const PrefillArgs& a, const char HCA_LDS* ustage,
+                                                      const char HCA_LDS* vstage, char HCA_LDS* epi) {
   const int i8 = threadIdx.x, gh = i8 & 1;
   if (a.mix_u) {
     const int rank = a.mix_rank;
-    const float HCA_LDS* us = (const float HCA_LDS*)stage;
-    const float HCA_LDS* vs = (const float HCA_LDS*)(stage + kEpiStageV);
+    const float HCA_LDS* us = (const float HCA_LDS*)ustage;
+    const float HCA_LDS* vs = (const float HCA_LDS*)vstage;
     const int rv = i8 >> 3, sv = (i8 >> 1) & 3;  // V^T chunk: rank rv, heads 16 sv + kslot_index(gh, j)
     const int hu = i8 >> 2, su = (i8 >> 1) & 1;  // U^T chunk: head hu, ranks 16 su + kslot_index(gh, j)
     bf16x8 fv, fu;
@@ -707,9 +709,9 @@ __device__ __forceinline__ void build_epilogue_inputs(const PrefillArgs& a, cons
     *(bf16x8 HCA_LDS*)(epi + kEpiV + 16 * i8) = fv;
     *(bf16x8 HCA_LDS*)(epi + kEpiU + 16 * i8) = fu;
   }
-  if (a.gate && i8 < 128) {
-    const float gv = ((const float HCA_LDS*)(stage + kEpiStageGate))[(i8 >> 6) * 256 + (i8 & 63)];
-    ((float HCA_LDS*)(epi + kEpiGate))[i8] = sigmoid(gv);
+  if (a.gate && i8 < 128) {  // position i8 / 64, head i8 % 64: read and written by this thread only
+    float HCA_LDS* gp = (float HCA_LDS*)(epi + kEpiGate) + i8;
+    *gp = sigmoid(*gp);
   }
 }
 
@@ -826,6 +828,9 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, int pair0, in
   const bf16* qwave = (const bf16*)a.q + ((size_t)qrow * a.hq + kvh * G + 32 * hg) * D;
   bf16x8 qf[DSTEPS];
   {
+    // the epilogue's inputs go first, into LDS the query staging leaves free
+    if constexpr (EPI)
+      issue_epilogue_inputs(a, c.ws[0], c.ws[1], epi_s, kvh, start + (t0 - p0), t1_ok, wave, lane);
     if (wave == 0)
       load_q(qwave, c.kb[0], lane, c.koff, qf);
     else if (wave == 1)
@@ -834,15 +839,10 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, int pair0, in
       load_q(qwave, c.vb[0], lane, c.koff, qf);
     else
       load_q(qwave, c.vb[1], lane, c.koff, qf);
-    __syncthreads();  // every wave holds its fragments: the buffers are free
+    __syncthreads();  // every wave holds its fragments and every staged input has landed
     if constexpr (EPI) {
-      // the epilogue's inputs, staged in the freed k1_s and built into
-      // epi_s; the pass's barriers order these LDS accesses before the
-      // first tile load into k1_s
-      issue_epilogue_inputs(a, c.kb[1], kvh, start + (t0 - p0), t1_ok, wave, lane);
-      wait_vm_all();
-      __syncthreads();
-      build_epilogue_inputs(a, c.kb[1], epi_s);
+      build_epilogue_inputs(a, c.ws[0], c.ws[1], epi_s);
+      __syncthreads();  // the stages are read before the pass clears ws[0]
     }
   }
 

@@ -396,9 +396,11 @@ def run_prefill(torch, hca, c, steps, warmup, clock, min_warm_s, lens=None, extr
         gate = torch.randn((inp["q"].shape[0], c.hq), generator=g, device="cuda")
         u = torch.randn((c.hkv, c.hq // c.hkv, EPILOGUE_RANK), generator=g, device="cuda") * 0.1
         v = torch.randn_like(u) * 0.1
-        for _ in range(3):
-            hca.hca_attend_prefill_gated_vha(p, inp["cu_seqlens"], inp["cu_blocks"], inp["max_seqlen"], inp["q"],
-                                             inp["k"], inp["v"], kc, vc, gate=gate, vha_u=u, vha_v=v, o=o)
+        # warmed like the step: the pooling's cold loop above leaves the
+        # clocks low, and a few short launches would be timed before they ramp
+        warm_up(torch, lambda i: hca.hca_attend_prefill_gated_vha(
+            p, inp["cu_seqlens"], inp["cu_blocks"], inp["max_seqlen"], inp["q"], inp["k"], inp["v"], kc, vc,
+            gate=gate, vha_u=u, vha_v=v, o=o), 3, min_warm_s)
         for _ in range(steps):
             clock.run("prefill_gated_vha", lambda: hca.hca_attend_prefill_gated_vha(
                 p, inp["cu_seqlens"], inp["cu_blocks"], inp["max_seqlen"], inp["q"], inp["k"], inp["v"], kc, vc,
@@ -418,8 +420,7 @@ def run_prefill(torch, hca, c, steps, warmup, clock, min_warm_s, lens=None, extr
             return hca.hca_attend_prefill_backward(p, inp["cu_seqlens"], inp["cu_blocks"], inp["max_seqlen"],
                                                    inp["total_blocks"], inp["q"], inp["k"], inp["v"], inp["w"], kc,
                                                    vc, o2, lse, dout, workspace=ws, dq=dq, dk=dk, dv=dv, dw=dw)
-        for _ in range(2):
-            bwd()
+        warm_up(torch, lambda i: bwd(), 2, min_warm_s)
         for _ in range(steps):
             clock.run("prefill_lse", lambda: hca.hca_attend_prefill_lse(
                 p, inp["cu_seqlens"], inp["cu_blocks"], inp["max_seqlen"], inp["q"], inp["k"], inp["v"], kc, vc,

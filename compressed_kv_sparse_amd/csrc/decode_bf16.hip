@@ -284,15 +284,31 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a, int t
     w.m[prow] = st.m;
     w.l[prow] = l_tot;
   }
+  // O / l of the wave's 16 rows, staged in LDS (the tile buffers are free:
+  // the last pass ended with no load in flight and a barrier after its last
+  // fragment reads) and stored as whole 1 KiB rows, 16 bytes per lane: the
+  // accumulator layout would otherwise store 32-byte pieces of 16 rows per
+  // instruction.
   const float inv = 1.f / l_tot;
-  bf16* po = w.o + prow * D + 4 * (lane >> 4);
+  char HCA_LDS* stg = (char HCA_LDS*)kv0_s + wave * 16 * KSTR;
+  {
+    char HCA_LDS* rowp = stg + (lane & 15) * KSTR + 8 * (lane >> 4);
 #pragma unroll
-  for (int ct = 0; ct < CTILES16; ++ct) {
-    bf16x4 v;
+    for (int ct = 0; ct < CTILES16; ++ct) {
+      bf16x4 v;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = (bf16)(st.o[ct][i] * inv);
-    *(bf16x4*)(po + 16 * ct) = v;
+      for (int i = 0; i < 4; ++i) v[i] = (bf16)(st.o[ct][i] * inv);
+      *(bf16x4 HCA_LDS*)(rowp + 32 * ct) = v;
+    }
   }
+  // the wave reads rows its other lanes wrote: order the stores before the loads
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  bf16* po = w.o + (prow - (lane & 15)) * D + 8 * lane;  // row wave*16 of this split, columns 8 lane ..
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    *(bf16x8*)(po + (size_t)r * D) = *(const bf16x8 HCA_LDS*)(stg + r * KSTR + 16 * lane);
 }
 
 // Merge of the split partials: O = sum_s 2^(m_s - M) l_s O_s / sum_s 2^(m_s - M) l_s

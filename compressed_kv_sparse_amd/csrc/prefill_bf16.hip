@@ -138,27 +138,31 @@ __device__ __forceinline__ int vfrag_off(int f) { return (f >> 3) * 16 * VSTR + 
 // score product of tile s+1 (K in kb[1-P]) into `sacc`, the softmax of tile
 // s from `sprev` (weights into `own` and the wave's slot ws[P]) and the
 // output product of tile s-1 (V in vb[1-P]; weights in `own` and the
-// partner's from ws[1-P]).  Every stage runs all three parts, so the hot
-// loop is straight-line code and the accumulators never change registers;
-// a part whose tile lies outside [0, n) computes on stale (finite) buffer
-// contents and contributes nothing: the softmax of a missing tile writes
-// zero weights, and an output product with zero weights adds zero.  Loads
-// K(s+2) into kb[P] and V(s) into vb[P], and ends with the workgroup
+// partner's from ws[1-P]).  PARTS selects the parts (kScore, kSoftmax,
+// kOutput): the loop's stages run all three, so the hot loop is
+// straight-line code and the accumulators never change registers; the first
+// two and the last two stages of a pass run only the parts whose tiles
+// exist.  A part whose tile lies outside [0, n) computes on stale (finite)
+// buffer contents and contributes nothing: the softmax of a missing tile
+// writes zero weights, and an output product with zero weights adds zero.
+// Loads K(s+2) into kb[P] and V(s) into vb[P], and ends with the workgroup
 // barrier.  A kLazy softmax that exceeds the headroom raises flag[0] for the
 // rest of the pass.
-template <int P, int MODE>
+constexpr int kScore = 1, kSoftmax = 2, kOutput = 4, kAllParts = 7;
+template <int P, int MODE, int PARTS = kAllParts>
 __device__ __forceinline__ void stage(const Ctx& c, int s, const bf16x8 (&qf)[DSTEPS], f32x16& sacc,
                                       f32x16& sprev, Wts& own, PState& st) {
+  constexpr bool SC = (PARTS & kScore) != 0, SM = (PARTS & kSoftmax) != 0, OU = (PARTS & kOutput) != 0;
   const bool hm = s >= 0 && s < c.n;  // tile s exists
   const unsigned keep = hm ? ~0u : 0u;  // weights of a missing tile are zeroed (no branch)
   if (s + 2 < c.n) issue_tile<4, true, false>(c.ks, s + 2, c.kb[P], nullptr, c.wave, c.lane);
   if (hm) issue_tile<4, false, true>(c.ks, s, nullptr, c.vb[P], c.wave, c.lane);
-  if (hm && tile_needs_mask(s, c.rm.nc, c.rm.nkeys)) {
+  if (SM && hm && tile_needs_mask(s, c.rm.nc, c.rm.nkeys)) {
     asm volatile("");  // a branch: most tiles need no mask
     mask_scores(sprev, c.rm, s, c.lane);
   }
   Wts par;
-  {
+  if constexpr (OU) {
     const char HCA_LDS* pin = c.ws[1 - P] + c.wpar;
     par.hi[0] = *(const bf16x8 HCA_LDS*)pin;
     par.hi[1] = *(const bf16x8 HCA_LDS*)(pin + 1024);
@@ -167,23 +171,33 @@ __device__ __forceinline__ void stage(const Ctx& c, int s, const bf16x8 (&qf)[DS
   bf16x8 kf[KPF], vf[3];
   const char HCA_LDS* kr = c.kb[1 - P] + c.koff;
   const char HCA_LDS* vr = c.vb[1 - P] + c.voff;
+  if constexpr (SC) {
 #pragma unroll
-  for (int k = 0; k < KPF; ++k) kf[k] = lds_k_frag(kr + k * 32);
-  vf[0] = lds_v_frag(vr + vfrag_off(0));
-  vf[1] = lds_v_frag(vr + vfrag_off(1));
+    for (int k = 0; k < KPF; ++k) kf[k] = lds_k_frag(kr + k * 32);
+  }
+  if constexpr (OU) {
+    vf[0] = lds_v_frag(vr + vfrag_off(0));
+    vf[1] = lds_v_frag(vr + vfrag_off(1));
+  }
 
   SmWork w;
   // 32 steps: one score MFMA, one output MFMA, a slice of the softmax
 #pragma unroll
   for (int j = 0; j < DSTEPS; ++j) {
-    s_mfma(j, sacc, kf[j % KPF], qf[j]);
-    if (j + KPF < DSTEPS) kf[j % KPF] = lds_k_frag(kr + (j + KPF) * 32);
-    {
+    if constexpr (SC) {
+      s_mfma(j, sacc, kf[j % KPF], qf[j]);
+      if (j + KPF < DSTEPS) kf[j % KPF] = lds_k_frag(kr + (j + KPF) * 32);
+    }
+    if constexpr (OU) {
       // output step u = j: fragment f = u / 2, head group u % 2 (0 = own)
       const int f = j >> 1, g = j & 1;
       const bf16x8 b = g ? par.hi[f >> 3] : own.hi[f >> 3];
       st.o[g][f & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[f % 3], b, st.o[g][f & 7], 0, 0, 0);
       if (g == 1 && f + 2 < 16) vf[(f + 2) % 3] = lds_v_frag(vr + vfrag_off(f + 2));
+    }
+    if (!SM) {
+      __builtin_amdgcn_sched_barrier(0);
+      continue;
     }
     if (j == 0) {
 #pragma unroll
@@ -218,35 +232,46 @@ __device__ __forceinline__ void stage(const Ctx& c, int s, const bf16x8 (&qf)[DS
   }
   // a VALU read of an MFMA result needs up to 18 wait states; the compiler
   // does not see inside the inline MFMAs, so they are spent here (24)
-  asm volatile("s_nop 15\n\ts_nop 7" : "+v"(sacc));
-  st.l += w.la + w.lb;
-  own.hi[0] = __builtin_bit_cast(bf16x8, w.ua);
-  own.hi[1] = __builtin_bit_cast(bf16x8, w.ub);
-  char HCA_LDS* pout = c.ws[P] + c.wown;
-  *(u32x4 HCA_LDS*)pout = w.ua;
-  *(u32x4 HCA_LDS*)(pout + 1024) = w.ub;
-  if (MODE == kLazy && __any(w.over) && c.lane == 0) c.flag[0] = 1;
+  if constexpr (SC) asm volatile("s_nop 15\n\ts_nop 7" : "+v"(sacc));
+  if constexpr (SM) {
+    st.l += w.la + w.lb;
+    own.hi[0] = __builtin_bit_cast(bf16x8, w.ua);
+    own.hi[1] = __builtin_bit_cast(bf16x8, w.ub);
+    char HCA_LDS* pout = c.ws[P] + c.wown;
+    *(u32x4 HCA_LDS*)pout = w.ua;
+    *(u32x4 HCA_LDS*)(pout + 1024) = w.ub;
+    if (MODE == kLazy && __any(w.over) && c.lane == 0) c.flag[0] = 1;
+  }
   wait_vm_all();
   __syncthreads();
 }
 
-// One software-pipelined pass over all n tiles in schedule MODE (kLazy or
-// kFixed): stages -1 .. n (plus one empty stage when the count is odd).
-// K(0) must be in kb[0], slot ws[0] must hold zero weights and all K and V
-// buffers finite values (the empty parts of the first stages read them).  The pass always runs to its end (an exit in the middle makes
-// the register allocator spill); the caller then reads flag[0] to learn
-// whether a kLazy pass must be redone.
+// One software-pipelined pass over all n >= 3 tiles in schedule MODE (kLazy
+// or kFixed): stages -1 .. n.  Stage -1 only scores tile 0 and stage 0 only
+// scores tile 1 and weighs tile 0; the loop runs full stages in pairs from
+// stage 1 while both of a pair's score products have tiles (for odd n its
+// last stage scores a missing tile); the last two stages weigh and add the
+// last tiles (for odd n the very last adds a missing tile with zero
+// weights).  So at most one stage's worth of the products is spent on
+// missing tiles.  Every part of a stage reads only buffers loaded in this
+// pass.  K(0) must be in kb[0].  The pass always runs to its end (an exit in
+// the middle makes the register allocator spill); the caller then reads
+// flag[0] to learn whether a kLazy pass must be redone.
 template <int MODE>
 __device__ __forceinline__ void pipelined_pass(const Ctx& c, const bf16x8 (&qf)[DSTEPS], PState& st) {
   f32x16 sa = {}, sb = {};  // score accumulators, alternating roles with the parity
   Wts own;
   own.hi[0] = own.hi[1] = bf16x8{};
-  int s = -1;
+  stage<1, MODE, kScore>(c, -1, qf, sa, sb, own, st);
+  stage<0, MODE, kScore | kSoftmax>(c, 0, qf, sb, sa, own, st);
+  int s = 1;
   do {
     stage<1, MODE>(c, s, qf, sa, sb, own, st);
     stage<0, MODE>(c, s + 1, qf, sb, sa, own, st);
     s += 2;
-  } while (s <= c.n);
+  } while (s <= c.n - 2);
+  stage<1, MODE, kSoftmax | kOutput>(c, s, qf, sa, sb, own, st);
+  stage<0, MODE, kOutput>(c, s + 1, qf, sb, sa, own, st);
 }
 
 // Plain per-tile loop (no overlap between the products): short key lists
@@ -349,9 +374,8 @@ __device__ __forceinline__ void plain_pass(const Ctx& c, const bf16x8 (&qf)[DSTE
   if (s < c.n) plain_tile<0, MODE, LO>(c, s, qf, st);
 }
 
-// Start of a pass: clear the flag and slot ws[0] (zero weights for the
-// first stage's empty output product), load K(0) (and V(0) for the plain
-// loop).
+// Start of a pass: clear the flag and slot ws[0], load K(0) (and V(0) for
+// the plain loop).
 __device__ __forceinline__ void pass_setup(const Ctx& c, bool with_v) {
   if (c.lane == 0 && c.wave == 0) c.flag[0] = c.flag[1] = 0;
   for (int o = threadIdx.x * 16; o < 4 * WSLOT; o += 256 * 16) *(u32x4 HCA_LDS*)(c.ws[0] + o) = u32x4{};
@@ -846,13 +870,6 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, int pair0, in
     }
   }
 
-  // the empty parts of the first pipeline stages read the V buffers with
-  // zero weights: make them finite.  (Stale K only feeds scores of missing
-  // tiles, whose weights are masked to zero bit for bit.)
-  for (int o = threadIdx.x * 16; !LO && o < VTILE; o += 256 * 16) {
-    *(u32x4 HCA_LDS*)(c.vb[0] + o) = u32x4{};
-    *(u32x4 HCA_LDS*)(c.vb[1] + o) = u32x4{};
-  }
   PState st;
   attend_pair<LO>(c, qf, st);
   bf16* obase = (bf16*)a.o + ((size_t)qrow * a.hq + kvh * G) * D + hg * 256;

@@ -452,7 +452,11 @@ template <bool EPI, bool INL>
 __device__ __forceinline__ void store_output(const Ctx& c, PState& st, float* linv, bf16* obase,
                                              bool row_ok, const PrefillArgs& a, const char HCA_LDS* epi,
                                              float* lse_row, const char* pf0, const char* pf1) {
-  const int lane = c.lane, wave = c.wave, hg = wave & 1;
+  // EPI: the lane index afresh from an opaque mbcnt (derived from the pass's
+  // copy, lane & 31 stayed live across the whole pass and was spilled)
+  int lane = c.lane;
+  if constexpr (EPI) asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+  const int wave = c.wave, hg = wave & 1;
   const float lt = st.l + __shfl_xor(st.l, 32);
   const float inv_own = 1.f / lt;
   if (lane < 32) linv[wave * 32 + lane] = lt;  // the row sums; the partner divides itself
